@@ -1,0 +1,242 @@
+"""CPU oracle of the cache-semantic bucketed hash table.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product
+library (``hash_table_cache_amd``) never does, and the two share no code.
+
+The arithmetic lives in ``hkv_oracle.cpp`` (plain single-threaded C++,
+following Algorithms 1-3 of the HierarchicalKV paper, §3.2-§3.4); this module
+only builds it with the host compiler and marshals numpy arrays through ctypes.
+Keys, scores, tags and positions are ``numpy.uint64``; values are
+``numpy.float32`` rows of ``dim`` elements; found flags are ``numpy.uint8``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import subprocess
+
+import numpy as np
+
+_HERE = pathlib.Path(__file__).resolve().parent
+SOURCE = _HERE / "hkv_oracle.cpp"
+LIB_PATH = _HERE / "_build" / "liboracle.so"
+
+# Outcome codes written by insert_or_assign (same values as the C enum).
+SKIPPED, UPDATED, INSERTED, EVICTED, REJECTED = 0, 1, 2, 3, 4
+
+EMPTY_KEY = np.uint64(0xFFFFFFFFFFFFFFFF)
+LOCKED_KEY = np.uint64(0xFFFFFFFFFFFFFFFE)
+SLOTS = 128
+
+_lib = None
+
+
+def build() -> pathlib.Path:
+    """Compile the oracle with the host C++ compiler (no GPU code involved)."""
+    LIB_PATH.parent.mkdir(parents=True, exist_ok=True)
+    tmp = LIB_PATH.with_suffix(".so.tmp")
+    subprocess.check_call(
+        ["g++", "-O2", "-std=c++17", "-Wall", "-shared", "-fPIC", "-o", str(tmp), str(SOURCE)]
+    )
+    tmp.replace(LIB_PATH)
+    return LIB_PATH
+
+
+def _u64p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+
+
+def _f32p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _u8p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _u32p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
+
+
+def lib():
+    """Load the oracle library, building it first if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        build()
+    L = ctypes.CDLL(str(LIB_PATH))
+    u64, u32, vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+    P64 = ctypes.POINTER(ctypes.c_uint64)
+    PF = ctypes.POINTER(ctypes.c_float)
+    P8 = ctypes.POINTER(ctypes.c_uint8)
+    P32 = ctypes.POINTER(ctypes.c_uint32)
+    L.oracle_create.argtypes = [u64, u32, ctypes.c_int, ctypes.c_int]
+    L.oracle_create.restype = vp
+    L.oracle_destroy.argtypes = [vp]
+    L.oracle_destroy.restype = None
+    L.oracle_fmix64.argtypes = [u64]
+    L.oracle_fmix64.restype = u64
+    L.oracle_murmur3_x64_128.argtypes = [vp, u64, u32, P64]
+    L.oracle_murmur3_x64_128.restype = None
+    L.oracle_route.argtypes = [vp, u64, P64, P64, P64, P8]
+    L.oracle_route.restype = None
+    L.oracle_find.argtypes = [vp, u64, P64, PF, P8, P64, P64]
+    L.oracle_find.restype = None
+    L.oracle_insert_or_assign.argtypes = [vp, u64, P64, PF, P64, P64, P32]
+    L.oracle_insert_or_assign.restype = None
+    L.oracle_assign.argtypes = [vp, u64, P64, PF, P64, P64]
+    L.oracle_assign.restype = None
+    L.oracle_size.argtypes = [vp]
+    L.oracle_size.restype = u64
+    L.oracle_export.argtypes = [vp, u64, u64, P64, PF, P64, P64, P64]
+    L.oracle_export.restype = u64
+    L.oracle_digests.argtypes = [vp, P8]
+    L.oracle_digests.restype = None
+    L.oracle_probe_stats.argtypes = [vp, P64]
+    L.oracle_probe_stats.restype = None
+    L.oracle_reset_probe_stats.argtypes = [vp]
+    L.oracle_reset_probe_stats.restype = None
+    _lib = L
+    return L
+
+
+def _keys(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.int64:
+        a = a.view(np.uint64)
+    if a.dtype != np.uint64:
+        raise TypeError(f"keys/scores must be uint64 (or int64 bit patterns), got {a.dtype}")
+    return a
+
+
+def fmix64(k: int) -> int:
+    return int(lib().oracle_fmix64(int(k)))
+
+
+def murmur3_x64_128(data: bytes, seed: int) -> tuple[int, int]:
+    out = np.zeros(2, dtype=np.uint64)
+    buf = ctypes.create_string_buffer(bytes(data), max(len(data), 1))
+    lib().oracle_murmur3_x64_128(buf, len(data), seed & 0xFFFFFFFF, _u64p(out))
+    return int(out[0]), int(out[1])
+
+
+class OracleTable:
+    """Single-threaded CPU table; see ``hkv_oracle.cpp`` for the semantics.
+
+    ``tag_mode=True`` stores one u64 tag per slot instead of ``dim`` floats, so
+    that tables whose value rows would not fit in host memory can still be
+    followed exactly (the caller derives the row from the tag).
+    """
+
+    def __init__(self, capacity: int, dim: int, dual: bool = False, tag_mode: bool = False):
+        self._lib = lib()
+        self.capacity = int(capacity)
+        self.dim = int(dim)
+        self.dual = bool(dual)
+        self.tag_mode = bool(tag_mode)
+        self.buckets = self.capacity // SLOTS
+        h = self._lib.oracle_create(self.capacity, self.dim, int(dual), int(tag_mode))
+        if not h:
+            raise ValueError(f"oracle_create rejected capacity={capacity} dim={dim}")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.oracle_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def route(self, keys):
+        keys = _keys(keys)
+        n = keys.size
+        b1 = np.empty(n, np.uint64)
+        b2 = np.empty(n, np.uint64)
+        d = np.empty(n, np.uint8)
+        self._lib.oracle_route(self._h, n, _u64p(keys), _u64p(b1), _u64p(b2), _u8p(d))
+        return b1, b2, d
+
+    def find(self, keys, values_out=None, scores_out=None, tags_out=None):
+        """Returns (values, found, scores, tags). Rows/scores/tags of misses keep
+        whatever the passed-in output arrays held (zeros if none given)."""
+        keys = _keys(keys)
+        n = keys.size
+        found = np.zeros(n, np.uint8)
+        if scores_out is None:
+            scores_out = np.zeros(n, np.uint64)
+        if self.tag_mode:
+            if tags_out is None:
+                tags_out = np.zeros(n, np.uint64)
+            self._lib.oracle_find(self._h, n, _u64p(keys), None, _u8p(found), _u64p(scores_out), _u64p(tags_out))
+            return None, found, scores_out, tags_out
+        if values_out is None:
+            values_out = np.zeros((n, self.dim), np.float32)
+        assert values_out.dtype == np.float32 and values_out.flags.c_contiguous
+        self._lib.oracle_find(self._h, n, _u64p(keys), _f32p(values_out), _u8p(found), _u64p(scores_out), None)
+        return values_out, found, scores_out, None
+
+    def insert_or_assign(self, keys, scores, values=None, tags=None):
+        """Applies the batch in input order; returns one outcome code per key."""
+        keys = _keys(keys)
+        scores = _keys(scores)
+        n = keys.size
+        assert scores.size == n
+        out = np.zeros(n, np.uint32)
+        if self.tag_mode:
+            tags = _keys(tags)
+            assert tags.size == n
+            self._lib.oracle_insert_or_assign(self._h, n, _u64p(keys), None, _u64p(tags), _u64p(scores), _u32p(out))
+        else:
+            values = np.ascontiguousarray(values, dtype=np.float32)
+            assert values.shape == (n, self.dim)
+            self._lib.oracle_insert_or_assign(self._h, n, _u64p(keys), _f32p(values), None, _u64p(scores), _u32p(out))
+        return out
+
+    def assign(self, keys, values=None, scores=None, tags=None):
+        keys = _keys(keys)
+        n = keys.size
+        if scores is not None:
+            scores = _keys(scores)
+        if values is not None:
+            values = np.ascontiguousarray(values, dtype=np.float32)
+            assert values.shape == (n, self.dim)
+        if tags is not None:
+            tags = _keys(tags)
+        self._lib.oracle_assign(self._h, n, _u64p(keys), _f32p(values), _u64p(tags), _u64p(scores))
+
+    def size(self) -> int:
+        return int(self._lib.oracle_size(self._h))
+
+    def export(self, offset: int = 0, n_slots: int | None = None):
+        """Occupied slots in [offset, offset + n_slots), ascending position.
+        Returns dict(keys, scores, pos, values | tags)."""
+        if n_slots is None:
+            n_slots = self.capacity - offset
+        m_max = max(0, min(n_slots, self.capacity - offset))
+        keys = np.empty(m_max, np.uint64)
+        scores = np.empty(m_max, np.uint64)
+        pos = np.empty(m_max, np.uint64)
+        if self.tag_mode:
+            tags = np.empty(m_max, np.uint64)
+            m = self._lib.oracle_export(self._h, offset, n_slots, _u64p(keys), None, _u64p(scores), _u64p(pos), _u64p(tags))
+            return dict(keys=keys[:m], scores=scores[:m], pos=pos[:m], tags=tags[:m])
+        values = np.empty((m_max, self.dim), np.float32)
+        m = self._lib.oracle_export(self._h, offset, n_slots, _u64p(keys), _f32p(values), _u64p(scores), _u64p(pos), None)
+        return dict(keys=keys[:m], scores=scores[:m], pos=pos[:m], values=values[:m])
+
+    def digests(self) -> np.ndarray:
+        out = np.empty(self.capacity, np.uint8)
+        self._lib.oracle_digests(self._h, _u8p(out))
+        return out
+
+    def probe_stats(self) -> tuple[int, int]:
+        out = np.zeros(2, np.uint64)
+        self._lib.oracle_probe_stats(self._h, _u64p(out))
+        return int(out[0]), int(out[1])
+
+    def reset_probe_stats(self):
+        self._lib.oracle_reset_probe_stats(self._h)
