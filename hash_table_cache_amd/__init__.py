@@ -1,0 +1,114 @@
+"""Cache-semantic bucketed GPU hash table for MI355X (gfx950).
+
+The table and every operation on it live in the HIP library ``libhkv.so``
+behind the C ABI of ``include/hkv.h``; this package is its Python binding.
+``HashTable`` owns one table and allocates output tensors; the functions of
+``hash_table_cache_amd._native`` mirror the C entry points one to one.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _native
+from ._native import (  # noqa: F401
+    BUCKET_SLOTS,
+    EMPTY_KEY,
+    HKV_FLAG_SERIAL_INSERT,
+    LOCKED_KEY,
+    HkvError,
+    hkv_assign,
+    hkv_create,
+    hkv_destroy,
+    hkv_export_batch,
+    hkv_find,
+    hkv_get_options,
+    hkv_insert_or_assign,
+    hkv_size,
+)
+
+__all__ = ["HashTable", "HkvError", "BUCKET_SLOTS", "EMPTY_KEY", "LOCKED_KEY", "HKV_FLAG_SERIAL_INSERT"]
+
+
+class HashTable:
+    """One table on one GPU.
+
+    capacity: slots (a multiple of 128); dim: float32 values per row;
+    dual_bucket: score-based dual-bucket mode; values_on_host: value rows in
+    pinned host memory mapped into the GPU; serial_insert: apply inserts one key
+    at a time in input order (deterministic placement, slow).
+    """
+
+    def __init__(self, capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
+                 device: int = 0, serial_insert: bool = False):
+        self.capacity = int(capacity)
+        self.dim = int(dim)
+        self.dual_bucket = bool(dual_bucket)
+        self.values_on_host = bool(values_on_host)
+        self.device = int(device)
+        flags = HKV_FLAG_SERIAL_INSERT if serial_insert else 0
+        self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            hkv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def _dev(self):
+        return torch.device("cuda", self.device)
+
+    def find(self, keys, values_out=None, found_out=None, scores_out=None, with_scores=False, stream=None):
+        n = keys.numel()
+        if values_out is None:
+            values_out = torch.zeros((n, self.dim), dtype=torch.float32, device=self._dev())
+        if found_out is None:
+            found_out = torch.empty(n, dtype=torch.uint8, device=self._dev())
+        if scores_out is None and with_scores:
+            scores_out = torch.zeros(n, dtype=torch.int64, device=self._dev())
+        hkv_find(self._h, keys, values_out, found_out, scores_out, stream, dim=self.dim, device=self.device)
+        return values_out, found_out, scores_out
+
+    def insert_or_assign(self, keys, values, scores, stream=None) -> None:
+        hkv_insert_or_assign(self._h, keys, values, scores, stream, dim=self.dim, device=self.device)
+
+    def assign(self, keys, values=None, scores=None, stream=None) -> None:
+        hkv_assign(self._h, keys, values, scores, stream, dim=self.dim, device=self.device)
+
+    def size(self, stream=None) -> int:
+        return hkv_size(self._h, stream, device=self.device)
+
+    def export_batch(self, offset: int = 0, n_slots: int | None = None, with_values: bool = True, stream=None):
+        """Returns (keys, values, scores, pos) of the occupied slots in
+        [offset, offset + n_slots), in unspecified order; synchronizes."""
+        if n_slots is None:
+            n_slots = self.capacity - offset
+        m = max(0, min(int(n_slots), self.capacity - int(offset)))
+        dev = self._dev()
+        keys = torch.empty(max(m, 1), dtype=torch.int64, device=dev)
+        vals = torch.empty((max(m, 1), self.dim), dtype=torch.float32, device=dev) if with_values else None
+        scores = torch.empty(max(m, 1), dtype=torch.int64, device=dev)
+        pos = torch.empty(max(m, 1), dtype=torch.int64, device=dev)
+        count = torch.zeros(1, dtype=torch.int64, device=dev)
+        hkv_export_batch(self._h, offset, n_slots, keys, vals, scores, pos, count, stream,
+                         dim=self.dim, device=self.device)
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream), device=dev)
+        (stream or torch.cuda.current_stream(dev)).synchronize()
+        c = int(count.item())
+        return keys[:c], (vals[:c] if vals is not None else None), scores[:c], pos[:c]

@@ -1,0 +1,190 @@
+"""ctypes binding of ``libhkv.so`` (the C ABI of ``include/hkv.h``).
+
+Argument marshalling only: every step of every operation runs in the HIP
+library. Tensors are passed by ``data_ptr()``; the stream defaults to torch's
+current stream on the table's device. If the library has not been built the
+import of this module fails; there is no fallback implementation.
+
+64-bit keys and scores are ``torch.int64`` (or ``torch.uint64``) tensors that
+hold the unsigned bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "_lib" / "libhkv.so"
+
+HKV_OK = 0
+HKV_EINVAL = -1
+HKV_ENOMEM = -2
+HKV_EHIP = -3
+HKV_EUNSUPPORTED = -4
+HKV_FLAG_SERIAL_INSERT = 0x1
+BUCKET_SLOTS = 128
+EMPTY_KEY = 0xFFFFFFFFFFFFFFFF
+LOCKED_KEY = 0xFFFFFFFFFFFFFFFE
+
+# Every entry point declared in include/hkv.h.
+EXPORTS = (
+    "hkv_create",
+    "hkv_destroy",
+    "hkv_get_options",
+    "hkv_find",
+    "hkv_insert_or_assign",
+    "hkv_assign",
+    "hkv_size",
+    "hkv_export_batch",
+    "hkv_last_error",
+)
+
+
+class HkvOptions(ctypes.Structure):
+    _fields_ = [
+        ("capacity", ctypes.c_uint64),
+        ("dim", ctypes.c_uint32),
+        ("bucket_slots", ctypes.c_uint32),
+        ("dual_bucket", ctypes.c_uint32),
+        ("values_on_host", ctypes.c_uint32),
+        ("device", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class HkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"hkv status {status}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(
+            f"{LIB_PATH} is missing; build it with `python -m hash_table_cache_amd.build`"
+        )
+    L = ctypes.CDLL(str(LIB_PATH))
+    vp, u64, st = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32
+    L.hkv_create.argtypes = [ctypes.POINTER(HkvOptions), ctypes.POINTER(ctypes.c_void_p)]
+    L.hkv_create.restype = st
+    L.hkv_destroy.argtypes = [vp]
+    L.hkv_destroy.restype = st
+    L.hkv_get_options.argtypes = [vp, ctypes.POINTER(HkvOptions)]
+    L.hkv_get_options.restype = st
+    L.hkv_find.argtypes = [vp, u64, vp, vp, vp, vp, vp]
+    L.hkv_find.restype = st
+    L.hkv_insert_or_assign.argtypes = [vp, u64, vp, vp, vp, vp]
+    L.hkv_insert_or_assign.restype = st
+    L.hkv_assign.argtypes = [vp, u64, vp, vp, vp, vp]
+    L.hkv_assign.restype = st
+    L.hkv_size.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), vp]
+    L.hkv_size.restype = st
+    L.hkv_export_batch.argtypes = [vp, u64, u64, vp, vp, vp, vp, vp, vp]
+    L.hkv_export_batch.restype = st
+    L.hkv_last_error.argtypes = []
+    L.hkv_last_error.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != HKV_OK:
+        raise HkvError(status, lib.hkv_last_error().decode(errors="replace"))
+
+
+_U64_DTYPES = (torch.int64, torch.uint64)
+
+
+def _ptr(t, dtypes, numel, name, nullable=False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream, device: int):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def hkv_create(capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
+               device: int = 0, flags: int = 0) -> ctypes.c_void_p:
+    opt = HkvOptions(int(capacity), int(dim), BUCKET_SLOTS, int(bool(dual_bucket)),
+                     int(bool(values_on_host)), int(device), int(flags))
+    h = ctypes.c_void_p()
+    _check(lib.hkv_create(ctypes.byref(opt), ctypes.byref(h)))
+    return h
+
+
+def hkv_destroy(table) -> None:
+    _check(lib.hkv_destroy(table))
+
+
+def hkv_get_options(table) -> HkvOptions:
+    o = HkvOptions()
+    _check(lib.hkv_get_options(table, ctypes.byref(o)))
+    return o
+
+
+def hkv_find(table, keys, values_out, found_out, scores_out=None, stream=None, *, dim, device):
+    n = keys.numel()
+    _check(lib.hkv_find(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values_out, (torch.float32,), n * dim, "values_out"),
+        _ptr(found_out, (torch.uint8, torch.bool), n, "found_out"),
+        _ptr(scores_out, _U64_DTYPES, n, "scores_out", nullable=True),
+        _stream(stream, device)))
+
+
+def hkv_insert_or_assign(table, keys, values, scores, stream=None, *, dim, device):
+    n = keys.numel()
+    _check(lib.hkv_insert_or_assign(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values, (torch.float32,), n * dim, "values"),
+        _ptr(scores, _U64_DTYPES, n, "scores"),
+        _stream(stream, device)))
+
+
+def hkv_assign(table, keys, values=None, scores=None, stream=None, *, dim, device):
+    n = keys.numel()
+    _check(lib.hkv_assign(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values, (torch.float32,), n * dim, "values", nullable=True),
+        _ptr(scores, _U64_DTYPES, n, "scores", nullable=True),
+        _stream(stream, device)))
+
+
+def hkv_size(table, stream=None, *, device) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib.hkv_size(table, ctypes.byref(out), _stream(stream, device)))
+    return int(out.value)
+
+
+def hkv_export_batch(table, offset, n_slots, keys_out, values_out, scores_out, pos_out, count_out,
+                     stream=None, *, dim, device):
+    m = int(n_slots)
+    _check(lib.hkv_export_batch(
+        table, int(offset), m,
+        _ptr(keys_out, _U64_DTYPES, 0, "keys_out"),
+        _ptr(values_out, (torch.float32,), 0, "values_out", nullable=True),
+        _ptr(scores_out, _U64_DTYPES, 0, "scores_out", nullable=True),
+        _ptr(pos_out, _U64_DTYPES, 0, "pos_out", nullable=True),
+        _ptr(count_out, _U64_DTYPES, 1, "count_out"),
+        _stream(stream, device)))

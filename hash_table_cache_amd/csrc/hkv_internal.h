@@ -1,0 +1,50 @@
+// Internal interface between the host runtime (hkv_runtime.cpp) and the
+// gfx950 kernels (hkv_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hkv {
+
+// Device-side view of one table. Slot s of bucket b is position p = b*128 + s
+// in digests/keys/scores and row p of values (row-major, dim floats).
+struct TableView {
+  uint8_t* digests;   // [nb*128]  one-byte digest per slot; 0 marks an empty slot
+  uint64_t* keys;     // [nb*128]
+  uint64_t* scores;   // [nb*128]
+  float* values;      // [nb*128*dim]  HBM, or host-mapped pinned memory
+  uint32_t* occ;      // [nb]  occupied slots; slots [0, occ) are the occupied ones
+  uint32_t* head;     // [nb]  inserter chain heads; all 0xFFFFFFFF between calls
+  uint64_t nb;        // number of buckets
+  uint64_t nb_mask;   // nb - 1 when nb is a power of two
+  uint32_t dim;
+  uint32_t pow2;      // nb is a power of two
+  uint32_t dual;      // dual-bucket mode
+};
+
+// Row copies use 16-byte vectors when dim % 4 == 0 and every row pointer
+// involved is 16-byte aligned; the host decides and passes `vec4`.
+
+hipError_t launch_init(const TableView& t, hipStream_t s);
+
+hipError_t launch_find(const TableView& t, uint64_t n, const uint64_t* keys, float* values_out,
+                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s);
+
+hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys,
+                         const float* values, const uint64_t* scores, bool vec4, hipStream_t s);
+
+// next: [n] u32 workspace; target: [n] u32 workspace (dual mode only).
+hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
+                         const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
+                         bool serial, hipStream_t s);
+
+// Writes the number of occupied slots to *dev_out (device memory).
+hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s);
+
+hipError_t launch_export(const TableView& t, uint64_t begin, uint64_t end, uint64_t* keys_out,
+                         float* values_out, uint64_t* scores_out, uint64_t* pos_out,
+                         unsigned long long* count_out, bool vec4, hipStream_t s);
+
+}  // namespace hkv

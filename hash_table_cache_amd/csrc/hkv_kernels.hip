@@ -1,0 +1,763 @@
+// gfx950 kernels of the cache-semantic bucketed hash table.
+//
+// Method: "HierarchicalKV: A GPU Hash Table with Cache Semantics for
+// Continuous Online Embedding Storage" (arXiv 2603.17168).
+//   find      - §3.2, Algorithm 1 (one 128-byte digest line per bucket, full
+//               key compare only on digest match); two lines in dual mode (§3.4)
+//   assign    - §3.5 updater: value/score writes to resident keys only
+//   insert    - §3.3, Algorithm 2 (update / empty slot / evict-or-reject);
+//               §3.4, Algorithm 3 (dual-bucket D1/D2 selection)
+//   size, export - §3.5 readers, §4.1 export
+//
+// Work decomposition (wave64, CDNA4):
+//   * A "group" of G consecutive lanes of a wave serves one key. Lane l of a
+//     group holds digest bytes [l*128/G, (l+1)*128/G) of the bucket's line, so
+//     one vector load per lane fetches the whole 128-byte line coalesced.
+//     Digest compares are SWAR byte compares; the lane that owns a matching
+//     slot loads and compares that slot's key; a wave ballot picks the hit.
+//   * Value rows are moved by the whole group in 16-byte pieces.
+//   * Inserts need every bucket to see its keys one at a time (serializable
+//     per bucket). Instead of spin locks, a link kernel threads the batch's
+//     keys into one chain per target bucket with a single atomic exchange per
+//     key; in the second kernel the group of the chain's last element owns
+//     the bucket exclusively and applies the chain's keys one after another.
+//     No two groups ever write the same bucket inside a kernel, so no lock,
+//     CAS retry or cross-XCD cache maintenance is needed; kernel boundaries
+//     publish the result.
+//   * In the inserter, slot s of a bucket belongs to lane s/8 of the
+//     16-lane group: only that lane loads or stores the slot's key, score and
+//     digest, so every read-after-write inside a chain is same-thread.
+//
+// Digest encoding: the digest of a key is bits 32..39 of its hash, except that
+// the value 0 is stored as 1; 0 marks an empty slot, so empty slots never
+// produce a candidate. This only affects the filter, never a result.
+#include "hkv_internal.h"
+
+namespace hkv {
+namespace {
+
+constexpr int kSlots = 128;
+constexpr uint64_t kLockedKey = ~0ull - 1;  // keys >= this are reserved
+constexpr uint32_t kNoIdx = 0xFFFFFFFFu;    // chain end / empty chain head
+constexpr uint32_t kSkipIdx = 0xFFFFFFFEu;  // key takes no part in the insert
+constexpr uint64_t kSecondSalt = 0x9E3779B97F4A7C15ull;
+constexpr int kBlock = 256;
+constexpr int kInsG = 16;  // lanes per key in the inserter (8 slots per lane)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool is_reserved(uint64_t k) { return k >= kLockedKey; }
+
+// MurmurHash3's 64-bit finalizer, the table's hash (§3.2 names a Murmur3
+// variant without giving it).
+__device__ __forceinline__ uint64_t fmix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return k;
+}
+
+__device__ __forceinline__ uint32_t bucket_of(const TableView& t, uint64_t h) {
+  return t.pow2 ? static_cast<uint32_t>(h & t.nb_mask) : static_cast<uint32_t>(h % t.nb);
+}
+
+__device__ __forceinline__ uint32_t digest_of(uint64_t h) {
+  const uint32_t d = static_cast<uint32_t>(h >> 32) & 0xFFu;
+  return d == 0 ? 1u : d;
+}
+
+// 0x80 in every byte of x that is zero, 0 in the others. Exact: the low seven
+// bits are summed separately so no carry crosses a byte.
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
+  const uint32_t t = (x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+  return ~(t | x | 0x7F7F7F7Fu);
+}
+
+__device__ __forceinline__ int wave_lane() { return static_cast<int>(threadIdx.x & 63); }
+
+template <int G>
+__device__ __forceinline__ uint64_t group_bits(uint64_t ballot) {
+  const int base = wave_lane() & ~(G - 1);
+  const uint64_t m = (G == 64) ? ~0ull : ((1ull << G) - 1);
+  return (ballot >> base) & m;
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t group_min(uint64_t v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(v, o, G);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
+// Copies a row of dim floats with the G lanes of a group.
+template <int G, bool V4, bool NT>
+__device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* __restrict__ src,
+                                         uint32_t dim, int lane) {
+  if constexpr (V4) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+    f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+    const uint32_t n4 = dim >> 2;
+    for (uint32_t c = lane; c < n4; c += G) {
+      const f32x4 v = s4[c];
+      if constexpr (NT) {
+        __builtin_nontemporal_store(v, d4 + c);
+      } else {
+        d4[c] = v;
+      }
+    }
+  } else {
+    for (uint32_t c = lane; c < dim; c += G) dst[c] = src[c];
+  }
+}
+
+// Loads this lane's share (NW dwords) of a bucket's 128-byte digest line.
+template <int NW>
+__device__ __forceinline__ void load_digest_words(const uint8_t* line, int lane, uint32_t (&w)[NW]) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(line) + lane * NW;
+  if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < NW; q += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + q);
+      w[q] = v.x;
+      w[q + 1] = v.y;
+      w[q + 2] = v.z;
+      w[q + 3] = v.w;
+    }
+  }
+}
+
+// Candidate scan of one bucket for key k: every slot of this lane whose digest
+// byte equals the key's digest gets a full key compare. Returns the table
+// position of the hit or -1.
+template <int NW>
+__device__ __forceinline__ int64_t scan_line(const TableView& t, uint32_t b, const uint32_t (&w)[NW],
+                                             uint32_t pat, uint64_t k, int lane) {
+  int64_t hit = -1;
+  const uint64_t base = static_cast<uint64_t>(b) * kSlots + static_cast<uint64_t>(lane) * (NW * 4);
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    uint32_t z = zero_bytes(w[q] ^ pat);
+    while (z) {
+      const int byte = __builtin_ctz(z) >> 3;
+      z &= z - 1;
+      const uint64_t p = base + q * 4 + byte;
+      if (t.keys[p] == k) hit = static_cast<int64_t>(p);
+    }
+  }
+  return hit;
+}
+
+// Group-wide probe of the key's candidate bucket(s). Returns the hit position
+// (same value in every lane of the group) or -1.
+template <int G, bool DUAL>
+__device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane) {
+  constexpr int NW = kSlots / G / 4;
+  const uint64_t h = fmix64(k);
+  const uint32_t pat = digest_of(h) * 0x01010101u;
+  const uint32_t b1 = bucket_of(t, h);
+  uint32_t w1[NW];
+  load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
+  uint32_t b2 = b1;
+  uint32_t w2[NW];
+  if constexpr (DUAL) {
+    b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+    if (b2 != b1) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
+  }
+  int64_t hit = -1;
+  if (!is_reserved(k)) {
+    hit = scan_line<NW>(t, b1, w1, pat, k, lane);
+    if constexpr (DUAL) {
+      if (b2 != b1) {
+        const int64_t h2 = scan_line<NW>(t, b2, w2, pat, k, lane);
+        if (h2 >= 0) hit = h2;
+      }
+    }
+  }
+  const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
+  if (bits == 0) return -1;
+  return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
+}
+
+// ---------------------------------------------------------------- readers --
+
+template <int G, bool V4, bool DUAL>
+__global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
+                                                      const uint64_t* __restrict__ keys,
+                                                      float* __restrict__ out,
+                                                      uint8_t* __restrict__ found,
+                                                      uint64_t* __restrict__ scores_out) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
+  if (i >= n) return;  // groups are lane-aligned, so a whole group leaves together
+  const uint64_t k = keys[i];
+  const int64_t p = probe<G, DUAL>(t, k, lane);
+  if (p < 0) {
+    if (lane == 0) found[i] = 0;
+    return;
+  }
+  copy_row<G, V4, true>(out + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
+  if (lane == 0) {
+    found[i] = 1;
+    if (scores_out) scores_out[i] = t.scores[p];
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void size_kernel(const uint32_t* __restrict__ occ, uint64_t nb,
+                                                      unsigned long long* out) {
+  unsigned long long acc = 0;
+  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; b < nb;
+       b += static_cast<uint64_t>(gridDim.x) * kBlock)
+    acc += occ[b];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (wave_lane() == 0 && acc) atomicAdd(out, acc);
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0; }
+
+template <bool V4>
+__global__ __launch_bounds__(kBlock) void export_kernel(TableView t, uint64_t begin, uint64_t end,
+                                                        uint64_t* __restrict__ keys_out,
+                                                        float* __restrict__ values_out,
+                                                        uint64_t* __restrict__ scores_out,
+                                                        uint64_t* __restrict__ pos_out,
+                                                        unsigned long long* count) {
+  const uint64_t p = begin + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  bool live = false;
+  if (p < end) live = (p & (kSlots - 1)) < t.occ[p / kSlots];
+  const uint64_t bal = __ballot(live);
+  const int lane = wave_lane();
+  unsigned long long base = 0;
+  if (lane == 0 && bal) base = atomicAdd(count, static_cast<unsigned long long>(__popcll(bal)));
+  base = __shfl(base, 0, 64);
+  if (!live) return;
+  const uint64_t j = base + __popcll(bal & ((1ull << lane) - 1));
+  keys_out[j] = t.keys[p];
+  if (scores_out) scores_out[j] = t.scores[p];
+  if (pos_out) pos_out[j] = p;
+  if (values_out) copy_row<1, V4, false>(values_out + j * t.dim, t.values + p * t.dim, t.dim, 0);
+}
+
+// --------------------------------------------------------------- updaters --
+
+template <int G, bool V4, bool DUAL>
+__global__ __launch_bounds__(kBlock) void assign_kernel(TableView t, uint64_t n,
+                                                        const uint64_t* __restrict__ keys,
+                                                        const float* __restrict__ values,
+                                                        const uint64_t* __restrict__ scores) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
+  if (i >= n) return;
+  const int64_t p = probe<G, DUAL>(t, keys[i], lane);
+  if (p < 0) return;
+  if (values)
+    copy_row<G, V4, false>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+  if (scores && lane == 0) t.scores[p] = scores[i];
+}
+
+// -------------------------------------------------------------- inserters --
+
+// One bucket held by a 16-lane group: occupancy (group-uniform), this lane's
+// 8 digest bytes and, once the bucket has been found full, its 8 scores.
+struct Owned {
+  uint32_t b;
+  uint32_t occ;
+  uint32_t dig0, dig1;  // digest bytes of slots 8*lane .. 8*lane+7
+  uint64_t sc[8];       // scores of the same slots (valid when have_scores)
+  bool have_scores;
+};
+
+__device__ __forceinline__ void own_load(Owned& o, const TableView& t, uint32_t b, int lane) {
+  o.b = b;
+  uint32_t occ = 0;
+  if (lane == 0) occ = t.occ[b];  // lane 0 alone reads and writes the occupancy word
+  o.occ = __shfl(occ, 0, kInsG);
+  const uint2 v = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(b) * kSlots + lane * 8);
+  o.dig0 = v.x;
+  o.dig1 = v.y;
+  o.have_scores = false;
+}
+
+__device__ __forceinline__ void own_store_occ(const Owned& o, const TableView& t, int lane) {
+  if (lane == 0) t.occ[o.b] = o.occ;
+}
+
+__device__ __forceinline__ void own_load_scores(Owned& o, const TableView& t, int lane) {
+  if (o.have_scores) return;
+  const uint64_t* src = t.scores + static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(src + u);
+    o.sc[u] = v.x;
+    o.sc[u + 1] = v.y;
+  }
+  o.have_scores = true;
+}
+
+// Slot of key k in the owned bucket, or -1 (group-uniform).
+__device__ __forceinline__ int own_find(const Owned& o, const TableView& t, uint64_t k, uint32_t pat,
+                                        int lane) {
+  int hit = -1;
+  const int first = lane * 8;
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots;
+  uint32_t z0 = zero_bytes(o.dig0 ^ pat);
+  uint32_t z1 = zero_bytes(o.dig1 ^ pat);
+  while (z0) {
+    const int s = first + (__builtin_ctz(z0) >> 3);
+    z0 &= z0 - 1;
+    if (s < static_cast<int>(o.occ) && t.keys[base + s] == k) hit = s;
+  }
+  while (z1) {
+    const int s = first + 4 + (__builtin_ctz(z1) >> 3);
+    z1 &= z1 - 1;
+    if (s < static_cast<int>(o.occ) && t.keys[base + s] == k) hit = s;
+  }
+  const uint64_t bits = group_bits<kInsG>(__ballot(hit >= 0));
+  if (bits == 0) return -1;
+  return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, kInsG);
+}
+
+// Lowest (score, key) entry of a full owned bucket (group-uniform results).
+__device__ __forceinline__ void own_lowest(Owned& o, const TableView& t, int lane, uint64_t* min_score,
+                                           uint64_t* min_key, int* slot) {
+  own_load_scores(o, t, lane);
+  uint64_t ls = o.sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
+  const uint64_t gs = group_min<kInsG>(ls);
+  // Among the slots at the minimum score, the smallest key ranks lowest.
+  uint64_t lk = ~0ull;
+  int lslot = -1;
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (o.sc[u] == gs) {
+      const uint64_t kk = t.keys[base + u];
+      if (lslot < 0 || kk < lk) {
+        lk = kk;
+        lslot = lane * 8 + u;
+      }
+    }
+  }
+  const uint64_t gk = group_min<kInsG>(lslot >= 0 ? lk : ~0ull);
+  const uint64_t bits = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
+  *min_score = gs;
+  *min_key = gk;
+  *slot = __shfl(lslot, __ffsll(static_cast<unsigned long long>(bits)) - 1, kInsG);
+}
+
+// o.sc[u] = score for u == idx, written as selects on every element so the
+// array stays in registers.
+__device__ __forceinline__ void set_score_reg(Owned& o, int idx, uint64_t score) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) o.sc[u] = (u == idx) ? score : o.sc[u];
+}
+
+// Writes (key, digest, score) of slot s (by its owner lane) and keeps the
+// group's register copies current. The value row is written by the caller.
+__device__ __forceinline__ void own_write_slot(Owned& o, const TableView& t, int s, uint64_t k,
+                                               uint32_t d, uint64_t score, int lane) {
+  if (lane != (s >> 3)) return;
+  const uint64_t p = static_cast<uint64_t>(o.b) * kSlots + s;
+  t.keys[p] = k;
+  t.scores[p] = score;
+  t.digests[p] = static_cast<uint8_t>(d);
+  const int sh = (s & 3) * 8;
+  if (s & 4) {
+    o.dig1 = (o.dig1 & ~(0xFFu << sh)) | (d << sh);
+  } else {
+    o.dig0 = (o.dig0 & ~(0xFFu << sh)) | (d << sh);
+  }
+  if (o.have_scores) set_score_reg(o, s & 7, score);
+}
+
+__device__ __forceinline__ void own_write_score(Owned& o, const TableView& t, int s, uint64_t score,
+                                                int lane) {
+  if (lane != (s >> 3)) return;
+  t.scores[static_cast<uint64_t>(o.b) * kSlots + s] = score;
+  if (o.have_scores) set_score_reg(o, s & 7, score);
+}
+
+template <bool V4>
+__device__ __forceinline__ void own_write_row(const Owned& o, const TableView& t, int s,
+                                              const float* row, int lane) {
+  copy_row<kInsG, V4, false>(t.values + (static_cast<uint64_t>(o.b) * kSlots + s) * t.dim, row, t.dim,
+                             lane);
+}
+
+// Algorithm 2 for one key against an owned bucket: update if present, else
+// the lowest empty slot, else evict the lowest-ranked entry if the key ranks
+// higher, else reject. Empty slots are [occ, 128) because nothing is erased.
+template <bool V4>
+__device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_t k, const float* row,
+                                           uint64_t score, int lane) {
+  const uint64_t h = fmix64(k);
+  const uint32_t d = digest_of(h);
+  const int hit = own_find(o, t, k, d * 0x01010101u, lane);
+  if (hit >= 0) {
+    own_write_score(o, t, hit, score, lane);
+    own_write_row<V4>(o, t, hit, row, lane);
+    return;
+  }
+  if (o.occ < kSlots) {
+    const int s = static_cast<int>(o.occ);
+    own_write_slot(o, t, s, k, d, score, lane);
+    own_write_row<V4>(o, t, s, row, lane);
+    o.occ += 1;
+    return;
+  }
+  uint64_t ms, mk;
+  int vs;
+  own_lowest(o, t, lane, &ms, &mk, &vs);
+  if (score > ms || (score == ms && k > mk)) {
+    own_write_slot(o, t, vs, k, d, score, lane);
+    own_write_row<V4>(o, t, vs, row, lane);
+  }
+}
+
+// Link kernel, single-bucket mode: one thread per key pushes the key onto the
+// chain of its bucket. next[i] is the previously pushed key of that bucket,
+// kNoIdx for the first one (which will own the bucket), kSkipIdx for reserved keys.
+__global__ __launch_bounds__(kBlock) void link_single_kernel(TableView t, uint64_t n,
+                                                             const uint64_t* __restrict__ keys,
+                                                             uint32_t* __restrict__ next) {
+  const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t k = keys[i];
+  if (is_reserved(k)) {
+    next[i] = kSkipIdx;
+    return;
+  }
+  const uint32_t b = bucket_of(t, fmix64(k));
+  next[i] = __hip_atomic_exchange(t.head + b, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lowest (score, key) of a full bucket, read-only, 16 lanes (group-uniform).
+__device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int lane, uint64_t* ms,
+                                            uint64_t* mk) {
+  const uint64_t base = static_cast<uint64_t>(b) * kSlots + lane * 8;
+  uint64_t sc[8];
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
+    sc[u] = v.x;
+    sc[u + 1] = v.y;
+  }
+  uint64_t ls = sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = sc[u] < ls ? sc[u] : ls;
+  const uint64_t gs = group_min<kInsG>(ls);
+  uint64_t lk = ~0ull;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (sc[u] == gs) {
+      const uint64_t kk = t.keys[base + u];
+      lk = kk < lk ? kk : lk;
+    }
+  }
+  *ms = gs;
+  *mk = group_min<kInsG>(lk);
+}
+
+// Link kernel, dual-bucket mode: a 16-lane group per key chooses the bucket
+// the key will be applied to, from the table as it was before the batch
+// (Algorithm 3): the bucket holding it; else the less-occupied candidate if
+// either has room (tie: the first); else the candidate whose lowest-ranked
+// entry is lower. It then pushes the key onto that bucket's chain.
+__global__ __launch_bounds__(kBlock) void link_dual_kernel(TableView t, uint64_t n,
+                                                           const uint64_t* __restrict__ keys,
+                                                           uint32_t* __restrict__ next,
+                                                           uint32_t* __restrict__ target) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / kInsG;
+  const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
+  if (i >= n) return;
+  const uint64_t k = keys[i];
+  if (is_reserved(k)) {
+    if (lane == 0) next[i] = kSkipIdx;
+    return;
+  }
+  const uint64_t h = fmix64(k);
+  const uint32_t b1 = bucket_of(t, h);
+  const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+  uint32_t tb = b1;
+  if (b2 != b1) {
+    const int64_t p = probe<kInsG, true>(t, k, lane);
+    if (p >= 0) {
+      tb = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
+    } else {
+      const uint32_t o1 = t.occ[b1], o2 = t.occ[b2];
+      if (o1 < kSlots || o2 < kSlots) {
+        tb = (o1 <= o2) ? b1 : b2;
+      } else {
+        uint64_t s1, k1, s2, k2;
+        peek_lowest(t, b1, lane, &s1, &k1);
+        peek_lowest(t, b2, lane, &s2, &k2);
+        tb = (s2 < s1 || (s2 == s1 && k2 < k1)) ? b2 : b1;
+      }
+    }
+  }
+  if (lane == 0) {
+    target[i] = tb;
+    next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Owner kernel: the group of the chain's first-pushed key (next == kNoIdx)
+// owns the bucket, walks the chain from its head and applies each key in
+// turn, then resets the chain head for the next call.
+template <bool V4, bool DUAL>
+__global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
+                                                              const uint64_t* __restrict__ keys,
+                                                              const float* __restrict__ values,
+                                                              const uint64_t* __restrict__ scores,
+                                                              const uint32_t* __restrict__ next,
+                                                              const uint32_t* __restrict__ target) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / kInsG;
+  const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
+  if (i >= n) return;
+  if (next[i] != kNoIdx) return;
+  const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(keys[i]));
+  uint32_t c = 0;
+  if (lane == 0) c = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  c = __shfl(c, 0, kInsG);
+  Owned o;
+  own_load(o, t, b, lane);
+  const uint32_t occ0 = o.occ;
+  // A chain visits at most n distinct keys and ends at this group's own key;
+  // the index and step checks only guard against a corrupted chain.
+  for (uint64_t step = 0; c < n && step < n; ++step) {
+    own_upsert<V4>(o, t, keys[c], values + static_cast<uint64_t>(c) * t.dim, scores[c], lane);
+    if (c == static_cast<uint32_t>(i)) break;
+    c = next[c];
+  }
+  if (o.occ != occ0) own_store_occ(o, t, lane);
+  if (lane == 0)
+    __hip_atomic_store(t.head + b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Serial inserter: one 16-lane group applies the whole batch in input order
+// (Algorithm 2, or Algorithm 3 in dual mode, one key at a time).
+template <bool V4, bool DUAL>
+__global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t n,
+                                                           const uint64_t* __restrict__ keys,
+                                                           const float* __restrict__ values,
+                                                           const uint64_t* __restrict__ scores) {
+  if (threadIdx.x >= kInsG) return;
+  const int lane = static_cast<int>(threadIdx.x);
+  for (uint64_t i = 0; i < n; ++i) {
+    const uint64_t k = keys[i];
+    if (is_reserved(k)) continue;
+    const float* row = values + i * t.dim;
+    const uint64_t score = scores[i];
+    const uint64_t h = fmix64(k);
+    const uint32_t d = digest_of(h);
+    const uint32_t pat = d * 0x01010101u;
+    const uint32_t b1 = bucket_of(t, h);
+    const uint32_t b2 = DUAL ? bucket_of(t, fmix64(k ^ kSecondSalt)) : b1;
+    Owned o1;
+    own_load(o1, t, b1, lane);
+    if (!DUAL || b2 == b1) {
+      const uint32_t occ0 = o1.occ;
+      own_upsert<V4>(o1, t, k, row, score, lane);
+      if (o1.occ != occ0) own_store_occ(o1, t, lane);
+      continue;
+    }
+    int s = own_find(o1, t, k, pat, lane);
+    if (s >= 0) {
+      own_write_score(o1, t, s, score, lane);
+      own_write_row<V4>(o1, t, s, row, lane);
+      continue;
+    }
+    Owned o2;
+    own_load(o2, t, b2, lane);
+    s = own_find(o2, t, k, pat, lane);
+    if (s >= 0) {
+      own_write_score(o2, t, s, score, lane);
+      own_write_row<V4>(o2, t, s, row, lane);
+      continue;
+    }
+    if (o1.occ < kSlots || o2.occ < kSlots) {
+      Owned& o = (o1.occ <= o2.occ) ? o1 : o2;
+      s = static_cast<int>(o.occ);
+      own_write_slot(o, t, s, k, d, score, lane);
+      own_write_row<V4>(o, t, s, row, lane);
+      o.occ += 1;
+      own_store_occ(o, t, lane);
+      continue;
+    }
+    uint64_t ms1, mk1, ms2, mk2;
+    int v1, v2;
+    own_lowest(o1, t, lane, &ms1, &mk1, &v1);
+    own_lowest(o2, t, lane, &ms2, &mk2, &v2);
+    const bool second = ms2 < ms1 || (ms2 == ms1 && mk2 < mk1);
+    Owned& o = second ? o2 : o1;
+    const uint64_t ms = second ? ms2 : ms1, mk = second ? mk2 : mk1;
+    const int vs = second ? v2 : v1;
+    if (score > ms || (score == ms && k > mk)) {
+      own_write_slot(o, t, vs, k, d, score, lane);
+      own_write_row<V4>(o, t, vs, row, lane);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ setup --
+
+__global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
+  const uint64_t cap = t.nb * kSlots;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+  for (uint64_t p = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; p < cap; p += stride) {
+    t.keys[p] = ~0ull;
+    t.scores[p] = 0;
+    t.digests[p] = 0;
+    if (p < t.nb) {
+      t.occ[p] = 0;
+      t.head[p] = kNoIdx;
+    }
+  }
+}
+
+uint32_t grid_for(uint64_t threads) {
+  return static_cast<uint32_t>((threads + kBlock - 1) / kBlock);
+}
+
+// Lanes per key for find/assign: enough lanes to move a row in one or two
+// 16-byte pieces each, between 4 and 16.
+int lanes_for_dim(uint32_t dim) {
+  if (dim <= 16) return 4;
+  if (dim <= 32) return 8;
+  return 16;
+}
+
+template <int G, bool V4, bool DUAL>
+hipError_t find_g(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
+                  uint64_t* sc, hipStream_t s) {
+  hipLaunchKernelGGL((find_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), 0, s, t, n, keys,
+                     out, found, sc);
+  return hipGetLastError();
+}
+
+template <int G, bool V4, bool DUAL>
+hipError_t assign_g(const TableView& t, uint64_t n, const uint64_t* keys, const float* v,
+                    const uint64_t* sc, hipStream_t s) {
+  hipLaunchKernelGGL((assign_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), 0, s, t, n,
+                     keys, v, sc);
+  return hipGetLastError();
+}
+
+template <bool V4, bool DUAL>
+hipError_t find_d(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
+                  uint64_t* sc, hipStream_t s) {
+  switch (lanes_for_dim(t.dim)) {
+    case 4: return find_g<4, V4, DUAL>(t, n, keys, out, found, sc, s);
+    case 8: return find_g<8, V4, DUAL>(t, n, keys, out, found, sc, s);
+    default: return find_g<16, V4, DUAL>(t, n, keys, out, found, sc, s);
+  }
+}
+
+template <bool V4, bool DUAL>
+hipError_t assign_d(const TableView& t, uint64_t n, const uint64_t* keys, const float* v,
+                    const uint64_t* sc, hipStream_t s) {
+  switch (lanes_for_dim(t.dim)) {
+    case 4: return assign_g<4, V4, DUAL>(t, n, keys, v, sc, s);
+    case 8: return assign_g<8, V4, DUAL>(t, n, keys, v, sc, s);
+    default: return assign_g<16, V4, DUAL>(t, n, keys, v, sc, s);
+  }
+}
+
+template <bool V4, bool DUAL>
+hipError_t insert_d(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
+                    const uint64_t* scores, uint32_t* next, uint32_t* target, bool serial,
+                    hipStream_t s) {
+  if (serial) {
+    hipLaunchKernelGGL((upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), 0, s, t, n, keys, values,
+                       scores);
+    return hipGetLastError();
+  }
+  if (DUAL) {
+    hipLaunchKernelGGL(link_dual_kernel, dim3(grid_for(n * kInsG)), dim3(kBlock), 0, s, t, n, keys,
+                       next, target);
+  } else {
+    hipLaunchKernelGGL(link_single_kernel, dim3(grid_for(n)), dim3(kBlock), 0, s, t, n, keys, next);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n * kInsG)), dim3(kBlock), 0, s, t,
+                     n, keys, values, scores, next, target);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_init(const TableView& t, hipStream_t s) {
+  const uint64_t cap = t.nb * kSlots;
+  uint64_t blocks = (cap + kBlock - 1) / kBlock;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(init_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_find(const TableView& t, uint64_t n, const uint64_t* keys, float* values_out,
+                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s) {
+  if (t.dual)
+    return vec4 ? find_d<true, true>(t, n, keys, values_out, found_out, scores_out, s)
+                : find_d<false, true>(t, n, keys, values_out, found_out, scores_out, s);
+  return vec4 ? find_d<true, false>(t, n, keys, values_out, found_out, scores_out, s)
+              : find_d<false, false>(t, n, keys, values_out, found_out, scores_out, s);
+}
+
+hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
+                         const uint64_t* scores, bool vec4, hipStream_t s) {
+  if (t.dual)
+    return vec4 ? assign_d<true, true>(t, n, keys, values, scores, s)
+                : assign_d<false, true>(t, n, keys, values, scores, s);
+  return vec4 ? assign_d<true, false>(t, n, keys, values, scores, s)
+              : assign_d<false, false>(t, n, keys, values, scores, s);
+}
+
+hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
+                         const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
+                         bool serial, hipStream_t s) {
+  if (t.dual)
+    return vec4 ? insert_d<true, true>(t, n, keys, values, scores, next, target, serial, s)
+                : insert_d<false, true>(t, n, keys, values, scores, next, target, serial, s);
+  return vec4 ? insert_d<true, false>(t, n, keys, values, scores, next, target, serial, s)
+              : insert_d<false, false>(t, n, keys, values, scores, next, target, serial, s);
+}
+
+hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, dev_out);
+  uint64_t blocks = (t.nb + kBlock - 1) / kBlock;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(size_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s, t.occ, t.nb,
+                     dev_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const TableView& t, uint64_t begin, uint64_t end, uint64_t* keys_out,
+                         float* values_out, uint64_t* scores_out, uint64_t* pos_out,
+                         unsigned long long* count_out, bool vec4, hipStream_t s) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, count_out);
+  if (end > begin) {
+    if (vec4)
+      hipLaunchKernelGGL(export_kernel<true>, dim3(grid_for(end - begin)), dim3(kBlock), 0, s, t, begin,
+                         end, keys_out, values_out, scores_out, pos_out, count_out);
+    else
+      hipLaunchKernelGGL(export_kernel<false>, dim3(grid_for(end - begin)), dim3(kBlock), 0, s, t, begin,
+                         end, keys_out, values_out, scores_out, pos_out, count_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hkv

@@ -1,0 +1,405 @@
+// Host runtime of the C ABI declared in include/hkv.h: argument validation,
+// table storage, workspace management and reader/updater/inserter ordering.
+//
+// Group ordering follows the compatibility matrix of §3.5 (Table 4) of
+// "HierarchicalKV: A GPU Hash Table with Cache Semantics for Continuous Online
+// Embedding Storage": readers may overlap readers, updaters may overlap
+// updaters, inserters overlap nothing. The paper enforces it with host
+// counters mirrored to the device by a propagation kernel (§4.4); here every
+// call instead makes its own stream wait (hipStreamWaitEvent) on the last
+// event recorded by each incompatible group on every other stream, then
+// records its own event. The host never blocks, and calls issued on a single
+// stream need no waits at all because stream order already serializes them.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hkv.h"
+#include "hkv_internal.h"
+
+#define HKV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr uint64_t kSlots = HKV_BUCKET_SLOTS;
+constexpr uint64_t kMaxBatch = 0xFFFFFFFDull;  // indices 0xFFFFFFFE/F are chain markers
+constexpr uint32_t kMaxDim = 1u << 20;
+
+enum Group { kReader = 0, kUpdater = 1, kInserter = 2 };
+
+bool groups_conflict(int a, int b) { return !(a == b && a != kInserter); }
+
+thread_local std::string g_error;
+
+hkv_status fail(hkv_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+hkv_status fail_hip(hipError_t e, const char* what) {
+  return fail(HKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct StreamEvent {
+  hipStream_t stream;
+  hipEvent_t event;
+};
+
+// Makes `device` current for the lifetime of the guard.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int device) : target_(device) {
+    err_ = hipGetDevice(&prev_);
+    if (err_ == hipSuccess && prev_ != target_) err_ = hipSetDevice(target_);
+  }
+  ~DeviceGuard() {
+    if (err_ == hipSuccess && prev_ != target_) (void)hipSetDevice(prev_);
+  }
+  hipError_t error() const { return err_; }
+
+ private:
+  int prev_ = -1;
+  int target_;
+  hipError_t err_;
+};
+
+}  // namespace
+
+struct hkv_table {
+  hkv_options opt{};
+  hkv::TableView view{};
+  void* values_host = nullptr;  // hipHostMalloc base when values live in host memory
+  uint32_t* ws_next = nullptr;  // inserter workspace
+  uint32_t* ws_target = nullptr;
+  uint64_t ws_cap = 0;
+  unsigned long long* size_dev = nullptr;
+  unsigned long long* size_host = nullptr;  // pinned
+  std::mutex mu;
+  std::vector<StreamEvent> last[3];  // per group: last event recorded on each stream
+};
+
+namespace {
+
+void free_storage(hkv_table* t) {
+  hkv::TableView& v = t->view;
+  if (v.digests) (void)hipFree(v.digests);
+  if (v.keys) (void)hipFree(v.keys);
+  if (v.scores) (void)hipFree(v.scores);
+  if (v.occ) (void)hipFree(v.occ);
+  if (v.head) (void)hipFree(v.head);
+  if (t->values_host) {
+    (void)hipHostFree(t->values_host);
+  } else if (v.values) {
+    (void)hipFree(v.values);
+  }
+  if (t->ws_next) (void)hipFree(t->ws_next);
+  if (t->ws_target) (void)hipFree(t->ws_target);
+  if (t->size_dev) (void)hipFree(t->size_dev);
+  if (t->size_host) (void)hipHostFree(t->size_host);
+  for (auto& list : t->last)
+    for (auto& r : list) (void)hipEventDestroy(r.event);
+}
+
+// Checks that [p, p + bytes) is memory the table's GPU can access: device
+// memory of that GPU, or pinned/mapped host memory, inside one allocation.
+hkv_status check_buffer(const hkv_table* t, const void* p, uint64_t bytes, const char* what) {
+  if (!p) return fail(HKV_EINVAL, "%s is NULL", what);
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof(a));
+  hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess || a.type == hipMemoryTypeUnregistered) {
+    (void)hipGetLastError();
+    return fail(HKV_EINVAL, "%s (%p) is not device-accessible memory (pageable host memory?)", what, p);
+  }
+  if (a.type == hipMemoryTypeDevice && a.device != t->opt.device)
+    return fail(HKV_EINVAL, "%s lives on device %d, table on device %d", what, a.device, t->opt.device);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e == hipSuccess && base && size) {
+    const uint64_t off = reinterpret_cast<uintptr_t>(p) - reinterpret_cast<uintptr_t>(base);
+    if (off > size || bytes > size - off)
+      return fail(HKV_EINVAL, "%s holds %llu bytes past %p, call needs %llu", what,
+                  static_cast<unsigned long long>(size - off), p, static_cast<unsigned long long>(bytes));
+  } else {
+    (void)hipGetLastError();
+  }
+  return HKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Makes stream s wait for every outstanding call of a group incompatible with g
+// that was issued on another stream. Caller holds t->mu.
+hkv_status order_before(hkv_table* t, int g, hipStream_t s) {
+  for (int h = 0; h < 3; ++h) {
+    if (!groups_conflict(g, h)) continue;
+    for (auto& r : t->last[h]) {
+      if (r.stream == s) continue;
+      const hipError_t q = hipEventQuery(r.event);
+      if (q == hipSuccess) continue;
+      if (q != hipErrorNotReady) (void)hipGetLastError();
+      const hipError_t e = hipStreamWaitEvent(s, r.event, 0);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent");
+    }
+  }
+  return HKV_OK;
+}
+
+// Records group g's completion event on stream s. Caller holds t->mu.
+hkv_status record_after(hkv_table* t, int g, hipStream_t s) {
+  hipEvent_t ev = nullptr;
+  for (auto& r : t->last[g])
+    if (r.stream == s) ev = r.event;
+  if (!ev) {
+    const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    t->last[g].push_back({s, ev});
+  }
+  const hipError_t e = hipEventRecord(ev, s);
+  if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+  return HKV_OK;
+}
+
+// Waits for every recorded inserter call (used before replacing the workspace).
+hkv_status drain_group(hkv_table* t, int g) {
+  for (auto& r : t->last[g]) {
+    const hipError_t e = hipEventSynchronize(r.event);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+  }
+  return HKV_OK;
+}
+
+hkv_status ensure_workspace(hkv_table* t, uint64_t n) {
+  if (n <= t->ws_cap) return HKV_OK;
+  hkv_status st = drain_group(t, kInserter);
+  if (st != HKV_OK) return st;
+  uint64_t cap = t->ws_cap ? t->ws_cap : 1024;
+  while (cap < n) cap *= 2;
+  if (cap > kMaxBatch) cap = kMaxBatch;
+  if (t->ws_next) (void)hipFree(t->ws_next);
+  if (t->ws_target) (void)hipFree(t->ws_target);
+  t->ws_next = t->ws_target = nullptr;
+  t->ws_cap = 0;
+  if (hipMalloc(&t->ws_next, cap * sizeof(uint32_t)) != hipSuccess ||
+      (t->opt.dual_bucket && hipMalloc(&t->ws_target, cap * sizeof(uint32_t)) != hipSuccess)) {
+    (void)hipGetLastError();
+    if (t->ws_next) (void)hipFree(t->ws_next);
+    t->ws_next = nullptr;
+    return fail(HKV_ENOMEM, "inserter workspace of %llu entries", static_cast<unsigned long long>(cap));
+  }
+  t->ws_cap = cap;
+  return HKV_OK;
+}
+
+}  // namespace
+
+HKV_API const char* hkv_last_error(void) { return g_error.c_str(); }
+
+HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
+  if (!out) return fail(HKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!o) return fail(HKV_EINVAL, "options is NULL");
+  if (o->capacity == 0 || o->capacity % kSlots != 0)
+    return fail(HKV_EINVAL, "capacity %llu is not a positive multiple of 128",
+                static_cast<unsigned long long>(o->capacity));
+  if (o->capacity / kSlots > 0xFFFFFFFFull)
+    return fail(HKV_EINVAL, "capacity %llu exceeds 2^32 buckets", static_cast<unsigned long long>(o->capacity));
+  if (o->dim == 0 || o->dim > kMaxDim) return fail(HKV_EINVAL, "dim %u outside [1, %u]", o->dim, kMaxDim);
+  if (o->bucket_slots != 0 && o->bucket_slots != kSlots)
+    return fail(HKV_EINVAL, "bucket_slots %u: only 128-slot buckets exist", o->bucket_slots);
+  if (o->dual_bucket > 1 || o->values_on_host > 1) return fail(HKV_EINVAL, "dual_bucket/values_on_host must be 0 or 1");
+  if (o->flags & ~HKV_FLAG_SERIAL_INSERT) return fail(HKV_EINVAL, "unknown flags 0x%x", o->flags);
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev == 0) {
+    (void)hipGetLastError();
+    return fail(HKV_EHIP, "no HIP device available");
+  }
+  if (o->device < 0 || o->device >= ndev) return fail(HKV_EINVAL, "device %d outside [0, %d)", o->device, ndev);
+
+  hkv_table* t = new (std::nothrow) hkv_table();
+  if (!t) return fail(HKV_ENOMEM, "host allocation");
+  t->opt = *o;
+  t->opt.bucket_slots = kSlots;
+  DeviceGuard dg(o->device);
+  if (dg.error() != hipSuccess) {
+    delete t;
+    return fail_hip(dg.error(), "hipSetDevice");
+  }
+  const uint64_t cap = o->capacity, nb = cap / kSlots;
+  hkv::TableView& v = t->view;
+  v.nb = nb;
+  v.pow2 = (nb & (nb - 1)) == 0;
+  v.nb_mask = v.pow2 ? nb - 1 : 0;
+  v.dim = o->dim;
+  v.dual = o->dual_bucket;
+  const uint64_t value_bytes = cap * o->dim * sizeof(float);
+  bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
+            hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
+            hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&t->size_dev, 8) == hipSuccess &&
+            hipHostMalloc(&t->size_host, 8, hipHostMallocDefault) == hipSuccess;
+  if (ok) {
+    if (o->values_on_host) {
+      ok = hipHostMalloc(&t->values_host, value_bytes, hipHostMallocMapped) == hipSuccess &&
+           hipHostGetDevicePointer(reinterpret_cast<void**>(&v.values), t->values_host, 0) == hipSuccess;
+    } else {
+      ok = hipMalloc(&v.values, value_bytes) == hipSuccess;
+    }
+  }
+  if (!ok) {
+    (void)hipGetLastError();
+    free_storage(t);
+    delete t;
+    return fail(HKV_ENOMEM, "table storage for capacity %llu, dim %u (%s values)",
+                static_cast<unsigned long long>(cap), o->dim, o->values_on_host ? "host" : "device");
+  }
+  e = hkv::launch_init(v, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    free_storage(t);
+    delete t;
+    return fail_hip(e, "table initialisation");
+  }
+  *out = t;
+  return HKV_OK;
+}
+
+HKV_API hkv_status hkv_destroy(hkv_table* t) {
+  if (!t) return HKV_OK;
+  {
+    std::lock_guard<std::mutex> lk(t->mu);
+    DeviceGuard dg(t->opt.device);
+    for (int g = 0; g < 3; ++g) (void)drain_group(t, g);
+    free_storage(t);
+  }
+  delete t;
+  return HKV_OK;
+}
+
+HKV_API hkv_status hkv_get_options(const hkv_table* t, hkv_options* out) {
+  if (!t || !out) return fail(HKV_EINVAL, "NULL argument");
+  *out = t->opt;
+  return HKV_OK;
+}
+
+HKV_API hkv_status hkv_find(hkv_table* t, uint64_t n, const uint64_t* keys, float* values_out,
+                            uint8_t* found_out, uint64_t* scores_out, hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values_out, n * dim * 4, "values_out")) != HKV_OK) return st;
+  if ((st = check_buffer(t, found_out, n, "found_out")) != HKV_OK) return st;
+  if (scores_out && (st = check_buffer(t, scores_out, n * 8, "scores_out")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && aligned16(values_out);
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  if ((st = order_before(t, kReader, stream)) != HKV_OK) return st;
+  const hipError_t e = hkv::launch_find(t->view, n, keys, values_out, found_out, scores_out, vec4, stream);
+  if (e != hipSuccess) return fail_hip(e, "find launch");
+  return record_after(t, kReader, stream);
+}
+
+HKV_API hkv_status hkv_insert_or_assign(hkv_table* t, uint64_t n, const uint64_t* keys,
+                                        const float* values, const uint64_t* scores,
+                                        hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
+  if ((st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && aligned16(values);
+  const bool serial = (t->opt.flags & HKV_FLAG_SERIAL_INSERT) != 0;
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  if (!serial && (st = ensure_workspace(t, n)) != HKV_OK) return st;
+  if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
+  const hipError_t e =
+      hkv::launch_insert(t->view, n, keys, values, scores, t->ws_next, t->ws_target, vec4, serial, stream);
+  if (e != hipSuccess) return fail_hip(e, "insert_or_assign launch");
+  return record_after(t, kInserter, stream);
+}
+
+HKV_API hkv_status hkv_assign(hkv_table* t, uint64_t n, const uint64_t* keys, const float* values,
+                              const uint64_t* scores, hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (!values && !scores) return fail(HKV_EINVAL, "assign needs values or scores");
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if (values && (st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
+  if (scores && (st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && (!values || aligned16(values));
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  if ((st = order_before(t, kUpdater, stream)) != HKV_OK) return st;
+  const hipError_t e = hkv::launch_assign(t->view, n, keys, values, scores, vec4, stream);
+  if (e != hipSuccess) return fail_hip(e, "assign launch");
+  return record_after(t, kUpdater, stream);
+}
+
+HKV_API hkv_status hkv_size(hkv_table* t, uint64_t* out_host, hipStream_t stream) {
+  if (!t || !out_host) return fail(HKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  hkv_status st = order_before(t, kReader, stream);
+  if (st != HKV_OK) return st;
+  hipError_t e = hkv::launch_size(t->view, t->size_dev, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(t->size_host, t->size_dev, sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return fail_hip(e, "size launch");
+  if ((st = record_after(t, kReader, stream)) != HKV_OK) return st;
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+  *out_host = *t->size_host;
+  return HKV_OK;
+}
+
+HKV_API hkv_status hkv_export_batch(hkv_table* t, uint64_t offset, uint64_t n_slots, uint64_t* keys_out,
+                                    float* values_out, uint64_t* scores_out, uint64_t* pos_out,
+                                    uint64_t* count_out, hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  const uint64_t cap = t->opt.capacity;
+  const uint64_t begin = offset < cap ? offset : cap;
+  const uint64_t end = (n_slots > cap - begin) ? cap : begin + n_slots;
+  const uint64_t m = end - begin;
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, count_out, 8, "count_out")) != HKV_OK) return st;
+  if (m > 0) {
+    if ((st = check_buffer(t, keys_out, m * 8, "keys_out")) != HKV_OK) return st;
+    if (values_out && (st = check_buffer(t, values_out, m * dim * 4, "values_out")) != HKV_OK) return st;
+    if (scores_out && (st = check_buffer(t, scores_out, m * 8, "scores_out")) != HKV_OK) return st;
+    if (pos_out && (st = check_buffer(t, pos_out, m * 8, "pos_out")) != HKV_OK) return st;
+  }
+  const bool vec4 = dim % 4 == 0 && (!values_out || aligned16(values_out));
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  if ((st = order_before(t, kReader, stream)) != HKV_OK) return st;
+  const hipError_t e = hkv::launch_export(t->view, begin, end, keys_out, values_out, scores_out, pos_out,
+                                          reinterpret_cast<unsigned long long*>(count_out), vec4, stream);
+  if (e != hipSuccess) return fail_hip(e, "export launch");
+  return record_after(t, kReader, stream);
+}

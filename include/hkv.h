@@ -1,0 +1,176 @@
+/*
+ * hkv.h - C ABI of a cache-semantic bucketed GPU hash table for gfx950.
+ *
+ * The table follows "HierarchicalKV: A GPU Hash Table with Cache Semantics for
+ * Continuous Online Embedding Storage" (arXiv 2603.17168):
+ *   - §3.2 and Figure 4: buckets of 128 slots; each bucket has a contiguous
+ *     128-byte line of one-byte digests, 64-bit keys, 64-bit scores and value
+ *     rows addressed by (bucket, slot) position; no rehash, chain or stash.
+ *   - §3.3, Algorithm 2: a full bucket resolves an upsert in place by evicting
+ *     its lowest-score entry or by refusing admission to the incoming key.
+ *   - §3.4, Algorithm 3: optional score-based dual-bucket selection.
+ *   - §3.5, Table 4: readers (find, size, export), updaters (assign) and
+ *     inserters (insert_or_assign); readers may overlap readers and updaters
+ *     may overlap updaters, every other pair is exclusive.
+ *   - §3.6 and §4.2: optional placement of value rows in pinned host memory
+ *     mapped into the GPU address space, keys/digests/scores staying in HBM.
+ *
+ * Types: keys and scores are uint64_t, values are float32 rows of `dim`
+ * elements stored row-major (n x dim for batches). A full table is the normal
+ * operating state, not an error (Definition 2.1, CS1/CS2).
+ *
+ * Conventions shared by every call below:
+ *   - All array arguments are caller-owned, contiguous, and must be readable
+ *     (inputs) or writable (outputs) by the table's GPU: device memory or
+ *     pinned/mapped host memory. Pageable host pointers are rejected with
+ *     HKV_EINVAL before anything is enqueued.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) except
+ *     hkv_size. Inputs must stay valid and outputs unread until the stream has
+ *     passed the call.
+ *   - Group ordering (§3.5, Table 4) is enforced with stream/event ordering:
+ *     a call waits, on its own stream, for every outstanding call of an
+ *     incompatible group issued earlier on another stream. The host never
+ *     blocks for this. Several host threads may call concurrently.
+ *   - Arguments are validated synchronously; on any error nothing is enqueued,
+ *     the call returns a negative status and hkv_last_error() describes it.
+ *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 3 keys.
+ *   - The reserved keys HKV_EMPTY_KEY and HKV_LOCKED_KEY always miss in find
+ *     and are skipped by insert_or_assign and assign.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef HKV_H_
+#define HKV_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hkv_table hkv_table;
+typedef int32_t hkv_status;
+
+#define HKV_OK 0
+#define HKV_EINVAL (-1)       /* bad argument (null, size, alignment, pointer kind) */
+#define HKV_ENOMEM (-2)       /* device or pinned host allocation failed */
+#define HKV_EHIP (-3)         /* a HIP runtime call or kernel launch failed */
+#define HKV_EUNSUPPORTED (-4) /* valid request this build does not implement */
+
+#define HKV_BUCKET_SLOTS 128u
+/* Reserved key values: an empty slot and the slot-lock sentinel (§4.4). */
+#define HKV_EMPTY_KEY 0xFFFFFFFFFFFFFFFFull
+#define HKV_LOCKED_KEY 0xFFFFFFFFFFFFFFFEull
+
+/* Option flags. */
+/* The inserter applies a batch one key at a time, in input order, in a single
+ * group of lanes. Slow; gives run-to-run identical slot placement and, in
+ * dual-bucket mode, exactly Algorithm 3's sequential decisions. */
+#define HKV_FLAG_SERIAL_INSERT 0x1u
+
+typedef struct hkv_options {
+  uint64_t capacity;        /* slots; a positive multiple of 128 (§3.2). B = capacity / 128 buckets */
+  uint32_t dim;             /* float32 elements per value row, >= 1 */
+  uint32_t bucket_slots;    /* must be 128 (or 0, meaning 128) */
+  uint32_t dual_bucket;     /* 0: single-bucket (§3.2); 1: score-based dual-bucket (§3.4) */
+  uint32_t values_on_host;  /* 0: value rows in HBM; 1: in pinned, GPU-mapped host memory (§3.6) */
+  int32_t device;           /* HIP device ordinal that owns the table */
+  uint32_t flags;           /* HKV_FLAG_* */
+} hkv_options;
+
+/*
+ * hkv_create - allocate an empty table (§3.2 layout, §4.2 placement).
+ * Storage per slot: key 8 B + score 8 B + digest 1 B in HBM (§5.1, memory
+ * overhead), plus a value row of 4*dim bytes in HBM or in pinned host memory.
+ * Every slot starts empty. The table owns all of its storage.
+ * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128,
+ * dim == 0, bucket_slots not 128, bad device), HKV_ENOMEM, HKV_EHIP.
+ * On error *out is set to NULL.
+ */
+hkv_status hkv_create(const hkv_options* options, hkv_table** out);
+
+/* hkv_destroy - wait for the table's outstanding work, free everything.
+ * NULL is accepted and ignored. */
+hkv_status hkv_destroy(hkv_table* table);
+
+/* hkv_get_options - copy the options the table was created with. */
+hkv_status hkv_get_options(const hkv_table* table, hkv_options* out);
+
+/*
+ * hkv_find - reader (§3.2, Algorithm 1; dual buckets per §3.4).
+ * For each i < n: if keys[i] is resident, copies its value row to
+ * values_out[i*dim .. i*dim+dim), sets found_out[i] = 1 and, when scores_out is
+ * not NULL, scores_out[i] = its score. Otherwise sets found_out[i] = 0 and
+ * leaves values_out's row and scores_out[i] untouched. Scores in the table are
+ * never modified. Duplicate keys in the batch are allowed.
+ *   keys       [n] uint64, input
+ *   values_out [n*dim] float32, output (16-byte alignment enables wide copies)
+ *   found_out  [n] uint8, output
+ *   scores_out [n] uint64, output, nullable
+ */
+hkv_status hkv_find(hkv_table* table, uint64_t n, const uint64_t* keys, float* values_out,
+                    uint8_t* found_out, uint64_t* scores_out, hipStream_t stream);
+
+/*
+ * hkv_insert_or_assign - inserter (§3.3, Algorithm 2; §3.4, Algorithm 3).
+ * For each non-reserved key: if resident, its value row and score are
+ * overwritten; else it is written to an empty slot of its bucket (dual mode:
+ * of the less-occupied candidate bucket); else the lowest-ranked entry of the
+ * full bucket (dual mode: of the two buckets, the lower one) is evicted if the
+ * incoming key ranks higher, and the key is rejected otherwise. Rank is the
+ * pair (score, key) ordered lexicographically, which fixes ties. None of these
+ * outcomes is an error.
+ * Keys within one batch must be distinct for a deterministic result; with
+ * duplicates, which occurrence ends up stored is unspecified (the table stays
+ * consistent). For single-bucket tables and batches of distinct keys whose
+ * scores never decrease over time, the resulting bucket contents equal those
+ * of applying the batch one key at a time, whatever the in-batch order.
+ *   keys   [n] uint64, input
+ *   values [n*dim] float32, input
+ *   scores [n] uint64, input, required
+ * The call uses a table-owned workspace of 8*n bytes, grown on demand.
+ */
+hkv_status hkv_insert_or_assign(hkv_table* table, uint64_t n, const uint64_t* keys,
+                                const float* values, const uint64_t* scores,
+                                hipStream_t stream);
+
+/*
+ * hkv_assign - updater (§3.5): overwrites the value row (when values is not
+ * NULL) and the score (when scores is not NULL) of keys already resident.
+ * Absent and reserved keys are ignored; the bucket structure never changes.
+ * values and scores may not both be NULL (HKV_EINVAL).
+ *   keys   [n] uint64, input
+ *   values [n*dim] float32, input, nullable
+ *   scores [n] uint64, input, nullable
+ */
+hkv_status hkv_assign(hkv_table* table, uint64_t n, const uint64_t* keys, const float* values,
+                      const uint64_t* scores, hipStream_t stream);
+
+/*
+ * hkv_size - reader (§3.5): number of resident entries. Enqueues the count on
+ * `stream`, synchronizes that stream, and stores the result in *out_host.
+ */
+hkv_status hkv_size(hkv_table* table, uint64_t* out_host, hipStream_t stream);
+
+/*
+ * hkv_export_batch - reader (§4.1, export for checkpointing): scans slot
+ * positions p in [offset, offset + n_slots) clipped to [0, capacity), where
+ * p = bucket * 128 + slot, and writes every occupied one, compacted, to the
+ * outputs: keys_out[j], values_out[j*dim ..), scores_out[j], pos_out[j] = p.
+ * *count_out (a device-accessible uint64) receives the number written; it is
+ * reset by the call itself. Output order is unspecified. Outputs must hold
+ * n_slots entries (clipped). values_out, scores_out and pos_out are nullable.
+ */
+hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
+                            uint64_t* keys_out, float* values_out, uint64_t* scores_out,
+                            uint64_t* pos_out, uint64_t* count_out, hipStream_t stream);
+
+/* hkv_last_error - description of the last failure on the calling thread. */
+const char* hkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HKV_H_ */

@@ -1,0 +1,101 @@
+"""The C ABI library: it loads, exports every entry point include/hkv.h
+declares, and rejects bad arguments before touching a GPU. No kernels run."""
+
+import ctypes
+import pathlib
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+HEADER = pathlib.Path(ROOT) / "include" / "hkv.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(hkv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted([
+        "hkv_create", "hkv_destroy", "hkv_get_options", "hkv_find", "hkv_insert_or_assign",
+        "hkv_assign", "hkv_size", "hkv_export_batch", "hkv_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    from hash_table_cache_amd import _native
+
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_native.LIB_PATH)], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(_native.lib, name) is not None
+    assert set(_native.EXPORTS) == set(declared_functions())
+    # nothing but the ABI is exported from the library's own code
+    assert {n for n in exported if n.startswith("hkv")} == set(declared_functions())
+
+
+def test_oracle_library_exports():
+    import oracle
+
+    L = oracle.lib()
+    for name in ["oracle_create", "oracle_find", "oracle_insert_or_assign", "oracle_assign",
+                 "oracle_size", "oracle_export", "oracle_route"]:
+        assert getattr(L, name) is not None
+
+
+def _create(**kw):
+    from hash_table_cache_amd import _native
+
+    o = dict(capacity=1024, dim=8, bucket_slots=128, dual_bucket=0, values_on_host=0, device=0, flags=0)
+    o.update(kw)
+    opt = _native.HkvOptions(o["capacity"], o["dim"], o["bucket_slots"], o["dual_bucket"],
+                             o["values_on_host"], o["device"], o["flags"])
+    h = ctypes.c_void_p()
+    st = _native.lib.hkv_create(ctypes.byref(opt), ctypes.byref(h))
+    return st, h, _native.lib.hkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(capacity=0), "multiple of 128"),
+    (dict(capacity=1000), "multiple of 128"),
+    (dict(dim=0), "dim"),
+    (dict(bucket_slots=64), "128-slot"),
+    (dict(dual_bucket=2), "0 or 1"),
+    (dict(flags=0x80), "flags"),
+])
+def test_create_rejects_bad_options(kw, needle):
+    from hash_table_cache_amd import _native
+
+    st, h, msg = _create(**kw)
+    assert st == _native.HKV_EINVAL
+    assert h.value is None
+    assert needle in msg
+
+
+def test_null_arguments():
+    from hash_table_cache_amd import _native
+
+    L = _native.lib
+    assert L.hkv_create(None, None) == _native.HKV_EINVAL
+    assert L.hkv_find(None, 1, None, None, None, None, None) == _native.HKV_EINVAL
+    assert L.hkv_insert_or_assign(None, 1, None, None, None, None) == _native.HKV_EINVAL
+    assert L.hkv_assign(None, 1, None, None, None, None) == _native.HKV_EINVAL
+    assert L.hkv_export_batch(None, 0, 1, None, None, None, None, None, None) == _native.HKV_EINVAL
+    out = ctypes.c_uint64()
+    assert L.hkv_size(None, ctypes.byref(out), None) == _native.HKV_EINVAL
+    assert L.hkv_destroy(None) == _native.HKV_OK
+    assert "NULL" in L.hkv_last_error().decode()
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device error path")
+def test_create_without_device_reports_hip_error():
+    from hash_table_cache_amd import _native
+
+    st, h, msg = _create()
+    assert st == _native.HKV_EHIP
+    assert "no HIP device" in msg
