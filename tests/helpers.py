@@ -18,6 +18,8 @@ SLOTS = 128
 
 
 def as_u64(a) -> np.ndarray:
+    if not isinstance(a, np.ndarray):
+        return np.array([int(x) for x in a], dtype=np.uint64)
     a = np.ascontiguousarray(a)
     if a.dtype == np.int64:
         return a.view(np.uint64)
