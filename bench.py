@@ -1,0 +1,321 @@
+"""Find / upsert throughput of the cache-semantic hash table on one MI355X.
+
+Workload (defaults): four single-bucket tables of 2^26 slots with dim-64
+float32 rows, pre-filled with uniform distinct 64-bit keys (score = batch
+counter) to load factors 0.50, 0.75, 0.90 and 1.00. One step issues, on each
+table, a find of 2^20 keys (90 % resident, 10 % never inserted) followed by an
+insert_or_assign of 2^20 keys (90 % resident keys refreshed with new rows and
+the current step as score, 10 % new keys). Inputs are generated on the GPU
+before the timed region. value = keys processed by all calls / wall time.
+
+The dominant kernel's roofline figure uses algorithmic bytes per key:
+find (single bucket, no scores out) moves 8 B key in + 128 B digest line +
+4 B expected false-positive key reads + 8h B key + 4Dh B row read +
+4Dh B row write + 1 B found flag, h = measured hit fraction.
+
+Prints one JSON line. --gpus N > 1 exits: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "find & upsert B-KV/s at λ=0.5–1.0, dim=64 fp32; % of HBM BW peak"
+HBM_PEAK_GBS = 8000.0
+SEED = 0x484B560000000002
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--dim", type=int, default=64)
+    p.add_argument("--capacity-log2", type=int, default=26)
+    p.add_argument("--batch-log2", type=int, default=20)
+    p.add_argument("--lambdas", default="0.5,0.75,0.9,1.0")
+    p.add_argument("--hit-frac", type=float, default=0.9)
+    p.add_argument("--new-frac", type=float, default=0.1, help="fraction of new keys in each upsert batch")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--find-only", action="store_true", help="time find batches only")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB 10 times (counter calibration) and exit")
+    return p.parse_args()
+
+
+def find_bytes_per_key(dim: int, h: float) -> float:
+    return 8 + 128 + 4 + 8 * h + 4 * dim * h + 4 * dim * h + 1
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                      "copy_GBps": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def fill_table(tab, lam, cap, batch, dim, seed, stream_id, device):
+    """Upserts fresh distinct keys (score = batch counter) until size >= lam*cap.
+    Returns (next counter of the key stream, next score)."""
+    import torch
+
+    import hkv_inputs as gen
+
+    target = int(round(lam * cap))
+    cursor, step, size = 0, 1, 0
+    while size < target:
+        n = batch if lam >= 1.0 else min(batch, target - size)
+        keys = gen.unique_keys(seed, stream_id, cursor, n, device=device)
+        vals = gen.values(keys, step, dim, seed)
+        sc = torch.full((n,), step, dtype=torch.int64, device=device)
+        tab.insert_or_assign(keys, vals, sc)
+        cursor += n
+        step += 1
+        size = tab.size()
+    return cursor, step, size
+
+
+def run_gpu(args):
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap = 1 << args.capacity_log2
+    batch = 1 << args.batch_log2
+    dim = args.dim
+    lams = [float(x) for x in args.lambdas.split(",")]
+    total_steps = args.warmup + args.steps
+    tables = []
+    for li, lam in enumerate(lams):
+        t0 = time.perf_counter()
+        tab = H.HashTable(cap, dim, device=0)
+        cursor, step, size = fill_table(tab, lam, cap, batch, dim, SEED, 1 + li, dev)
+        torch.cuda.synchronize()
+        log(f"lambda={lam}: filled to size {size} ({size / cap:.4f}) with {cursor} keys "
+            f"in {time.perf_counter() - t0:.1f}s")
+        # Inputs of every step, generated now (outside the timed region).
+        n_hit = int(round(batch * args.hit_frac))
+        n_new = int(round(batch * args.new_frac))
+        recent = min(cursor, 2 * batch)
+        pool = gen.unique_keys(SEED, 1 + li, cursor - recent, recent, device=dev)
+        finds, ups = [], []
+        vals_pool = [gen.values(pool[:batch], 1000 + j, dim, SEED) for j in range(2)]
+        for s in range(total_steps):
+            pick = torch.argsort(gen.counter_words(SEED, 100 + li, s * recent, recent, dev))
+            hits = pool[pick[:n_hit]]
+            miss = gen.unique_keys(SEED, 40 + li, s * batch, batch - n_hit, device=dev)
+            fk = gen.shuffle(torch.cat([hits, miss]), SEED, 200 + li * 1000 + s)
+            res = pool[pick[n_hit:n_hit + (batch - n_new)]] if batch - n_new <= recent - n_hit else pool[pick[:batch - n_new]]
+            new = gen.unique_keys(SEED, 60 + li, s * batch, n_new, device=dev)
+            uk = gen.shuffle(torch.cat([res, new]), SEED, 300 + li * 1000 + s)
+            sc = torch.full((batch,), step + s, dtype=torch.int64, device=dev)
+            finds.append(fk)
+            ups.append((uk, sc))
+        out = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        tables.append(dict(lam=lam, tab=tab, finds=finds, ups=ups, vals=vals_pool, out=out, found=found,
+                           lam_start=size / cap, hits=[]))
+    torch.cuda.synchronize()
+
+    ev = []
+    total_keys = 0
+
+    def one_step(s, timed):
+        nonlocal total_keys
+        for T in tables:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"])
+            e1.record()
+            if timed:
+                T["hits"].append(T["found"].sum())
+            if not args.find_only:
+                uk, sc = T["ups"][s]
+                T["tab"].insert_or_assign(uk, T["vals"][s % 2], sc)
+            e2.record()
+            if timed:
+                ev.append((T["lam"], e0, e1, e2))
+                total_keys += batch * (1 if args.find_only else 2)
+
+    for s in range(args.warmup):
+        one_step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        one_step(s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_lam = {}
+    find_ms_all = []
+    for lam, e0, e1, e2 in ev:
+        d = per_lam.setdefault(lam, dict(find_ms=[], upsert_ms=[]))
+        f = e0.elapsed_time(e1)
+        d["find_ms"].append(f)
+        find_ms_all.append(f)
+        if not args.find_only:
+            d["upsert_ms"].append(e1.elapsed_time(e2))
+    hit = {}
+    for T in tables:
+        hit[T["lam"]] = float(torch.stack(T["hits"]).sum().item()) / (batch * args.steps)
+        T["lam_end"] = T["tab"].size() / cap
+    h_avg = sum(hit.values()) / len(hit)
+    detail = {}
+    for lam, d in per_lam.items():
+        fm = sorted(d["find_ms"])[len(d["find_ms"]) // 2]
+        e = dict(find_ms_median=round(fm, 4), find_bkvs=round(batch / fm / 1e6, 3), hit_rate=round(hit[lam], 4))
+        if d["upsert_ms"]:
+            um = sorted(d["upsert_ms"])[len(d["upsert_ms"]) // 2]
+            e.update(upsert_ms_median=round(um, 4), upsert_bkvs=round(batch / um / 1e6, 3))
+        T = next(t for t in tables if t["lam"] == lam)
+        e.update(lambda_start=round(T["lam_start"], 4), lambda_end=round(T["lam_end"], 4))
+        detail[str(lam)] = e
+    fb = [v["find_bkvs"] for v in detail.values()]
+    find_var = (max(fb) - min(fb)) / max(fb)
+    avg_find_ms = sum(find_ms_all) / len(find_ms_all)
+    bpk = find_bytes_per_key(dim, h_avg)
+    achieved = bpk * batch / (avg_find_ms * 1e-3) / 1e9
+    for T in tables:
+        T["tab"].close()
+    return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, achieved=achieved,
+                bpk=bpk, avg_find_ms=avg_find_ms, h=h_avg)
+
+
+def run_cpu_baseline(args):
+    """The CPU oracle, single-threaded, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import hkv_inputs as gen
+    import oracle
+
+    cap = 1 << 21
+    batch = 1 << 18
+    dim = args.dim
+    lams = [float(x) for x in args.lambdas.split(",")]
+    zeros = np.zeros((batch, dim), np.float32)
+    ops = 0
+    secs = 0.0
+    t_all = time.perf_counter()
+    for li, lam in enumerate(lams):
+        o = oracle.OracleTable(cap, dim)
+        target = int(round(lam * cap))
+        cursor, step = 0, 1
+        while o.size() < target:
+            n = batch if lam >= 1.0 else min(batch, target - o.size())
+            k = gen.unique_keys(SEED, 1 + li, cursor, n).numpy().view(np.uint64)
+            o.insert_or_assign(k, np.full(n, step, np.uint64), values=zeros[:n])
+            cursor += n
+            step += 1
+        recent = gen.unique_keys(SEED, 1 + li, cursor - batch, batch).numpy().view(np.uint64)
+        n_hit = int(round(batch * args.hit_frac))
+        fk = np.concatenate([recent[:n_hit], gen.unique_keys(SEED, 40 + li, 0, batch - n_hit).numpy().view(np.uint64)])
+        n_new = int(round(batch * args.new_frac))
+        uk = np.concatenate([recent[:batch - n_new], gen.unique_keys(SEED, 60 + li, 0, n_new).numpy().view(np.uint64)])
+        t0 = time.perf_counter()
+        o.find(fk)
+        o.insert_or_assign(uk, np.full(batch, step, np.uint64), values=zeros)
+        secs += time.perf_counter() - t0
+        ops += 2 * batch
+        o.close()
+    return dict(value=ops / secs / 1e9, secs=secs, total=time.perf_counter() - t_all, cap=cap, batch=batch)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the table is a single-GPU "
+              "structure in this build and multi-GPU sharding is not implemented.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    g = run_gpu(args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("running the CPU oracle baseline")
+        cpu = run_cpu_baseline(args)
+        log(f"cpu baseline: {cpu['value'] * 1e3:.3f} M-KV/s over {cpu['secs']:.1f}s timed, {cpu['total']:.1f}s total")
+    value = g["total_keys"] / g["wall"] / 1e9
+    n_lams = len(args.lambdas.split(","))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "B-KV/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["wall"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"lambda sweep, single-bucket, capacity 2^{args.capacity_log2}, dim {args.dim} fp32 rows, "
+                         f"uniform distinct u64 keys, per step per lambda: find 2^{args.batch_log2} "
+                         f"({int(args.hit_frac * 100)}% resident)"
+                         + ("" if args.find_only else
+                            f" + insert_or_assign 2^{args.batch_log2} ({int(round((1 - args.new_frac) * 100))}% resident, "
+                            f"{int(round(args.new_frac * 100))}% new), scores = step counter")),
+            "capacity": 1 << args.capacity_log2,
+            "dim": args.dim,
+            "batch": 1 << args.batch_log2,
+            "lambdas": [float(x) for x in args.lambdas.split(",")],
+            "tables": n_lams,
+            "bucket_mode": "single",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "find_kernel",
+            "bound": "hbm",
+            "achieved": round(g["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(g["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_key": round(g["bpk"], 1),
+            "avg_launch_ms": round(g["avg_find_ms"], 5),
+        },
+        "cpu_baseline": None if cpu is None else {
+            "value": round(cpu["value"], 6),
+            "unit": "B-KV/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": (f"single-threaded oracle, capacity 2^21 dim {args.dim} tables at lambda {args.lambdas}, "
+                       f"one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign (same resident/new mix) "
+                       f"per lambda; {cpu['secs']:.1f}s timed"),
+        },
+        "detail": {
+            "per_lambda": g["detail"],
+            "find_lambda_variation": round(g["find_var"], 4),
+            "hit_rate": round(g["h"], 4),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
