@@ -8,10 +8,22 @@ insert_or_assign of 2^20 keys (90 % resident keys refreshed with new rows and
 the current step as score, 10 % new keys). Inputs are generated on the GPU
 before the timed region. value = keys processed by all calls / wall time.
 
-The dominant kernel's roofline figure uses algorithmic bytes per key:
-find (single bucket, no scores out) moves 8 B key in + 128 B digest line +
-4 B expected false-positive key reads + 8h B key + 4Dh B row read +
-4Dh B row write + 1 B found flag, h = measured hit fraction.
+Every kernel launch in the timed region is timed with HIP events recorded
+on its stream by the library (hkv_profile_start/stop); the kernel with the
+largest total time is the dominant one and gets the roofline figure:
+algorithmic bytes per launch / average launch time, against 8 TB/s.
+Algorithmic bytes per key (D = dim, h = hit fraction, f = resident fraction
+of an upsert batch, e = fraction of new keys that evict, i.e. land in a full
+bucket):
+  find          8 key + 128 digest line + 4 false-positive keys (0.5 x 8)
+                + h (8 key + 4D row read + 4D row write) + 1 found flag
+  upsert_probe  8 key + 128 digest line + 4 false-positive keys
+                + f (8 key + 4D row in + 8 score in + 4D row write + 8 score write)
+                + (1 - f) 8 (chain link: head exchange + next)
+  upsert_owner  4 next (every key) + (1 - f) [8 key + 8 score + 4D row in
+                + 4 head + 4 occ + 128 digest line + 4 false-positive keys
+                + 8 key + 1 digest + 8 score + 4D row write
+                + e (1024 score column + 8 tied key)]
 
 Prints one JSON line. --gpus N > 1 exits: this build runs on one GPU.
 """
@@ -56,7 +68,15 @@ def parse_args():
 
 
 def find_bytes_per_key(dim: int, h: float) -> float:
-    return 8 + 128 + 4 + 8 * h + 4 * dim * h + 4 * dim * h + 1
+    return 8 + 128 + 4 + h * (8 + 8 * dim) + 1
+
+
+def probe_bytes_per_key(dim: int, f: float) -> float:
+    return 8 + 128 + 4 + f * (8 + 8 * dim + 16) + (1 - f) * 8
+
+
+def owner_bytes_per_key(dim: int, f: float, e: float) -> float:
+    return 4 + (1 - f) * (8 + 8 + 4 * dim + 4 + 4 + 128 + 4 + 8 + 1 + 8 + 4 * dim + e * (1024 + 8))
 
 
 def calibrate_copy(mib: int) -> None:
@@ -163,11 +183,22 @@ def run_gpu(args):
     for s in range(args.warmup):
         one_step(s, False)
     torch.cuda.synchronize()
+    for T in tables:
+        T["size0"] = T["tab"].size()
+        T["tab"].profile_start()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.warmup, total_steps):
         one_step(s, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kstats = {}
+    for T in tables:
+        T["kernels"] = T["tab"].profile_stop()
+        for name, (cnt, tot, mx) in T["kernels"].items():
+            a = kstats.setdefault(name, [0, 0.0])
+            a[0] += cnt
+            a[1] += tot
 
     per_lam = {}
     find_ms_all = []
@@ -195,13 +226,32 @@ def run_gpu(args):
         detail[str(lam)] = e
     fb = [v["find_bkvs"] for v in detail.values()]
     find_var = (max(fb) - min(fb)) / max(fb)
-    avg_find_ms = sum(find_ms_all) / len(find_ms_all)
-    bpk = find_bytes_per_key(dim, h_avg)
-    achieved = bpk * batch / (avg_find_ms * 1e-3) / 1e9
+    # algorithmic bytes per launch of each kernel, averaged over the tables
+    f_res = 1.0 - args.new_frac
+    n_new = int(round(batch * args.new_frac)) * args.steps
+    bytes_per_launch = {"find": 0.0, "upsert_probe": 0.0, "upsert_owner": 0.0}
+    for T in tables:
+        inserted = T["tab"].size() - T["size0"]
+        e = max(0.0, 1.0 - inserted / n_new) if n_new else 0.0
+        T["evict_frac"] = e
+        bytes_per_launch["find"] += batch * find_bytes_per_key(dim, hit[T["lam"]]) / len(tables)
+        bytes_per_launch["upsert_probe"] += batch * probe_bytes_per_key(dim, f_res) / len(tables)
+        bytes_per_launch["upsert_owner"] += batch * owner_bytes_per_key(dim, f_res, e) / len(tables)
+        detail[str(T["lam"])]["evicting_new_frac"] = round(e, 4)
+        detail[str(T["lam"])]["kernel_avg_ms"] = {k: round(v[1] / v[0], 5) for k, v in T["kernels"].items()}
+    kernels = {}
+    for name, (cnt, tot) in kstats.items():
+        k = dict(launches=cnt, total_ms=round(tot, 3), avg_ms=round(tot / cnt, 5))
+        if name in bytes_per_launch:
+            gbs = bytes_per_launch[name] / (tot / cnt * 1e-3) / 1e9
+            k.update(bytes_per_launch=round(bytes_per_launch[name]), achieved_GBps=round(gbs, 1),
+                     frac=round(gbs / HBM_PEAK_GBS, 4))
+        kernels[name] = k
+    dominant = max(kernels, key=lambda n: kernels[n]["total_ms"])
     for T in tables:
         T["tab"].close()
-    return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, achieved=achieved,
-                bpk=bpk, avg_find_ms=avg_find_ms, h=h_avg)
+    return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
+                dominant=dominant, h=h_avg, find_ms_events=sum(find_ms_all) / len(find_ms_all))
 
 
 def run_cpu_baseline(args):
@@ -211,8 +261,9 @@ def run_cpu_baseline(args):
     import hkv_inputs as gen
     import oracle
 
-    cap = 1 << 21
+    cap = 1 << 22
     batch = 1 << 18
+    rounds = 4
     dim = args.dim
     lams = [float(x) for x in args.lambdas.split(",")]
     zeros = np.zeros((batch, dim), np.float32)
@@ -231,14 +282,18 @@ def run_cpu_baseline(args):
             step += 1
         recent = gen.unique_keys(SEED, 1 + li, cursor - batch, batch).numpy().view(np.uint64)
         n_hit = int(round(batch * args.hit_frac))
-        fk = np.concatenate([recent[:n_hit], gen.unique_keys(SEED, 40 + li, 0, batch - n_hit).numpy().view(np.uint64)])
         n_new = int(round(batch * args.new_frac))
-        uk = np.concatenate([recent[:batch - n_new], gen.unique_keys(SEED, 60 + li, 0, n_new).numpy().view(np.uint64)])
-        t0 = time.perf_counter()
-        o.find(fk)
-        o.insert_or_assign(uk, np.full(batch, step, np.uint64), values=zeros)
-        secs += time.perf_counter() - t0
-        ops += 2 * batch
+        for r in range(rounds):
+            rot = np.roll(recent, r * 7919)
+            fk = np.concatenate([rot[:n_hit],
+                                 gen.unique_keys(SEED, 40 + li, r * batch, batch - n_hit).numpy().view(np.uint64)])
+            uk = np.concatenate([rot[:batch - n_new],
+                                 gen.unique_keys(SEED, 60 + li, r * batch, n_new).numpy().view(np.uint64)])
+            t0 = time.perf_counter()
+            o.find(fk)
+            o.insert_or_assign(uk, np.full(batch, step + r, np.uint64), values=zeros)
+            secs += time.perf_counter() - t0
+            ops += 2 * batch
         o.close()
     return dict(value=ops / secs / 1e9, secs=secs, total=time.perf_counter() - t_all, cap=cap, batch=batch)
 
@@ -289,26 +344,28 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "find_kernel",
+            "kernel": g["dominant"],
             "bound": "hbm",
-            "achieved": round(g["achieved"], 1),
+            "achieved": g["kernels"][g["dominant"]]["achieved_GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(g["achieved"] / HBM_PEAK_GBS, 4),
+            "frac": g["kernels"][g["dominant"]]["frac"],
             "traffic": None,
-            "bytes_per_key": round(g["bpk"], 1),
-            "avg_launch_ms": round(g["avg_find_ms"], 5),
+            "bytes_per_launch": g["kernels"][g["dominant"]]["bytes_per_launch"],
+            "avg_launch_ms": g["kernels"][g["dominant"]]["avg_ms"],
         },
         "cpu_baseline": None if cpu is None else {
             "value": round(cpu["value"], 6),
             "unit": "B-KV/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": (f"single-threaded oracle, capacity 2^21 dim {args.dim} tables at lambda {args.lambdas}, "
-                       f"one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign (same resident/new mix) "
-                       f"per lambda; {cpu['secs']:.1f}s timed"),
+            "sample": (f"single-threaded oracle, capacity 2^22 dim {args.dim} tables at lambda {args.lambdas}, "
+                       f"4 rounds of one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign "
+                       f"(same resident/new mix) per lambda; {cpu['secs']:.1f}s timed of {cpu['total']:.1f}s"),
         },
         "detail": {
+            "kernels": g["kernels"],
+            "find_call_ms_events": round(g["find_ms_events"], 5),
             "per_lambda": g["detail"],
             "find_lambda_variation": round(g["find_var"], 4),
             "hit_rate": round(g["h"], 4),

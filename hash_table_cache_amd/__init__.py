@@ -24,6 +24,8 @@ from ._native import (  # noqa: F401
     hkv_find,
     hkv_get_options,
     hkv_insert_or_assign,
+    hkv_profile_start,
+    hkv_profile_stop,
     hkv_size,
 )
 
@@ -92,6 +94,14 @@ class HashTable:
 
     def size(self, stream=None) -> int:
         return hkv_size(self._h, stream, device=self.device)
+
+    def profile_start(self) -> None:
+        """Time every kernel this table launches from now on (events on its stream)."""
+        hkv_profile_start(self._h)
+
+    def profile_stop(self) -> dict:
+        """Stop timing; {kernel: (launches, total_ms, max_ms)}. Waits for the timed work."""
+        return hkv_profile_stop(self._h)
 
     def export_batch(self, offset: int = 0, n_slots: int | None = None, with_values: bool = True, stream=None):
         """Returns (keys, values, scores, pos) of the occupied slots in

@@ -38,6 +38,8 @@ EXPORTS = (
     "hkv_assign",
     "hkv_size",
     "hkv_export_batch",
+    "hkv_profile_start",
+    "hkv_profile_stop",
     "hkv_last_error",
 )
 
@@ -51,6 +53,15 @@ class HkvOptions(ctypes.Structure):
         ("values_on_host", ctypes.c_uint32),
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class HkvKernelStat(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char * 32),
+        ("launches", ctypes.c_uint64),
+        ("total_ms", ctypes.c_double),
+        ("max_ms", ctypes.c_double),
     ]
 
 
@@ -83,6 +94,11 @@ def _load() -> ctypes.CDLL:
     L.hkv_size.restype = st
     L.hkv_export_batch.argtypes = [vp, u64, u64, vp, vp, vp, vp, vp, vp]
     L.hkv_export_batch.restype = st
+    L.hkv_profile_start.argtypes = [vp]
+    L.hkv_profile_start.restype = st
+    L.hkv_profile_stop.argtypes = [vp, ctypes.POINTER(HkvKernelStat), ctypes.c_uint32,
+                                   ctypes.POINTER(ctypes.c_uint32)]
+    L.hkv_profile_stop.restype = st
     L.hkv_last_error.argtypes = []
     L.hkv_last_error.restype = ctypes.c_char_p
     return L
@@ -188,3 +204,17 @@ def hkv_export_batch(table, offset, n_slots, keys_out, values_out, scores_out, p
         _ptr(pos_out, _U64_DTYPES, 0, "pos_out", nullable=True),
         _ptr(count_out, _U64_DTYPES, 1, "count_out"),
         _stream(stream, device)))
+
+
+def hkv_profile_start(table) -> None:
+    _check(lib.hkv_profile_start(table))
+
+
+def hkv_profile_stop(table) -> dict:
+    """Returns {kernel name: (launches, total_ms, max_ms)}."""
+    cap = 16
+    out = (HkvKernelStat * cap)()
+    count = ctypes.c_uint32(0)
+    _check(lib.hkv_profile_stop(table, out, cap, ctypes.byref(count)))
+    return {out[j].name.decode(): (int(out[j].launches), float(out[j].total_ms), float(out[j].max_ms))
+            for j in range(min(cap, count.value))}

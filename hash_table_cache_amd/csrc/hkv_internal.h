@@ -22,6 +22,18 @@ struct TableView {
   uint32_t dim;
   uint32_t pow2;      // nb is a power of two
   uint32_t dual;      // dual-bucket mode
+  uint32_t lanes;     // lanes per key of find/assign/insert probes; 0 = by dim
+};
+
+// Optional per-kernel timing: when a timer is passed, each launch is
+// bracketed by begin()/end() on the launch stream (the runtime records a
+// pair of hipEvents there).
+struct KernelTimer {
+  virtual void begin(hipStream_t s) = 0;
+  virtual void end(hipStream_t s, const char* kernel) = 0;
+
+ protected:
+  ~KernelTimer() = default;
 };
 
 // Row copies use 16-byte vectors when dim % 4 == 0 and every row pointer
@@ -30,21 +42,25 @@ struct TableView {
 hipError_t launch_init(const TableView& t, hipStream_t s);
 
 hipError_t launch_find(const TableView& t, uint64_t n, const uint64_t* keys, float* values_out,
-                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s);
+                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s,
+                       KernelTimer* timer);
 
 hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys,
-                         const float* values, const uint64_t* scores, bool vec4, hipStream_t s);
+                         const float* values, const uint64_t* scores, bool vec4, hipStream_t s,
+                         KernelTimer* timer);
 
 // next: [n] u32 workspace; target: [n] u32 workspace (dual mode only).
 hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
                          const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
-                         bool serial, hipStream_t s);
+                         bool serial, hipStream_t s, KernelTimer* timer);
 
 // Writes the number of occupied slots to *dev_out (device memory).
-hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s);
+hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s,
+                       KernelTimer* timer);
 
 hipError_t launch_export(const TableView& t, uint64_t begin, uint64_t end, uint64_t* keys_out,
                          float* values_out, uint64_t* scores_out, uint64_t* pos_out,
-                         unsigned long long* count_out, bool vec4, hipStream_t s);
+                         unsigned long long* count_out, bool vec4, hipStream_t s,
+                         KernelTimer* timer);
 
 }  // namespace hkv

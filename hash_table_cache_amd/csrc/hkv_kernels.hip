@@ -94,20 +94,31 @@ __device__ __forceinline__ uint64_t group_min(uint64_t v) {
   return v;
 }
 
-// Copies a row of dim floats with the G lanes of a group.
+// Copies a row of dim floats with the G lanes of a group. Each lane loads up
+// to R 16-byte pieces (4, or 2 for 16-lane groups) before storing any, so a
+// row of up to 512 bytes costs one memory round trip.
 template <int G, bool V4, bool NT>
 __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* __restrict__ src,
                                          uint32_t dim, int lane) {
   if constexpr (V4) {
+    constexpr int R = G >= 16 ? 2 : 4;
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
     f32x4* d4 = reinterpret_cast<f32x4*>(dst);
     const uint32_t n4 = dim >> 2;
-    for (uint32_t c = lane; c < n4; c += G) {
-      const f32x4 v = s4[c];
-      if constexpr (NT) {
-        __builtin_nontemporal_store(v, d4 + c);
-      } else {
-        d4[c] = v;
+    for (uint32_t c0 = lane; c0 < n4; c0 += R * G) {
+      f32x4 v[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (c0 + r * G < n4) v[r] = s4[c0 + r * G];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (c0 + r * G < n4) {
+          if constexpr (NT) {
+            __builtin_nontemporal_store(v[r], d4 + c0 + r * G);
+          } else {
+            d4[c0 + r * G] = v[r];
+          }
+        }
       }
     }
   } else {
@@ -135,23 +146,58 @@ __device__ __forceinline__ void load_digest_words(const uint8_t* line, int lane,
   }
 }
 
-// Candidate scan of one bucket for key k: every slot of this lane whose digest
-// byte equals the key's digest gets a full key compare. Returns the table
-// position of the hit or -1.
+// One bit per zero byte of x (bit j for byte j): the 0x80 markers of
+// zero_bytes gathered by a multiply that moves byte j's marker to bit 21 + j
+// with no carries between the four partial products.
+__device__ __forceinline__ uint32_t zero_byte_bits(uint32_t x) {
+  return (((zero_bytes(x) >> 7) * 0x204081u) >> 21) & 0xFu;
+}
+
+// Candidate mask of this lane's share of a digest line: bit j is set when the
+// digest of the lane's j-th slot equals the key's digest.
 template <int NW>
-__device__ __forceinline__ int64_t scan_line(const TableView& t, uint32_t b, const uint32_t (&w)[NW],
-                                             uint32_t pat, uint64_t k, int lane) {
-  int64_t hit = -1;
-  const uint64_t base = static_cast<uint64_t>(b) * kSlots + static_cast<uint64_t>(lane) * (NW * 4);
+__device__ __forceinline__ uint32_t candidate_mask(const uint32_t (&w)[NW], uint32_t pat) {
+  uint32_t m = 0;
 #pragma unroll
-  for (int q = 0; q < NW; ++q) {
-    uint32_t z = zero_bytes(w[q] ^ pat);
-    while (z) {
-      const int byte = __builtin_ctz(z) >> 3;
-      z &= z - 1;
-      const uint64_t p = base + q * 4 + byte;
-      if (t.keys[p] == k) hit = static_cast<int64_t>(p);
-    }
+  for (int q = 0; q < NW; ++q) m |= zero_byte_bits(w[q] ^ pat) << (4 * q);
+  return m;
+}
+
+// Full key compare of the candidate slots of up to two lines (mask m1 over
+// positions base1 + j, mask m2 over base2 + j). The first two candidate keys
+// are loaded back to back so that they cost one memory round trip; a third
+// candidate in the same lane is rare (about 1 in 4000 lanes) and is looped.
+// Returns the table position of the matching slot or -1.
+__device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__ keys, uint64_t k,
+                                                    uint32_t m1, uint64_t base1, uint32_t m2,
+                                                    uint64_t base2) {
+  // candidate positions in order: the bits of m1 (over base1), then of m2
+  const bool h0 = (m1 | m2) != 0;
+  const bool h1 = __builtin_popcount(m1) + __builtin_popcount(m2) >= 2;
+  uint64_t p0 = 0, p1 = 0;
+  if (h0) {
+    p0 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
+    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
+  }
+  if (h1) {
+    p1 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
+    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
+  }
+  uint64_t k0 = 0, k1 = 0;
+  if (h0) k0 = keys[p0];
+  if (h1) k1 = keys[p1];
+  int64_t hit = -1;
+  if (h0 && k0 == k) hit = static_cast<int64_t>(p0);
+  if (h1 && k1 == k) hit = static_cast<int64_t>(p1);
+  while (m1) {
+    const uint64_t p = base1 + __builtin_ctz(m1);
+    m1 &= m1 - 1;
+    if (keys[p] == k) hit = static_cast<int64_t>(p);
+  }
+  while (m2) {
+    const uint64_t p = base2 + __builtin_ctz(m2);
+    m2 &= m2 - 1;
+    if (keys[p] == k) hit = static_cast<int64_t>(p);
   }
   return hit;
 }
@@ -174,13 +220,14 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
   }
   int64_t hit = -1;
   if (!is_reserved(k)) {
-    hit = scan_line<NW>(t, b1, w1, pat, k, lane);
+    const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
+    const uint32_t m1 = candidate_mask<NW>(w1, pat);
+    uint32_t m2 = 0;
     if constexpr (DUAL) {
-      if (b2 != b1) {
-        const int64_t h2 = scan_line<NW>(t, b2, w2, pat, k, lane);
-        if (h2 >= 0) hit = h2;
-      }
+      if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
     }
+    hit = match_candidates(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
+                           static_cast<uint64_t>(b2) * kSlots + off);
   }
   const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (bits == 0) return -1;
@@ -213,13 +260,21 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
 
 __global__ __launch_bounds__(kBlock) void size_kernel(const uint32_t* __restrict__ occ, uint64_t nb,
                                                       unsigned long long* out) {
+  __shared__ unsigned long long part[kBlock / 64];
   unsigned long long acc = 0;
   for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; b < nb;
        b += static_cast<uint64_t>(gridDim.x) * kBlock)
     acc += occ[b];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (wave_lane() == 0 && acc) atomicAdd(out, acc);
+  if (wave_lane() == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long total = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) total += part[w];
+    if (total) atomicAdd(out, total);
+  }
 }
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0; }
@@ -266,14 +321,12 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(TableView t, uint64_t n,
 
 // -------------------------------------------------------------- inserters --
 
-// One bucket held by a 16-lane group: occupancy (group-uniform), this lane's
-// 8 digest bytes and, once the bucket has been found full, its 8 scores.
+// One bucket held by a 16-lane group: occupancy (group-uniform) and this
+// lane's 8 digest bytes.
 struct Owned {
   uint32_t b;
   uint32_t occ;
   uint32_t dig0, dig1;  // digest bytes of slots 8*lane .. 8*lane+7
-  uint64_t sc[8];       // scores of the same slots (valid when have_scores)
-  bool have_scores;
 };
 
 __device__ __forceinline__ void own_load(Owned& o, const TableView& t, uint32_t b, int lane) {
@@ -284,63 +337,51 @@ __device__ __forceinline__ void own_load(Owned& o, const TableView& t, uint32_t 
   const uint2 v = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(b) * kSlots + lane * 8);
   o.dig0 = v.x;
   o.dig1 = v.y;
-  o.have_scores = false;
 }
 
 __device__ __forceinline__ void own_store_occ(const Owned& o, const TableView& t, int lane) {
   if (lane == 0) t.occ[o.b] = o.occ;
 }
 
-__device__ __forceinline__ void own_load_scores(Owned& o, const TableView& t, int lane) {
-  if (o.have_scores) return;
-  const uint64_t* src = t.scores + static_cast<uint64_t>(o.b) * kSlots + lane * 8;
-#pragma unroll
-  for (int u = 0; u < 8; u += 2) {
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(src + u);
-    o.sc[u] = v.x;
-    o.sc[u + 1] = v.y;
-  }
-  o.have_scores = true;
-}
-
-// Slot of key k in the owned bucket, or -1 (group-uniform).
+// Slot of key k in the owned bucket, or -1 (group-uniform). Only slots below
+// the occupancy are compared (the rest are empty).
 __device__ __forceinline__ int own_find(const Owned& o, const TableView& t, uint64_t k, uint32_t pat,
                                         int lane) {
-  int hit = -1;
   const int first = lane * 8;
-  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots;
-  uint32_t z0 = zero_bytes(o.dig0 ^ pat);
-  uint32_t z1 = zero_bytes(o.dig1 ^ pat);
-  while (z0) {
-    const int s = first + (__builtin_ctz(z0) >> 3);
-    z0 &= z0 - 1;
-    if (s < static_cast<int>(o.occ) && t.keys[base + s] == k) hit = s;
-  }
-  while (z1) {
-    const int s = first + 4 + (__builtin_ctz(z1) >> 3);
-    z1 &= z1 - 1;
-    if (s < static_cast<int>(o.occ) && t.keys[base + s] == k) hit = s;
-  }
+  const int live = static_cast<int>(o.occ) - first;
+  const uint32_t valid = live >= 8 ? 0xFFu : (live <= 0 ? 0u : ((1u << live) - 1));
+  const uint32_t m = (zero_byte_bits(o.dig0 ^ pat) | (zero_byte_bits(o.dig1 ^ pat) << 4)) & valid;
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + first;
+  const int64_t p = match_candidates(t.keys, k, m, base, 0u, base);
+  const int hit = p >= 0 ? static_cast<int>(p - static_cast<int64_t>(o.b) * kSlots) : -1;
   const uint64_t bits = group_bits<kInsG>(__ballot(hit >= 0));
   if (bits == 0) return -1;
   return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, kInsG);
 }
 
 // Lowest (score, key) entry of a full owned bucket (group-uniform results).
-__device__ __forceinline__ void own_lowest(Owned& o, const TableView& t, int lane, uint64_t* min_score,
-                                           uint64_t* min_key, int* slot) {
-  own_load_scores(o, t, lane);
-  uint64_t ls = o.sc[0];
+// Each lane reads the scores and keys of its own 8 slots (written only by
+// itself earlier in the kernel).
+__device__ __forceinline__ void own_lowest(const Owned& o, const TableView& t, int lane,
+                                           uint64_t* min_score, uint64_t* min_key, int* slot) {
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+  uint64_t sc[8];
 #pragma unroll
-  for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
+    sc[u] = v.x;
+    sc[u + 1] = v.y;
+  }
+  uint64_t ls = sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = sc[u] < ls ? sc[u] : ls;
   const uint64_t gs = group_min<kInsG>(ls);
   // Among the slots at the minimum score, the smallest key ranks lowest.
   uint64_t lk = ~0ull;
   int lslot = -1;
-  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    if (o.sc[u] == gs) {
+    if (sc[u] == gs) {
       const uint64_t kk = t.keys[base + u];
       if (lslot < 0 || kk < lk) {
         lk = kk;
@@ -353,13 +394,6 @@ __device__ __forceinline__ void own_lowest(Owned& o, const TableView& t, int lan
   *min_score = gs;
   *min_key = gk;
   *slot = __shfl(lslot, __ffsll(static_cast<unsigned long long>(bits)) - 1, kInsG);
-}
-
-// o.sc[u] = score for u == idx, written as selects on every element so the
-// array stays in registers.
-__device__ __forceinline__ void set_score_reg(Owned& o, int idx, uint64_t score) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) o.sc[u] = (u == idx) ? score : o.sc[u];
 }
 
 // Writes (key, digest, score) of slot s (by its owner lane) and keeps the
@@ -377,14 +411,12 @@ __device__ __forceinline__ void own_write_slot(Owned& o, const TableView& t, int
   } else {
     o.dig0 = (o.dig0 & ~(0xFFu << sh)) | (d << sh);
   }
-  if (o.have_scores) set_score_reg(o, s & 7, score);
 }
 
 __device__ __forceinline__ void own_write_score(Owned& o, const TableView& t, int s, uint64_t score,
                                                 int lane) {
   if (lane != (s >> 3)) return;
   t.scores[static_cast<uint64_t>(o.b) * kSlots + s] = score;
-  if (o.have_scores) set_score_reg(o, s & 7, score);
 }
 
 template <bool V4>
@@ -424,24 +456,6 @@ __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_
   }
 }
 
-// Link kernel, single-bucket mode: one thread per key pushes the key onto the
-// chain of its bucket. next[i] is the previously pushed key of that bucket,
-// kNoIdx for the first one (which will own the bucket), kSkipIdx for reserved keys.
-__global__ __launch_bounds__(kBlock) void link_single_kernel(TableView t, uint64_t n,
-                                                             const uint64_t* __restrict__ keys,
-                                                             uint32_t* __restrict__ next) {
-  const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (i >= n) return;
-  const uint64_t k = keys[i];
-  if (is_reserved(k)) {
-    next[i] = kSkipIdx;
-    return;
-  }
-  const uint32_t b = bucket_of(t, fmix64(k));
-  next[i] = __hip_atomic_exchange(t.head + b, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Lowest (score, key) of a full bucket, read-only, 16 lanes (group-uniform).
 __device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int lane, uint64_t* ms,
                                             uint64_t* mk) {
@@ -469,32 +483,48 @@ __device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int 
   *mk = group_min<kInsG>(lk);
 }
 
-// Link kernel, dual-bucket mode: a 16-lane group per key chooses the bucket
-// the key will be applied to, from the table as it was before the batch
-// (Algorithm 3): the bucket holding it; else the less-occupied candidate if
-// either has room (tie: the first); else the candidate whose lowest-ranked
-// entry is lower. It then pushes the key onto that bucket's chain.
-__global__ __launch_bounds__(kBlock) void link_dual_kernel(TableView t, uint64_t n,
-                                                           const uint64_t* __restrict__ keys,
-                                                           uint32_t* __restrict__ next,
-                                                           uint32_t* __restrict__ target) {
-  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / kInsG;
-  const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
+// Insert, first kernel: a group of G lanes per key probes the key's
+// candidate bucket(s). A resident key is updated in place (value row and
+// score only, no structural change, so concurrent probes stay valid). A
+// missing key is pushed onto the chain of the bucket it goes to: in
+// single-bucket mode its bucket; in dual-bucket mode the bucket Algorithm 3
+// picks from the table as it was before the batch (the less-occupied one if
+// either has room, tie: the first; else the one whose lowest-ranked entry is
+// lower). next[i] receives the previously pushed key of that chain, kNoIdx
+// for the first one (whose group will own the bucket), kSkipIdx for keys
+// that need no insert. The updates all happen before any insert of the batch,
+// which is one of the serial orders of the batch.
+template <int G, bool V4, bool DUAL>
+__global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint64_t n,
+                                                              const uint64_t* __restrict__ keys,
+                                                              const float* __restrict__ values,
+                                                              const uint64_t* __restrict__ scores,
+                                                              uint32_t* __restrict__ next,
+                                                              uint32_t* __restrict__ target) {
+  static_assert(!DUAL || G == kInsG, "dual-bucket selection works on 16-lane groups");
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
   const uint64_t k = keys[i];
   if (is_reserved(k)) {
     if (lane == 0) next[i] = kSkipIdx;
     return;
   }
+  const int64_t p = probe<G, DUAL>(t, k, lane);
+  if (p >= 0) {
+    copy_row<G, V4, false>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    if (lane == 0) {
+      t.scores[p] = scores[i];
+      next[i] = kSkipIdx;
+    }
+    return;
+  }
   const uint64_t h = fmix64(k);
-  const uint32_t b1 = bucket_of(t, h);
-  const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
-  uint32_t tb = b1;
-  if (b2 != b1) {
-    const int64_t p = probe<kInsG, true>(t, k, lane);
-    if (p >= 0) {
-      tb = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
-    } else {
+  uint32_t tb = bucket_of(t, h);
+  if constexpr (DUAL) {
+    const uint32_t b1 = tb;
+    const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+    if (b2 != b1) {
       const uint32_t o1 = t.occ[b1], o2 = t.occ[b2];
       if (o1 < kSlots || o2 < kSlots) {
         tb = (o1 <= o2) ? b1 : b2;
@@ -507,15 +537,20 @@ __global__ __launch_bounds__(kBlock) void link_dual_kernel(TableView t, uint64_t
     }
   }
   if (lane == 0) {
-    target[i] = tb;
+    if constexpr (DUAL) target[i] = tb;
     next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Owner kernel: the group of the chain's first-pushed key (next == kNoIdx)
-// owns the bucket, walks the chain from its head and applies each key in
-// turn, then resets the chain head for the next call.
+// Insert, second kernel: the group of each chain's first-pushed key
+// (next == kNoIdx) owns that bucket for the whole kernel. A 16-lane group
+// covers 16 consecutive keys: one coalesced load of their next words and a
+// ballot find the owners among them, which are then served one after the
+// other. An owner applies its own key first, then the chain from its head
+// down to itself, each with Algorithm 2 against the owned bucket, and finally
+// resets the chain head. Keys of a batch are distinct, so any order within a
+// chain gives the same bucket contents.
 template <bool V4, bool DUAL>
 __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
@@ -523,27 +558,34 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
                                                               const uint64_t* __restrict__ scores,
                                                               const uint32_t* __restrict__ next,
                                                               const uint32_t* __restrict__ target) {
-  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / kInsG;
+  const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) & ~uint64_t(kInsG - 1);
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
-  if (i >= n) return;
-  if (next[i] != kNoIdx) return;
-  const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(keys[i]));
-  uint32_t c = 0;
-  if (lane == 0) c = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  c = __shfl(c, 0, kInsG);
-  Owned o;
-  own_load(o, t, b, lane);
-  const uint32_t occ0 = o.occ;
-  // A chain visits at most n distinct keys and ends at this group's own key;
-  // the index and step checks only guard against a corrupted chain.
-  for (uint64_t step = 0; c < n && step < n; ++step) {
-    own_upsert<V4>(o, t, keys[c], values + static_cast<uint64_t>(c) * t.dim, scores[c], lane);
-    if (c == static_cast<uint32_t>(i)) break;
-    c = next[c];
+  if (first >= n) return;
+  const uint64_t mine = first + lane;
+  const bool owner = mine < n && next[mine] == kNoIdx;
+  uint64_t todo = group_bits<kInsG>(__ballot(owner));
+  while (todo) {
+    const uint64_t i = first + (__ffsll(static_cast<unsigned long long>(todo)) - 1);
+    todo &= todo - 1;
+    const uint64_t k = keys[i];
+    const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(k));
+    uint32_t c = 0;
+    if (lane == 0) c = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    Owned o;
+    own_load(o, t, b, lane);
+    const uint32_t occ0 = o.occ;
+    own_upsert<V4>(o, t, k, values + i * t.dim, scores[i], lane);
+    c = __shfl(c, 0, kInsG);
+    // The chain holds at most n keys and ends at this owner's own key; the
+    // index and step bounds only guard against a corrupted chain.
+    for (uint64_t step = 0; c != static_cast<uint32_t>(i) && c < n && step < n; ++step) {
+      own_upsert<V4>(o, t, keys[c], values + static_cast<uint64_t>(c) * t.dim, scores[c], lane);
+      c = next[c];
+    }
+    if (o.occ != occ0) own_store_occ(o, t, lane);
+    if (lane == 0)
+      __hip_atomic_store(t.head + b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (o.occ != occ0) own_store_occ(o, t, lane);
-  if (lane == 0)
-    __hip_atomic_store(t.head + b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Serial inserter: one 16-lane group applies the whole batch in input order
@@ -631,70 +673,91 @@ uint32_t grid_for(uint64_t threads) {
   return static_cast<uint32_t>((threads + kBlock - 1) / kBlock);
 }
 
-// Lanes per key for find/assign: enough lanes to move a row in one or two
-// 16-byte pieces each, between 4 and 16.
-int lanes_for_dim(uint32_t dim) {
-  if (dim <= 16) return 4;
-  if (dim <= 32) return 8;
+// Lanes per key for find/assign/insert probes: 4 for rows up to 64 bytes,
+// 8 up to 256 bytes (measured best at 256-byte rows), 16 above; t.lanes
+// overrides it (4, 8 or 16).
+int lanes_for(const TableView& t) {
+  if (t.lanes == 4 || t.lanes == 8 || t.lanes == 16) return static_cast<int>(t.lanes);
+  if (t.dim <= 16) return 4;
+  if (t.dim <= 64) return 8;
   return 16;
 }
 
+// Launch with optional timing events around the kernel (on the same stream).
+#define HKV_LAUNCH(timer, name, kernel, grid, block, stream, ...)              \
+  do {                                                                          \
+    if (timer) (timer)->begin(stream);                                          \
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);            \
+    if (timer) (timer)->end(stream, name);                                      \
+  } while (0)
+
 template <int G, bool V4, bool DUAL>
 hipError_t find_g(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
-                  uint64_t* sc, hipStream_t s) {
-  hipLaunchKernelGGL((find_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), 0, s, t, n, keys,
-                     out, found, sc);
+                  uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, "find", (find_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n, keys,
+             out, found, sc);
   return hipGetLastError();
 }
 
 template <int G, bool V4, bool DUAL>
 hipError_t assign_g(const TableView& t, uint64_t n, const uint64_t* keys, const float* v,
-                    const uint64_t* sc, hipStream_t s) {
-  hipLaunchKernelGGL((assign_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), 0, s, t, n,
-                     keys, v, sc);
+                    const uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, "assign", (assign_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n,
+             keys, v, sc);
+  return hipGetLastError();
+}
+
+template <int G, bool V4, bool DUAL>
+hipError_t insert_g(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
+                    const uint64_t* scores, uint32_t* next, uint32_t* target, hipStream_t s,
+                    KernelTimer* tm) {
+  HKV_LAUNCH(tm, "upsert_probe", (upsert_probe_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock),
+             s, t, n, keys, values, scores, next, target);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n)), dim3(kBlock), s, t,
+             n, keys, values, scores, next, target);
   return hipGetLastError();
 }
 
 template <bool V4, bool DUAL>
 hipError_t find_d(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
-                  uint64_t* sc, hipStream_t s) {
-  switch (lanes_for_dim(t.dim)) {
-    case 4: return find_g<4, V4, DUAL>(t, n, keys, out, found, sc, s);
-    case 8: return find_g<8, V4, DUAL>(t, n, keys, out, found, sc, s);
-    default: return find_g<16, V4, DUAL>(t, n, keys, out, found, sc, s);
+                  uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  switch (lanes_for(t)) {
+    case 4: return find_g<4, V4, DUAL>(t, n, keys, out, found, sc, s, tm);
+    case 8: return find_g<8, V4, DUAL>(t, n, keys, out, found, sc, s, tm);
+    default: return find_g<16, V4, DUAL>(t, n, keys, out, found, sc, s, tm);
   }
 }
 
 template <bool V4, bool DUAL>
 hipError_t assign_d(const TableView& t, uint64_t n, const uint64_t* keys, const float* v,
-                    const uint64_t* sc, hipStream_t s) {
-  switch (lanes_for_dim(t.dim)) {
-    case 4: return assign_g<4, V4, DUAL>(t, n, keys, v, sc, s);
-    case 8: return assign_g<8, V4, DUAL>(t, n, keys, v, sc, s);
-    default: return assign_g<16, V4, DUAL>(t, n, keys, v, sc, s);
+                    const uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  switch (lanes_for(t)) {
+    case 4: return assign_g<4, V4, DUAL>(t, n, keys, v, sc, s, tm);
+    case 8: return assign_g<8, V4, DUAL>(t, n, keys, v, sc, s, tm);
+    default: return assign_g<16, V4, DUAL>(t, n, keys, v, sc, s, tm);
   }
 }
 
 template <bool V4, bool DUAL>
 hipError_t insert_d(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
                     const uint64_t* scores, uint32_t* next, uint32_t* target, bool serial,
-                    hipStream_t s) {
+                    hipStream_t s, KernelTimer* tm) {
   if (serial) {
-    hipLaunchKernelGGL((upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), 0, s, t, n, keys, values,
-                       scores);
+    HKV_LAUNCH(tm, "upsert_serial", (upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), s, t, n, keys,
+               values, scores);
     return hipGetLastError();
   }
-  if (DUAL) {
-    hipLaunchKernelGGL(link_dual_kernel, dim3(grid_for(n * kInsG)), dim3(kBlock), 0, s, t, n, keys,
-                       next, target);
+  if constexpr (DUAL) {
+    return insert_g<kInsG, V4, true>(t, n, keys, values, scores, next, target, s, tm);
   } else {
-    hipLaunchKernelGGL(link_single_kernel, dim3(grid_for(n)), dim3(kBlock), 0, s, t, n, keys, next);
+    switch (lanes_for(t)) {
+      case 4: return insert_g<4, V4, false>(t, n, keys, values, scores, next, target, s, tm);
+      case 8: return insert_g<8, V4, false>(t, n, keys, values, scores, next, target, s, tm);
+      default: return insert_g<16, V4, false>(t, n, keys, values, scores, next, target, s, tm);
+    }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n * kInsG)), dim3(kBlock), 0, s, t,
-                     n, keys, values, scores, next, target);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -708,54 +771,55 @@ hipError_t launch_init(const TableView& t, hipStream_t s) {
 }
 
 hipError_t launch_find(const TableView& t, uint64_t n, const uint64_t* keys, float* values_out,
-                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s) {
+                       uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s,
+                       KernelTimer* tm) {
   if (t.dual)
-    return vec4 ? find_d<true, true>(t, n, keys, values_out, found_out, scores_out, s)
-                : find_d<false, true>(t, n, keys, values_out, found_out, scores_out, s);
-  return vec4 ? find_d<true, false>(t, n, keys, values_out, found_out, scores_out, s)
-              : find_d<false, false>(t, n, keys, values_out, found_out, scores_out, s);
+    return vec4 ? find_d<true, true>(t, n, keys, values_out, found_out, scores_out, s, tm)
+                : find_d<false, true>(t, n, keys, values_out, found_out, scores_out, s, tm);
+  return vec4 ? find_d<true, false>(t, n, keys, values_out, found_out, scores_out, s, tm)
+              : find_d<false, false>(t, n, keys, values_out, found_out, scores_out, s, tm);
 }
 
 hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
-                         const uint64_t* scores, bool vec4, hipStream_t s) {
+                         const uint64_t* scores, bool vec4, hipStream_t s, KernelTimer* tm) {
   if (t.dual)
-    return vec4 ? assign_d<true, true>(t, n, keys, values, scores, s)
-                : assign_d<false, true>(t, n, keys, values, scores, s);
-  return vec4 ? assign_d<true, false>(t, n, keys, values, scores, s)
-              : assign_d<false, false>(t, n, keys, values, scores, s);
+    return vec4 ? assign_d<true, true>(t, n, keys, values, scores, s, tm)
+                : assign_d<false, true>(t, n, keys, values, scores, s, tm);
+  return vec4 ? assign_d<true, false>(t, n, keys, values, scores, s, tm)
+              : assign_d<false, false>(t, n, keys, values, scores, s, tm);
 }
 
 hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
                          const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
-                         bool serial, hipStream_t s) {
+                         bool serial, hipStream_t s, KernelTimer* tm) {
   if (t.dual)
-    return vec4 ? insert_d<true, true>(t, n, keys, values, scores, next, target, serial, s)
-                : insert_d<false, true>(t, n, keys, values, scores, next, target, serial, s);
-  return vec4 ? insert_d<true, false>(t, n, keys, values, scores, next, target, serial, s)
-              : insert_d<false, false>(t, n, keys, values, scores, next, target, serial, s);
+    return vec4 ? insert_d<true, true>(t, n, keys, values, scores, next, target, serial, s, tm)
+                : insert_d<false, true>(t, n, keys, values, scores, next, target, serial, s, tm);
+  return vec4 ? insert_d<true, false>(t, n, keys, values, scores, next, target, serial, s, tm)
+              : insert_d<false, false>(t, n, keys, values, scores, next, target, serial, s, tm);
 }
 
-hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s) {
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, dev_out);
+hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, "zero", zero_u64_kernel, dim3(1), dim3(1), s, dev_out);
   uint64_t blocks = (t.nb + kBlock - 1) / kBlock;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 1024) blocks = 1024;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(size_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s, t.occ, t.nb,
-                     dev_out);
+  HKV_LAUNCH(tm, "size", size_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), s, t.occ, t.nb,
+             dev_out);
   return hipGetLastError();
 }
 
 hipError_t launch_export(const TableView& t, uint64_t begin, uint64_t end, uint64_t* keys_out,
                          float* values_out, uint64_t* scores_out, uint64_t* pos_out,
-                         unsigned long long* count_out, bool vec4, hipStream_t s) {
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, count_out);
+                         unsigned long long* count_out, bool vec4, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, "zero", zero_u64_kernel, dim3(1), dim3(1), s, count_out);
   if (end > begin) {
     if (vec4)
-      hipLaunchKernelGGL(export_kernel<true>, dim3(grid_for(end - begin)), dim3(kBlock), 0, s, t, begin,
-                         end, keys_out, values_out, scores_out, pos_out, count_out);
+      HKV_LAUNCH(tm, "export", export_kernel<true>, dim3(grid_for(end - begin)), dim3(kBlock), s, t, begin,
+                 end, keys_out, values_out, scores_out, pos_out, count_out);
     else
-      hipLaunchKernelGGL(export_kernel<false>, dim3(grid_for(end - begin)), dim3(kBlock), 0, s, t, begin,
-                         end, keys_out, values_out, scores_out, pos_out, count_out);
+      HKV_LAUNCH(tm, "export", export_kernel<false>, dim3(grid_for(end - begin)), dim3(kBlock), s, t, begin,
+                 end, keys_out, values_out, scores_out, pos_out, count_out);
   }
   return hipGetLastError();
 }

@@ -12,6 +12,7 @@
 // stream need no waits at all because stream order already serializes them.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -72,6 +73,56 @@ class DeviceGuard {
   hipError_t err_;
 };
 
+// Per-kernel timing (hkv_profile_start/stop): a pair of events recorded on
+// the launch stream around every kernel launch while profiling is on.
+class Profiler final : public hkv::KernelTimer {
+ public:
+  struct Rec {
+    const char* name;
+    hipEvent_t start;
+    hipEvent_t stop;
+  };
+  void begin(hipStream_t s) override {
+    pending_ = take();
+    if (pending_) (void)hipEventRecord(pending_, s);
+  }
+  void end(hipStream_t s, const char* kernel) override {
+    hipEvent_t e = take();
+    if (!pending_ || !e) return;
+    (void)hipEventRecord(e, s);
+    recs_.push_back({kernel, pending_, e});
+    pending_ = nullptr;
+  }
+  std::vector<Rec>& records() { return recs_; }
+  void give_back(hipEvent_t e) { pool_.push_back(e); }
+  void destroy_all() {
+    for (auto& r : recs_) {
+      (void)hipEventDestroy(r.start);
+      (void)hipEventDestroy(r.stop);
+    }
+    for (auto e : pool_) (void)hipEventDestroy(e);
+    if (pending_) (void)hipEventDestroy(pending_);
+    recs_.clear();
+    pool_.clear();
+    pending_ = nullptr;
+  }
+
+ private:
+  hipEvent_t take() {
+    if (!pool_.empty()) {
+      hipEvent_t e = pool_.back();
+      pool_.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  std::vector<Rec> recs_;
+  std::vector<hipEvent_t> pool_;
+  hipEvent_t pending_ = nullptr;
+};
+
 }  // namespace
 
 struct hkv_table {
@@ -85,6 +136,9 @@ struct hkv_table {
   unsigned long long* size_host = nullptr;  // pinned
   std::mutex mu;
   std::vector<StreamEvent> last[3];  // per group: last event recorded on each stream
+  Profiler prof;
+  bool profiling = false;
+  hkv::KernelTimer* timer() { return profiling ? &prof : nullptr; }
 };
 
 namespace {
@@ -107,6 +161,7 @@ void free_storage(hkv_table* t) {
   if (t->size_host) (void)hipHostFree(t->size_host);
   for (auto& list : t->last)
     for (auto& r : list) (void)hipEventDestroy(r.event);
+  t->prof.destroy_all();
 }
 
 // Checks that [p, p + bytes) is memory the table's GPU can access: device
@@ -243,6 +298,9 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   v.nb_mask = v.pow2 ? nb - 1 : 0;
   v.dim = o->dim;
   v.dual = o->dual_bucket;
+  // Tuning override of the lanes serving one key (4, 8 or 16); anything else
+  // keeps the default chosen from dim.
+  if (const char* g = std::getenv("HKV_GROUP_LANES")) v.lanes = static_cast<uint32_t>(std::atoi(g));
   const uint64_t value_bytes = cap * o->dim * sizeof(float);
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
@@ -308,7 +366,7 @@ HKV_API hkv_status hkv_find(hkv_table* t, uint64_t n, const uint64_t* keys, floa
   DeviceGuard dg(t->opt.device);
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   if ((st = order_before(t, kReader, stream)) != HKV_OK) return st;
-  const hipError_t e = hkv::launch_find(t->view, n, keys, values_out, found_out, scores_out, vec4, stream);
+  const hipError_t e = hkv::launch_find(t->view, n, keys, values_out, found_out, scores_out, vec4, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, "find launch");
   return record_after(t, kReader, stream);
 }
@@ -332,7 +390,8 @@ HKV_API hkv_status hkv_insert_or_assign(hkv_table* t, uint64_t n, const uint64_t
   if (!serial && (st = ensure_workspace(t, n)) != HKV_OK) return st;
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
   const hipError_t e =
-      hkv::launch_insert(t->view, n, keys, values, scores, t->ws_next, t->ws_target, vec4, serial, stream);
+      hkv::launch_insert(t->view, n, keys, values, scores, t->ws_next, t->ws_target, vec4, serial, stream,
+                         t->timer());
   if (e != hipSuccess) return fail_hip(e, "insert_or_assign launch");
   return record_after(t, kInserter, stream);
 }
@@ -353,7 +412,7 @@ HKV_API hkv_status hkv_assign(hkv_table* t, uint64_t n, const uint64_t* keys, co
   DeviceGuard dg(t->opt.device);
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   if ((st = order_before(t, kUpdater, stream)) != HKV_OK) return st;
-  const hipError_t e = hkv::launch_assign(t->view, n, keys, values, scores, vec4, stream);
+  const hipError_t e = hkv::launch_assign(t->view, n, keys, values, scores, vec4, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, "assign launch");
   return record_after(t, kUpdater, stream);
 }
@@ -365,7 +424,7 @@ HKV_API hkv_status hkv_size(hkv_table* t, uint64_t* out_host, hipStream_t stream
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   hkv_status st = order_before(t, kReader, stream);
   if (st != HKV_OK) return st;
-  hipError_t e = hkv::launch_size(t->view, t->size_dev, stream);
+  hipError_t e = hkv::launch_size(t->view, t->size_dev, stream, t->timer());
   if (e == hipSuccess)
     e = hipMemcpyAsync(t->size_host, t->size_dev, sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
   if (e != hipSuccess) return fail_hip(e, "size launch");
@@ -399,7 +458,54 @@ HKV_API hkv_status hkv_export_batch(hkv_table* t, uint64_t offset, uint64_t n_sl
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   if ((st = order_before(t, kReader, stream)) != HKV_OK) return st;
   const hipError_t e = hkv::launch_export(t->view, begin, end, keys_out, values_out, scores_out, pos_out,
-                                          reinterpret_cast<unsigned long long*>(count_out), vec4, stream);
+                                          reinterpret_cast<unsigned long long*>(count_out), vec4, stream,
+                                          t->timer());
   if (e != hipSuccess) return fail_hip(e, "export launch");
   return record_after(t, kReader, stream);
+}
+
+HKV_API hkv_status hkv_profile_start(hkv_table* t) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  for (auto& r : t->prof.records()) {
+    (void)hipEventSynchronize(r.stop);
+    t->prof.give_back(r.start);
+    t->prof.give_back(r.stop);
+  }
+  t->prof.records().clear();
+  t->profiling = true;
+  return HKV_OK;
+}
+
+HKV_API hkv_status hkv_profile_stop(hkv_table* t, hkv_kernel_stat* out, uint32_t cap, uint32_t* count) {
+  if (!t || !count || (cap && !out)) return fail(HKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  t->profiling = false;
+  std::vector<hkv_kernel_stat> agg;
+  hkv_status st = HKV_OK;
+  for (auto& r : t->prof.records()) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == HKV_OK) st = fail_hip(e, "timing event");
+    hkv_kernel_stat* a = nullptr;
+    for (auto& x : agg)
+      if (std::strncmp(x.name, r.name, sizeof(x.name)) == 0) a = &x;
+    if (!a) {
+      agg.push_back(hkv_kernel_stat{});
+      a = &agg.back();
+      std::snprintf(a->name, sizeof(a->name), "%s", r.name);
+    }
+    a->launches += 1;
+    a->total_ms += ms;
+    if (ms > a->max_ms) a->max_ms = ms;
+    t->prof.give_back(r.start);
+    t->prof.give_back(r.stop);
+  }
+  t->prof.records().clear();
+  *count = static_cast<uint32_t>(agg.size());
+  for (uint32_t j = 0; j < cap && j < agg.size(); ++j) out[j] = agg[j];
+  return st;
 }

@@ -166,6 +166,27 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
                             uint64_t* keys_out, float* values_out, uint64_t* scores_out,
                             uint64_t* pos_out, uint64_t* count_out, hipStream_t stream);
 
+/*
+ * Kernel timing (tracing aid; not part of the paper's API).
+ * While profiling is on, every kernel the table launches is bracketed by two
+ * timing events recorded on the stream it is launched on; a record's time is
+ * the elapsed time between them.
+ */
+typedef struct hkv_kernel_stat {
+  char name[32];      /* find, assign, upsert_probe, upsert_owner, upsert_serial, size, export, zero */
+  uint64_t launches;  /* timed launches of that kernel */
+  double total_ms;    /* sum of their times */
+  double max_ms;      /* longest one */
+} hkv_kernel_stat;
+
+/* hkv_profile_start - discards earlier records and turns timing on. */
+hkv_status hkv_profile_start(hkv_table* table);
+
+/* hkv_profile_stop - turns timing off, waits for every timed launch, writes
+ * one record per kernel name to out[0 .. min(cap, *count)) and the number of
+ * distinct kernels to *count. out may be NULL when cap == 0. */
+hkv_status hkv_profile_stop(hkv_table* table, hkv_kernel_stat* out, uint32_t cap, uint32_t* count);
+
 /* hkv_last_error - description of the last failure on the calling thread. */
 const char* hkv_last_error(void);
 
