@@ -155,23 +155,22 @@ def run_gpu(args):
             finds.append(fk)
             ups.append((uk, sc))
         out = torch.empty((batch, dim), dtype=torch.float32, device=dev)
-        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        found = [torch.empty(batch, dtype=torch.uint8, device=dev) for _ in range(total_steps)]
         tables.append(dict(lam=lam, tab=tab, finds=finds, ups=ups, vals=vals_pool, out=out, found=found,
-                           lam_start=size / cap, hits=[]))
+                           lam_start=size / cap))
     torch.cuda.synchronize()
 
     ev = []
     total_keys = 0
 
     def one_step(s, timed):
+        # warm-up steps run exactly the same calls as timed ones
         nonlocal total_keys
         for T in tables:
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             e0.record()
-            T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"])
+            T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"][s])
             e1.record()
-            if timed:
-                T["hits"].append(T["found"].sum())
             if not args.find_only:
                 uk, sc = T["ups"][s]
                 T["tab"].insert_or_assign(uk, T["vals"][s % 2], sc)
@@ -211,7 +210,8 @@ def run_gpu(args):
             d["upsert_ms"].append(e1.elapsed_time(e2))
     hit = {}
     for T in tables:
-        hit[T["lam"]] = float(torch.stack(T["hits"]).sum().item()) / (batch * args.steps)
+        hits = sum(int(f.sum().item()) for f in T["found"][args.warmup:])
+        hit[T["lam"]] = hits / (batch * args.steps)
         T["lam_end"] = T["tab"].size() / cap
     h_avg = sum(hit.values()) / len(hit)
     detail = {}

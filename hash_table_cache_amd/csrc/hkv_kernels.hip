@@ -96,7 +96,8 @@ __device__ __forceinline__ uint64_t group_min(uint64_t v) {
 
 // Copies a row of dim floats with the G lanes of a group. Each lane loads up
 // to R 16-byte pieces (4, or 2 for 16-lane groups) before storing any, so a
-// row of up to 512 bytes costs one memory round trip.
+// row of up to 512 bytes costs one memory round trip. NT: nontemporal loads
+// and stores (rows streamed out by find).
 template <int G, bool V4, bool NT>
 __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* __restrict__ src,
                                          uint32_t dim, int lane) {
@@ -109,7 +110,7 @@ __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* _
       f32x4 v[R];
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (c0 + r * G < n4) v[r] = s4[c0 + r * G];
+        if (c0 + r * G < n4) v[r] = NT ? __builtin_nontemporal_load(s4 + c0 + r * G) : s4[c0 + r * G];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (c0 + r * G < n4) {
@@ -167,7 +168,9 @@ __device__ __forceinline__ uint32_t candidate_mask(const uint32_t (&w)[NW], uint
 // positions base1 + j, mask m2 over base2 + j). The first two candidate keys
 // are loaded back to back so that they cost one memory round trip; a third
 // candidate in the same lane is rare (about 1 in 4000 lanes) and is looped.
-// Returns the table position of the matching slot or -1.
+// NT: the first two loads are nontemporal (readers only). Returns the table
+// position of the matching slot or -1.
+template <bool NT>
 __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__ keys, uint64_t k,
                                                     uint32_t m1, uint64_t base1, uint32_t m2,
                                                     uint64_t base2) {
@@ -184,8 +187,8 @@ __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__
     if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
   }
   uint64_t k0 = 0, k1 = 0;
-  if (h0) k0 = keys[p0];
-  if (h1) k1 = keys[p1];
+  if (h0) k0 = NT ? __builtin_nontemporal_load(keys + p0) : keys[p0];
+  if (h1) k1 = NT ? __builtin_nontemporal_load(keys + p1) : keys[p1];
   int64_t hit = -1;
   if (h0 && k0 == k) hit = static_cast<int64_t>(p0);
   if (h1 && k1 == k) hit = static_cast<int64_t>(p1);
@@ -204,7 +207,7 @@ __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__
 
 // Group-wide probe of the key's candidate bucket(s). Returns the hit position
 // (same value in every lane of the group) or -1.
-template <int G, bool DUAL>
+template <int G, bool DUAL, bool NT = false>
 __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane) {
   constexpr int NW = kSlots / G / 4;
   const uint64_t h = fmix64(k);
@@ -226,8 +229,8 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
     if constexpr (DUAL) {
       if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
     }
-    hit = match_candidates(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
-                           static_cast<uint64_t>(b2) * kSlots + off);
+    hit = match_candidates<NT>(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
+                               static_cast<uint64_t>(b2) * kSlots + off);
   }
   const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (bits == 0) return -1;
@@ -236,7 +239,7 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
 
 // ---------------------------------------------------------------- readers --
 
-template <int G, bool V4, bool DUAL>
+template <int G, bool V4, bool DUAL, bool NT>
 __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
                                                       const uint64_t* __restrict__ keys,
                                                       float* __restrict__ out,
@@ -246,12 +249,12 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;  // groups are lane-aligned, so a whole group leaves together
   const uint64_t k = keys[i];
-  const int64_t p = probe<G, DUAL>(t, k, lane);
+  const int64_t p = probe<G, DUAL, NT>(t, k, lane);
   if (p < 0) {
     if (lane == 0) found[i] = 0;
     return;
   }
-  copy_row<G, V4, true>(out + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
+  copy_row<G, V4, NT>(out + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
   if (lane == 0) {
     found[i] = 1;
     if (scores_out) scores_out[i] = t.scores[p];
@@ -312,10 +315,10 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(TableView t, uint64_t n,
   const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
-  const int64_t p = probe<G, DUAL>(t, keys[i], lane);
+  const int64_t p = probe<G, DUAL, true>(t, keys[i], lane);
   if (p < 0) return;
   if (values)
-    copy_row<G, V4, false>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    copy_row<G, V4, true>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
   if (scores && lane == 0) t.scores[p] = scores[i];
 }
 
@@ -352,7 +355,7 @@ __device__ __forceinline__ int own_find(const Owned& o, const TableView& t, uint
   const uint32_t valid = live >= 8 ? 0xFFu : (live <= 0 ? 0u : ((1u << live) - 1));
   const uint32_t m = (zero_byte_bits(o.dig0 ^ pat) | (zero_byte_bits(o.dig1 ^ pat) << 4)) & valid;
   const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + first;
-  const int64_t p = match_candidates(t.keys, k, m, base, 0u, base);
+  const int64_t p = match_candidates<false>(t.keys, k, m, base, 0u, base);
   const int hit = p >= 0 ? static_cast<int>(p - static_cast<int64_t>(o.b) * kSlots) : -1;
   const uint64_t bits = group_bits<kInsG>(__ballot(hit >= 0));
   if (bits == 0) return -1;
@@ -422,8 +425,8 @@ __device__ __forceinline__ void own_write_score(Owned& o, const TableView& t, in
 template <bool V4>
 __device__ __forceinline__ void own_write_row(const Owned& o, const TableView& t, int s,
                                               const float* row, int lane) {
-  copy_row<kInsG, V4, false>(t.values + (static_cast<uint64_t>(o.b) * kSlots + s) * t.dim, row, t.dim,
-                             lane);
+  copy_row<kInsG, V4, true>(t.values + (static_cast<uint64_t>(o.b) * kSlots + s) * t.dim, row, t.dim,
+                            lane);
 }
 
 // Algorithm 2 for one key against an owned bucket: update if present, else
@@ -494,7 +497,7 @@ __device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int 
 // for the first one (whose group will own the bucket), kSkipIdx for keys
 // that need no insert. The updates all happen before any insert of the batch,
 // which is one of the serial orders of the batch.
-template <int G, bool V4, bool DUAL>
+template <int G, bool V4, bool DUAL, bool NT>
 __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
                                                               const float* __restrict__ values,
@@ -510,9 +513,9 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     if (lane == 0) next[i] = kSkipIdx;
     return;
   }
-  const int64_t p = probe<G, DUAL>(t, k, lane);
+  const int64_t p = probe<G, DUAL, NT>(t, k, lane);
   if (p >= 0) {
-    copy_row<G, V4, false>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
     if (lane == 0) {
       t.scores[p] = scores[i];
       next[i] = kSkipIdx;
@@ -694,8 +697,8 @@ int lanes_for(const TableView& t) {
 template <int G, bool V4, bool DUAL>
 hipError_t find_g(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
                   uint64_t* sc, hipStream_t s, KernelTimer* tm) {
-  HKV_LAUNCH(tm, "find", (find_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n, keys,
-             out, found, sc);
+  HKV_LAUNCH(tm, "find", (find_kernel<G, V4, DUAL, true>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n,
+             keys, out, found, sc);
   return hipGetLastError();
 }
 
@@ -711,8 +714,8 @@ template <int G, bool V4, bool DUAL>
 hipError_t insert_g(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
                     const uint64_t* scores, uint32_t* next, uint32_t* target, hipStream_t s,
                     KernelTimer* tm) {
-  HKV_LAUNCH(tm, "upsert_probe", (upsert_probe_kernel<G, V4, DUAL>), dim3(grid_for(n * G)), dim3(kBlock),
-             s, t, n, keys, values, scores, next, target);
+  HKV_LAUNCH(tm, "upsert_probe", (upsert_probe_kernel<G, V4, DUAL, true>), dim3(grid_for(n * G)),
+             dim3(kBlock), s, t, n, keys, values, scores, next, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n)), dim3(kBlock), s, t,
