@@ -67,6 +67,34 @@ def parse_args():
     return p.parse_args()
 
 
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "hash_table_cache_amd", "csrc", "hkv_kernels.hip")
+PROFILE_NAMES = {"find": "find_kernel", "upsert_probe": "upsert_probe_kernel", "upsert_owner": "upsert_owner_kernel"}
+
+
+def profiled_traffic(kernel: str, dim: int, capacity_log2: int):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 summary of
+    this workload, or None when no summary matches the current kernel source."""
+    import glob
+    import hashlib
+
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(PROFILE_DIR, "*.txt"))):
+        fields = {}
+        traffic = {}
+        for line in open(path):
+            parts = line.split()
+            if len(parts) == 2 and parts[0] in ("kernel_source_sha256", "workload_dim", "workload_capacity_log2"):
+                fields[parts[0]] = parts[1]
+            elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
+                traffic[parts[1]] = int(parts[2])
+        if (fields.get("kernel_source_sha256") == sha and fields.get("workload_dim") == str(dim)
+                and fields.get("workload_capacity_log2") == str(capacity_log2)
+                and PROFILE_NAMES.get(kernel) in traffic):
+            return traffic[PROFILE_NAMES[kernel]]
+    return None
+
+
 def find_bytes_per_key(dim: int, h: float) -> float:
     return 8 + 128 + 4 + h * (8 + 8 * dim) + 1
 
@@ -350,7 +378,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": g["kernels"][g["dominant"]]["frac"],
-            "traffic": None,
+            "traffic": profiled_traffic(g["dominant"], args.dim, args.capacity_log2),
             "bytes_per_launch": g["kernels"][g["dominant"]]["bytes_per_launch"],
             "avg_launch_ms": g["kernels"][g["dominant"]]["avg_ms"],
         },
