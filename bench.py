@@ -61,6 +61,8 @@ def parse_args():
     p.add_argument("--hit-frac", type=float, default=0.9)
     p.add_argument("--new-frac", type=float, default=0.1, help="fraction of new keys in each upsert batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--insert-steps", type=int, default=5,
+                   help="extra all-new-key insert batches on the full table, reported in detail")
     p.add_argument("--find-only", action="store_true", help="time find batches only")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (counter calibration) and exit")
@@ -276,10 +278,35 @@ def run_gpu(args):
                      frac=round(gbs / HBM_PEAK_GBS, 4))
         kernels[name] = k
     dominant = max(kernels, key=lambda n: kernels[n]["total_ms"])
+    # Eviction-heavy phase (reported in detail only): all-new keys into the
+    # full table, every key lands in a full bucket (evict or reject).
+    insert_new = None
+    full = [T for T in tables if T["lam"] >= 1.0]
+    if full and args.insert_steps > 0:
+        T = full[0]
+        tab = T["tab"]
+        batches = []
+        for j in range(args.insert_steps + 1):
+            k = gen.unique_keys(SEED, 90, j * batch, batch, device=dev)
+            batches.append((k, gen.values(k, 5000 + j, dim, SEED),
+                            torch.full((batch,), 10_000 + j, dtype=torch.int64, device=dev)))
+        tab.insert_or_assign(*batches[0])
+        torch.cuda.synchronize()
+        tab.profile_start()
+        t1 = time.perf_counter()
+        for k, v, sc in batches[1:]:
+            tab.insert_or_assign(k, v, sc)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        ks = tab.profile_stop()
+        insert_new = dict(batches=args.insert_steps, bkvs=round(args.insert_steps * batch / dt / 1e9, 3),
+                          kernel_avg_ms={n: round(v[1] / v[0], 5) for n, v in ks.items()},
+                          lambda_end=round(tab.size() / cap, 4))
     for T in tables:
         T["tab"].close()
     return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
-                dominant=dominant, h=h_avg, find_ms_events=sum(find_ms_all) / len(find_ms_all))
+                dominant=dominant, h=h_avg, find_ms_events=sum(find_ms_all) / len(find_ms_all),
+                insert_new=insert_new)
 
 
 def run_cpu_baseline(args):
@@ -396,6 +423,7 @@ def main():
             "find_call_ms_events": round(g["find_ms_events"], 5),
             "per_lambda": g["detail"],
             "find_lambda_variation": round(g["find_var"], 4),
+            "insert_all_new_at_lambda_1": g["insert_new"],
             "hit_rate": round(g["h"], 4),
         },
     }

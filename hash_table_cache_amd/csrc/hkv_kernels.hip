@@ -429,33 +429,111 @@ __device__ __forceinline__ void own_write_row(const Owned& o, const TableView& t
                             lane);
 }
 
+// A value row held in registers by a 16-lane group: up to two 16-byte pieces
+// per lane (rows of up to 128 floats), loaded before the decision that needs
+// them so that its latency overlaps the bucket loads.
+struct RowRegs {
+  f32x4 v[2];
+};
+
+__device__ __forceinline__ void row_regs_load(RowRegs& r, const float* src, uint32_t dim, int lane) {
+  const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+  const uint32_t n4 = dim >> 2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t c = lane + u * kInsG;
+    if (c < n4) r.v[u] = __builtin_nontemporal_load(s4 + c);
+  }
+}
+
+__device__ __forceinline__ void row_regs_store(const RowRegs& r, float* dst, uint32_t dim, int lane) {
+  f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+  const uint32_t n4 = dim >> 2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t c = lane + u * kInsG;
+    if (c < n4) __builtin_nontemporal_store(r.v[u], d4 + c);
+  }
+}
+
 // Algorithm 2 for one key against an owned bucket: update if present, else
 // the lowest empty slot, else evict the lowest-ranked entry if the key ranks
 // higher, else reject. Empty slots are [occ, 128) because nothing is erased.
+// The input row is prefetched on entry. A full bucket is decided from one
+// round trip: each lane loads the scores and keys of its 8 slots, compares the
+// key directly (no digest filter needed) and finds the lowest (score, key)
+// in registers.
 template <bool V4>
 __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_t k, const float* row,
                                            uint64_t score, int lane) {
+  const bool in_regs = V4 && t.dim <= 8 * kInsG;
+  RowRegs rr;
+  if (in_regs) row_regs_load(rr, row, t.dim, lane);
   const uint64_t h = fmix64(k);
   const uint32_t d = digest_of(h);
-  const int hit = own_find(o, t, k, d * 0x01010101u, lane);
-  if (hit >= 0) {
-    own_write_score(o, t, hit, score, lane);
-    own_write_row<V4>(o, t, hit, row, lane);
-    return;
-  }
+  float* const table_rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
+  auto write_row = [&](int s) {
+    if (in_regs) {
+      row_regs_store(rr, table_rows + static_cast<uint64_t>(s) * t.dim, t.dim, lane);
+    } else {
+      own_write_row<V4>(o, t, s, row, lane);
+    }
+  };
   if (o.occ < kSlots) {
+    const int hit = own_find(o, t, k, d * 0x01010101u, lane);
+    if (hit >= 0) {
+      own_write_score(o, t, hit, score, lane);
+      write_row(hit);
+      return;
+    }
     const int s = static_cast<int>(o.occ);
     own_write_slot(o, t, s, k, d, score, lane);
-    own_write_row<V4>(o, t, s, row, lane);
+    write_row(s);
     o.occ += 1;
     return;
   }
-  uint64_t ms, mk;
-  int vs;
-  own_lowest(o, t, lane, &ms, &mk, &vs);
-  if (score > ms || (score == ms && k > mk)) {
+  // Full bucket: the lane's scores and keys (64 contiguous bytes each).
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+  uint64_t sc[8], kc[8];
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
+    const ulonglong2 b = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
+    sc[u] = a.x;
+    sc[u + 1] = a.y;
+    kc[u] = b.x;
+    kc[u + 1] = b.y;
+  }
+  int lh = -1;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (kc[u] == k) lh = lane * 8 + u;
+  const uint64_t hb = group_bits<kInsG>(__ballot(lh >= 0));
+  if (hb) {
+    const int hit = __shfl(lh, __ffsll(static_cast<unsigned long long>(hb)) - 1, kInsG);
+    own_write_score(o, t, hit, score, lane);
+    write_row(hit);
+    return;
+  }
+  uint64_t ls = sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = sc[u] < ls ? sc[u] : ls;
+  const uint64_t gs = group_min<kInsG>(ls);
+  uint64_t lk = ~0ull;
+  int lslot = -1;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (sc[u] == gs && (lslot < 0 || kc[u] < lk)) {
+      lk = kc[u];
+      lslot = lane * 8 + u;
+    }
+  }
+  const uint64_t gk = group_min<kInsG>(lslot >= 0 ? lk : ~0ull);
+  if (score > gs || (score == gs && k > gk)) {
+    const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
+    const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
     own_write_slot(o, t, vs, k, d, score, lane);
-    own_write_row<V4>(o, t, vs, row, lane);
+    write_row(vs);
   }
 }
 
@@ -570,20 +648,21 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
   while (todo) {
     const uint64_t i = first + (__ffsll(static_cast<unsigned long long>(todo)) - 1);
     todo &= todo - 1;
-    const uint64_t k = keys[i];
-    const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(k));
-    uint32_t c = 0;
-    if (lane == 0) c = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(keys[i]));
+    uint32_t head = 0;
+    if (lane == 0) head = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Owned o;
     own_load(o, t, b, lane);
     const uint32_t occ0 = o.occ;
-    own_upsert<V4>(o, t, k, values + i * t.dim, scores[i], lane);
-    c = __shfl(c, 0, kInsG);
-    // The chain holds at most n keys and ends at this owner's own key; the
-    // index and step bounds only guard against a corrupted chain.
-    for (uint64_t step = 0; c != static_cast<uint32_t>(i) && c < n && step < n; ++step) {
-      own_upsert<V4>(o, t, keys[c], values + static_cast<uint64_t>(c) * t.dim, scores[c], lane);
-      c = next[c];
+    // Order: the owner's own key, then the chain from its head down to (and
+    // excluding) the owner. The chain holds at most n keys; the index and
+    // step bounds only guard against a corrupted chain.
+    uint32_t cur = static_cast<uint32_t>(i);
+    for (uint64_t step = 0; step <= n; ++step) {
+      const uint32_t after = step ? next[cur] : __shfl(head, 0, kInsG);
+      own_upsert<V4>(o, t, keys[cur], values + static_cast<uint64_t>(cur) * t.dim, scores[cur], lane);
+      cur = after;
+      if (cur == static_cast<uint32_t>(i) || cur >= n) break;
     }
     if (o.occ != occ0) own_store_occ(o, t, lane);
     if (lane == 0)
