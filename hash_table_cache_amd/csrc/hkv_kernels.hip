@@ -40,6 +40,7 @@ constexpr int kSlots = 128;
 constexpr uint64_t kLockedKey = ~0ull - 1;  // keys >= this are reserved
 constexpr uint32_t kNoIdx = 0xFFFFFFFFu;    // chain end / empty chain head
 constexpr uint32_t kSkipIdx = 0xFFFFFFFEu;  // key takes no part in the insert
+constexpr uint32_t kFullBit = 0x80000000u;  // target word: the bucket was full at probe time
 constexpr uint64_t kSecondSalt = 0x9E3779B97F4A7C15ull;
 constexpr int kBlock = 256;
 constexpr int kInsG = 16;  // lanes per key in the inserter (8 slots per lane)
@@ -205,10 +206,24 @@ __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__
   return hit;
 }
 
+// Occupied slots counted from a group's digest words: slots fill in order and
+// an occupied slot never has digest 0 (group-uniform result).
+template <int G, int NW>
+__device__ __forceinline__ uint32_t line_occupancy(const uint32_t (&w)[NW]) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < NW; ++q) c += 4 - __builtin_popcount(zero_byte_bits(w[q]));
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, G);
+  return c;
+}
+
 // Group-wide probe of the key's candidate bucket(s). Returns the hit position
-// (same value in every lane of the group) or -1.
+// (same value in every lane of the group) or -1. When occ1/occ2 are given they
+// receive the occupancy of the first / second candidate bucket.
 template <int G, bool DUAL, bool NT = false>
-__device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane) {
+__device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane, uint32_t* occ1 = nullptr,
+                                         uint32_t* occ2 = nullptr) {
   constexpr int NW = kSlots / G / 4;
   const uint64_t h = fmix64(k);
   const uint32_t pat = digest_of(h) * 0x01010101u;
@@ -231,6 +246,10 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
     }
     hit = match_candidates<NT>(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
                                static_cast<uint64_t>(b2) * kSlots + off);
+  }
+  if (occ1) *occ1 = line_occupancy<G, NW>(w1);
+  if constexpr (DUAL) {
+    if (occ2) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
   }
   const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (bits == 0) return -1;
@@ -565,16 +584,21 @@ __device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int 
 }
 
 // Insert, first kernel: a group of G lanes per key probes the key's
-// candidate bucket(s). A resident key is updated in place (value row and
-// score only, no structural change, so concurrent probes stay valid). A
-// missing key is pushed onto the chain of the bucket it goes to: in
-// single-bucket mode its bucket; in dual-bucket mode the bucket Algorithm 3
-// picks from the table as it was before the batch (the less-occupied one if
-// either has room, tie: the first; else the one whose lowest-ranked entry is
-// lower). next[i] receives the previously pushed key of that chain, kNoIdx
-// for the first one (whose group will own the bucket), kSkipIdx for keys
-// that need no insert. The updates all happen before any insert of the batch,
-// which is one of the serial orders of the batch.
+// candidate bucket(s).
+// Single-bucket mode: a resident key is updated in place (value row and score
+// only, no structural change, so concurrent probes stay valid); a missing key
+// is pushed onto the chain of its bucket. The updates all happen before any
+// insert of the batch, which is one of the serial orders of the batch.
+// Dual-bucket mode: the kernel writes nothing to the table, so every group
+// sees the table as it was before the batch and two copies of one key always
+// choose the same bucket. A resident key is pushed onto the chain of the
+// bucket holding it; a missing key onto the bucket Algorithm 3 picks (the
+// less-occupied one if either has room, tie: the first; else the one whose
+// lowest-ranked entry is lower).
+// next[i] receives the previously pushed key of that chain, kNoIdx for the
+// first one (whose group will own the bucket), kSkipIdx for keys that need
+// nothing more; target[i] the bucket, with kFullBit set when the bucket had
+// no empty slot.
 template <int G, bool V4, bool DUAL, bool NT>
 __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
@@ -591,8 +615,9 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     if (lane == 0) next[i] = kSkipIdx;
     return;
   }
-  const int64_t p = probe<G, DUAL, NT>(t, k, lane);
-  if (p >= 0) {
+  uint32_t o1 = 0, o2 = 0;
+  const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
+  if (!DUAL && p >= 0) {
     copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
     if (lane == 0) {
       t.scores[p] = scores[i];
@@ -602,13 +627,17 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   }
   const uint64_t h = fmix64(k);
   uint32_t tb = bucket_of(t, h);
+  uint32_t tocc = o1;
   if constexpr (DUAL) {
     const uint32_t b1 = tb;
     const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
-    if (b2 != b1) {
-      const uint32_t o1 = t.occ[b1], o2 = t.occ[b2];
+    if (p >= 0) {
+      tb = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
+      tocc = (tb == b1) ? o1 : o2;
+    } else if (b2 != b1) {
       if (o1 < kSlots || o2 < kSlots) {
         tb = (o1 <= o2) ? b1 : b2;
+        tocc = (o1 <= o2) ? o1 : o2;
       } else {
         uint64_t s1, k1, s2, k2;
         peek_lowest(t, b1, lane, &s1, &k1);
@@ -618,20 +647,142 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     }
   }
   if (lane == 0) {
-    if constexpr (DUAL) target[i] = tb;
+    target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
     next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
+// State of a bucket owned by a 16-lane group in the owner kernel: its
+// occupancy (group-uniform), this lane's 8 digest bytes and, once loaded, the
+// scores and keys of this lane's 8 slots (slots 8*lane .. 8*lane+7). Only the
+// lane owning a slot reads or writes that slot's key, score and digest.
+struct Bucket {
+  uint32_t b;
+  uint32_t occ;
+  uint32_t dig0, dig1;
+  bool cols;  // sc/kc valid (group-uniform)
+  uint64_t sc[8];
+  uint64_t kc[8];
+};
+
+__device__ __forceinline__ void bucket_load_cols(Bucket& o, const TableView& t, int lane) {
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
+    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
+    o.sc[u] = a.x;
+    o.sc[u + 1] = a.y;
+    o.kc[u] = c.x;
+    o.kc[u + 1] = c.y;
+  }
+  o.cols = true;
+}
+
+// Writes slot s (key only when `is_new`, then digest, score) through its owner
+// lane and keeps the register copies current.
+__device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int s, bool is_new, uint64_t k,
+                                             uint32_t d, uint64_t score, int lane) {
+  if (lane != (s >> 3)) return;
+  const uint64_t p = static_cast<uint64_t>(o.b) * kSlots + s;
+  t.scores[p] = score;
+  if (is_new) {
+    t.keys[p] = k;
+    t.digests[p] = static_cast<uint8_t>(d);
+    const int sh = (s & 3) * 8;
+    if (s & 4) {
+      o.dig1 = (o.dig1 & ~(0xFFu << sh)) | (d << sh);
+    } else {
+      o.dig0 = (o.dig0 & ~(0xFFu << sh)) | (d << sh);
+    }
+  }
+  if (o.cols) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool here = u == (s & 7);
+      o.sc[u] = here ? score : o.sc[u];
+      o.kc[u] = here ? k : o.kc[u];
+    }
+  }
+}
+
+// Algorithm 2 for one key against the owned bucket, with the input row already
+// loaded. `fresh`: the key is known to be absent (a chain's first key, which
+// the probe kernel found missing, before anything was inserted).
+template <bool V4>
+__device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint64_t k, uint64_t score,
+                                             const RowRegs& rr, const float* row, bool in_regs, bool fresh,
+                                             int lane) {
+  const uint32_t d = digest_of(fmix64(k));
+  float* const rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
+  auto write_row = [&](int s) {
+    if (in_regs) {
+      row_regs_store(rr, rows + static_cast<uint64_t>(s) * t.dim, t.dim, lane);
+    } else {
+      copy_row<kInsG, V4, true>(rows + static_cast<uint64_t>(s) * t.dim, row, t.dim, lane);
+    }
+  };
+  int hit = -1;
+  if (!fresh) {
+    if (o.cols) {
+      int lh = -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (o.kc[u] == k) lh = lane * 8 + u;
+      const uint64_t hb = group_bits<kInsG>(__ballot(lh >= 0));
+      if (hb) hit = __shfl(lh, __ffsll(static_cast<unsigned long long>(hb)) - 1, kInsG);
+    } else {
+      Owned tmp{o.b, o.occ, o.dig0, o.dig1};
+      hit = own_find(tmp, t, k, d * 0x01010101u, lane);
+    }
+  }
+  if (hit >= 0) {
+    bucket_write(o, t, hit, false, k, d, score, lane);
+    write_row(hit);
+    return;
+  }
+  if (o.occ < kSlots) {
+    const int s = static_cast<int>(o.occ);
+    bucket_write(o, t, s, true, k, d, score, lane);
+    write_row(s);
+    o.occ += 1;
+    return;
+  }
+  if (!o.cols) bucket_load_cols(o, t, lane);
+  uint64_t ls = o.sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
+  const uint64_t gs = group_min<kInsG>(ls);
+  uint64_t lk = ~0ull;
+  int lslot = -1;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (o.sc[u] == gs && (lslot < 0 || o.kc[u] < lk)) {
+      lk = o.kc[u];
+      lslot = lane * 8 + u;
+    }
+  }
+  const uint64_t gk = group_min<kInsG>(lslot >= 0 ? lk : ~0ull);
+  if (score > gs || (score == gs && k > gk)) {
+    const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
+    const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
+    bucket_write(o, t, vs, true, k, d, score, lane);
+    write_row(vs);
+  }
+}
+
 // Insert, second kernel: the group of each chain's first-pushed key
 // (next == kNoIdx) owns that bucket for the whole kernel. A 16-lane group
-// covers 16 consecutive keys: one coalesced load of their next words and a
-// ballot find the owners among them, which are then served one after the
-// other. An owner applies its own key first, then the chain from its head
-// down to itself, each with Algorithm 2 against the owned bucket, and finally
-// resets the chain head. Keys of a batch are distinct, so any order within a
-// chain gives the same bucket contents.
+// covers 16 consecutive keys: one coalesced load of their next / target /
+// key / score words and a ballot find the owners among them, which are then
+// served one after the other. An owner loads, in one round trip, the bucket's
+// digest line, the chain head, its key's row and - when the probe kernel saw
+// the bucket full - the scores and keys of all slots; it applies its own key,
+// then the chain from its head down to itself (Algorithm 2, each chain key
+// costing one round trip for its inputs), writes the occupancy and resets the
+// chain head. With distinct keys any order within a chain gives the same
+// bucket contents.
 template <bool V4, bool DUAL>
 __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
@@ -643,30 +794,59 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (first >= n) return;
   const uint64_t mine = first + lane;
-  const bool owner = mine < n && next[mine] == kNoIdx;
-  uint64_t todo = group_bits<kInsG>(__ballot(owner));
+  uint32_t my_next = kSkipIdx, my_tgt = 0;
+  uint64_t my_key = 0, my_score = 0;
+  if (mine < n) {
+    my_next = next[mine];
+    my_tgt = target[mine];
+    my_key = keys[mine];
+    my_score = scores[mine];
+  }
+  uint64_t todo = group_bits<kInsG>(__ballot(my_next == kNoIdx));
+  const bool in_regs = V4 && t.dim <= 8 * kInsG;
   while (todo) {
-    const uint64_t i = first + (__ffsll(static_cast<unsigned long long>(todo)) - 1);
+    const int src = __ffsll(static_cast<unsigned long long>(todo)) - 1;
     todo &= todo - 1;
-    const uint32_t b = DUAL ? target[i] : bucket_of(t, fmix64(keys[i]));
+    const uint32_t i = static_cast<uint32_t>(first + src);
+    const uint32_t tgt = __shfl(my_tgt, src, kInsG);
+    const uint64_t k = __shfl(my_key, src, kInsG);
+    const uint64_t score = __shfl(my_score, src, kInsG);
+    Bucket o;
+    o.b = tgt & ~kFullBit;
+    o.cols = false;
     uint32_t head = 0;
-    if (lane == 0) head = __hip_atomic_load(t.head + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    Owned o;
-    own_load(o, t, b, lane);
+    if (lane == 0) head = __hip_atomic_load(t.head + o.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
+    RowRegs rr;
+    const float* row = values + static_cast<uint64_t>(i) * t.dim;
+    if (in_regs) row_regs_load(rr, row, t.dim, lane);
+    if (tgt & kFullBit) bucket_load_cols(o, t, lane);
+    o.dig0 = dv.x;
+    o.dig1 = dv.y;
+    uint32_t c = 8 - __builtin_popcount(zero_byte_bits(o.dig0)) - __builtin_popcount(zero_byte_bits(o.dig1));
+#pragma unroll
+    for (int sh = kInsG / 2; sh > 0; sh >>= 1) c += __shfl_xor(c, sh, kInsG);
+    o.occ = c;
     const uint32_t occ0 = o.occ;
-    // Order: the owner's own key, then the chain from its head down to (and
-    // excluding) the owner. The chain holds at most n keys; the index and
-    // step bounds only guard against a corrupted chain.
-    uint32_t cur = static_cast<uint32_t>(i);
-    for (uint64_t step = 0; step <= n; ++step) {
-      const uint32_t after = step ? next[cur] : __shfl(head, 0, kInsG);
-      own_upsert<V4>(o, t, keys[cur], values + static_cast<uint64_t>(cur) * t.dim, scores[cur], lane);
+    // In single-bucket mode a chain holds only keys the probe found missing,
+    // so the owner's own key, applied first, is known to be absent.
+    bucket_apply<V4>(o, t, k, score, rr, row, in_regs, !DUAL, lane);
+    // The chain holds at most n keys and ends at this owner's own key; the
+    // index and step bounds only guard against a corrupted chain.
+    uint32_t cur = __shfl(head, 0, kInsG);
+    for (uint64_t step = 0; cur != i && cur < n && step < n; ++step) {
+      const uint32_t after = next[cur];
+      const uint64_t kc = keys[cur];
+      const uint64_t scc = scores[cur];
+      const float* rowc = values + static_cast<uint64_t>(cur) * t.dim;
+      if (in_regs) row_regs_load(rr, rowc, t.dim, lane);
+      bucket_apply<V4>(o, t, kc, scc, rr, rowc, in_regs, false, lane);
       cur = after;
-      if (cur == static_cast<uint32_t>(i) || cur >= n) break;
     }
-    if (o.occ != occ0) own_store_occ(o, t, lane);
-    if (lane == 0)
-      __hip_atomic_store(t.head + b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+      if (o.occ != occ0) t.occ[o.b] = o.occ;
+      __hip_atomic_store(t.head + o.b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -797,8 +977,8 @@ hipError_t insert_g(const TableView& t, uint64_t n, const uint64_t* keys, const 
              dim3(kBlock), s, t, n, keys, values, scores, next, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n)), dim3(kBlock), s, t,
-             n, keys, values, scores, next, target);
+  HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n)), dim3(kBlock), s, t, n,
+             keys, values, scores, next, target);
   return hipGetLastError();
 }
 

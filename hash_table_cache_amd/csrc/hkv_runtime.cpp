@@ -246,7 +246,7 @@ hkv_status ensure_workspace(hkv_table* t, uint64_t n) {
   t->ws_next = t->ws_target = nullptr;
   t->ws_cap = 0;
   if (hipMalloc(&t->ws_next, cap * sizeof(uint32_t)) != hipSuccess ||
-      (t->opt.dual_bucket && hipMalloc(&t->ws_target, cap * sizeof(uint32_t)) != hipSuccess)) {
+      hipMalloc(&t->ws_target, cap * sizeof(uint32_t)) != hipSuccess) {
     (void)hipGetLastError();
     if (t->ws_next) (void)hipFree(t->ws_next);
     t->ws_next = nullptr;
@@ -267,8 +267,8 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (o->capacity == 0 || o->capacity % kSlots != 0)
     return fail(HKV_EINVAL, "capacity %llu is not a positive multiple of 128",
                 static_cast<unsigned long long>(o->capacity));
-  if (o->capacity / kSlots > 0xFFFFFFFFull)
-    return fail(HKV_EINVAL, "capacity %llu exceeds 2^32 buckets", static_cast<unsigned long long>(o->capacity));
+  if (o->capacity / kSlots > 0x7FFFFFFFull)
+    return fail(HKV_EINVAL, "capacity %llu exceeds 2^31 - 1 buckets", static_cast<unsigned long long>(o->capacity));
   if (o->dim == 0 || o->dim > kMaxDim) return fail(HKV_EINVAL, "dim %u outside [1, %u]", o->dim, kMaxDim);
   if (o->bucket_slots != 0 && o->bucket_slots != kSlots)
     return fail(HKV_EINVAL, "bucket_slots %u: only 128-slot buckets exist", o->bucket_slots);

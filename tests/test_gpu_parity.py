@@ -449,3 +449,39 @@ def test_dual_bucket_invariants_and_retention():
     f = found.cpu().numpy().astype(bool)
     assert np.array_equal(f, np.array([x in res for x in qn.tolist()]))
     assert all(freq[x] == s for x, s in zip(qn[f].tolist(), np_u64(scs)[f].tolist()))
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_duplicate_keys_in_a_batch_keep_the_table_consistent(dual):
+    """Duplicates within one write batch: which occurrence wins is unspecified,
+    but no key may become resident twice and every stored row must be one of
+    the rows written for that key (full buckets, so evictions happen too)."""
+    H = hkv()
+    C, D = 32 * SLOTS, 4
+    tab = H.HashTable(C, D, dual_bucket=dual)
+    rng = np.random.default_rng(17)
+    pool = rng.integers(1, 1 << 62, size=3 * C, dtype=np.int64)
+    written = {}
+    for step in range(1, 9):
+        base = rng.choice(pool, size=C // 2, replace=False)
+        k = np.concatenate([base, rng.choice(base, size=C // 4)])  # ~1/3 duplicated
+        k = rng.permutation(k)
+        kt = torch.from_numpy(k).to(dev())
+        ver = torch.arange(k.size, dtype=torch.int64, device=dev()) + step * 100000
+        v = gen.values(kt, ver, D)
+        sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+        tab.insert_or_assign(kt, v, sc)
+        for kk, vv in zip(k.view(np.uint64).tolist(), ver.cpu().numpy().tolist()):
+            written.setdefault(kk, set()).add(vv)
+        gk, gv, gs, gp = tab.export_batch()
+        ku = np_u64(gk)
+        assert np.unique(ku).size == ku.size
+        assert tab.size() == ku.size <= C
+        # each resident row is the row of one of the versions written for that key
+        gvn = gv.cpu().numpy()
+        for j in rng.choice(ku.size, size=min(200, ku.size), replace=False).tolist():
+            key = int(ku[j])
+            vers = torch.tensor(sorted(written[key]), dtype=torch.int64)
+            cand = gen.values(torch.full((vers.numel(),), int(np.uint64(key).view(np.int64)), dtype=torch.int64),
+                              vers, D).numpy()
+            assert any(np.array_equal(cand[r].view(np.uint32), gvn[j].view(np.uint32)) for r in range(len(vers)))
