@@ -83,6 +83,8 @@ def lib():
     L.oracle_murmur3_x64_128.restype = None
     L.oracle_route.argtypes = [vp, u64, P64, P64, P64, P8]
     L.oracle_route.restype = None
+    L.oracle_route_buckets.argtypes = [u64, ctypes.c_int, u64, P64, P64, P64, P8]
+    L.oracle_route_buckets.restype = None
     L.oracle_find.argtypes = [vp, u64, P64, PF, P8, P64, P64]
     L.oracle_find.restype = None
     L.oracle_insert_or_assign.argtypes = [vp, u64, P64, PF, P64, P64, P32]
@@ -110,6 +112,17 @@ def _keys(a) -> np.ndarray:
     if a.dtype != np.uint64:
         raise TypeError(f"keys/scores must be uint64 (or int64 bit patterns), got {a.dtype}")
     return a
+
+
+def route_buckets(keys, buckets: int, dual: bool = False):
+    """(b1, b2, digest) of every key for a table of `buckets` buckets."""
+    keys = _keys(keys)
+    n = keys.size
+    b1 = np.empty(n, np.uint64)
+    b2 = np.empty(n, np.uint64)
+    d = np.empty(n, np.uint8)
+    lib().oracle_route_buckets(int(buckets), int(dual), n, _u64p(keys), _u64p(b1), _u64p(b2), _u8p(d))
+    return b1, b2, d
 
 
 def fmix64(k: int) -> int:

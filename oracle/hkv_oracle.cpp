@@ -325,6 +325,20 @@ void oracle_route(const oracle_table* h, uint64_t n, const uint64_t* keys, uint6
   }
 }
 
+// Routing of n keys for a table of `buckets` buckets, without a table.
+void oracle_route_buckets(uint64_t buckets, int dual, uint64_t n, const uint64_t* keys, uint64_t* b1,
+                          uint64_t* b2, uint8_t* d) {
+  Table t;
+  t.buckets = buckets;
+  t.dual = dual != 0;
+  for (uint64_t i = 0; i < n; ++i) {
+    const Route r = route(t, keys[i]);
+    if (b1) b1[i] = r.b1;
+    if (b2) b2[i] = r.b2;
+    if (d) d[i] = r.d;
+  }
+}
+
 // find (reader): on a hit writes the value row (or tag), found = 1 and the
 // score; on a miss writes found = 0 and leaves the row, tag and score alone.
 // Reserved keys always miss. Scores are never modified.

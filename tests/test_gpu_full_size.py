@@ -1,0 +1,320 @@
+"""Full-size GPU checks, in the launch configuration the benchmark uses.
+
+At these sizes the oracle cannot replay whole workloads in test time, so the
+checks are (a) exact on samples the closed form fixes one by one - the contents
+of sampled buckets are the top 128 by (score, key) of every key routed there
+(single-bucket mode, distinct keys, scores never decreasing) - and exact on
+every find output (found iff exported, row = the row generated for the
+key's last write, score = last written score), and (b) invariants at any size:
+no key resident twice, at most 128 entries per bucket, every entry in one of
+its candidate buckets, size = exported count <= capacity, and for dual-bucket
+mode top-N retention against the ideal top N by (score, key).
+
+Bucket routing of the expected sets comes from the oracle's route function.
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import hkv_inputs as gen
+import oracle
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+SLOTS = 128
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def hkv():
+    import hash_table_cache_amd
+
+    return hash_table_cache_amd
+
+
+def u64(t):
+    return t.detach().cpu().numpy().view(np.uint64)
+
+
+def log(msg):
+    print(f"[full-size] {msg}", flush=True)
+
+
+def route_all(keys_np, capacity, dual=False):
+    """(b1, b2) of keys under a table of `capacity` slots (oracle routing)."""
+    b1, b2, _ = oracle.route_buckets(keys_np, capacity // SLOTS, dual)
+    return b1, b2
+
+
+def export_all(tab, with_values=False):
+    k, v, s, p = tab.export_batch(with_values=with_values)
+    return k, v, s, p
+
+
+def check_invariants(tab, k, p, capacity):
+    n = k.numel()
+    assert tab.size() == n <= capacity
+    assert torch.unique(k).numel() == n, "a key is resident twice"
+    counts = torch.bincount(torch.div(p, SLOTS, rounding_mode="floor"), minlength=capacity // SLOTS)
+    assert int(counts.max()) <= SLOTS
+
+
+def check_find_exact(tab, q, resident_sorted, version_of):
+    """find outputs against the exported table: found iff resident, row = the
+    generated row of (key, version), score = version, misses untouched."""
+    n = q.numel()
+    d = tab.dim
+    nan = torch.full((n, d), 0x7FC00BAD, dtype=torch.int32, device=dev()).view(torch.float32)
+    sent = torch.full((n,), 0x5EED, dtype=torch.int64, device=dev())
+    vals, found, scores = tab.find(q, values_out=nan, scores_out=sent)
+    torch.cuda.synchronize()
+    idx = torch.searchsorted(resident_sorted, q)
+    idx = torch.clamp(idx, max=resident_sorted.numel() - 1)
+    expect = resident_sorted[idx] == q
+    assert torch.equal(found.bool(), expect)
+    f = expect
+    ver = version_of(q[f])
+    assert torch.equal(scores[f], ver)
+    assert torch.equal(vals[f].view(torch.int32), gen.values(q[f], ver, d).view(torch.int32))
+    assert bool((vals[~f].view(torch.int32) == 0x7FC00BAD).all())
+    assert bool((scores[~f] == 0x5EED).all())
+    return int(f.sum())
+
+
+@pytest.mark.parametrize("lam", [0.5, 1.0])
+def test_lambda_sweep_table_at_full_size(lam):
+    """2^26 slots, dim 64, single bucket: fill with distinct uniform keys in
+    2^20 batches (score = batch index), then exact contents of 2000 sampled
+    buckets, an exact 2^20-key find (90 % resident), one upsert step
+    (90 % resident, 10 % new), and the checks again."""
+    H = hkv()
+    cap, D, batch = 1 << 26, 64, 1 << 20
+    seed = 0x484B56000000AA00 + int(lam * 100)
+    tab = H.HashTable(cap, D)
+    t0 = time.time()
+    target = int(lam * cap)
+    cursor, step = 0, 0
+    score_parts = []
+    while tab.size() < target:
+        n = batch if lam >= 1.0 else min(batch, target - tab.size())
+        step += 1
+        k = gen.unique_keys(seed, 1, cursor, n, device=dev())
+        tab.insert_or_assign(k, gen.values(k, step, D), torch.full((n,), step, dtype=torch.int64, device=dev()))
+        score_parts.append((cursor, n, step))
+        cursor += n
+    log(f"lambda {lam}: {cursor} keys in {step} batches, size {tab.size()}, {time.time() - t0:.1f}s")
+    allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
+    alls = torch.cat([torch.full((n,), st, dtype=torch.int64, device=dev()) for _, n, st in score_parts])
+
+    def check(allk, alls):
+        k, _, s, p = export_all(tab)
+        check_invariants(tab, k, p, cap)
+        # every resident key's score is its last written score
+        order = torch.argsort(allk)
+        sk, ss = allk[order], alls[order]
+        pos = torch.searchsorted(sk, k)
+        assert torch.equal(sk[pos], k)
+        assert torch.equal(ss[pos], s)
+        # sampled buckets: exact top-128 by (score, key) of every key routed there
+        B = cap // SLOTS
+        rng = np.random.default_rng(int(lam * 1000) + allk.numel())
+        sample = np.sort(rng.choice(B, size=2000, replace=False)).astype(np.uint64)
+        akn, asn = u64(allk), alls.cpu().numpy().astype(np.uint64)
+        b1, _ = route_all(akn, cap)
+        sel = np.zeros(B, bool)
+        sel[sample.astype(np.int64)] = True
+        m = sel[b1.astype(np.int64)]
+        kk, ssel, bb = akn[m], asn[m], b1[m]
+        o = np.lexsort((kk, ssel, bb))
+        kk, bb = kk[o], bb[o]
+        expect = {}
+        for b in sample.tolist():
+            expect[b] = set()
+        ub, start, cnt = np.unique(bb, return_index=True, return_counts=True)
+        for b, st, c in zip(ub.tolist(), start.tolist(), cnt.tolist()):
+            expect[b] = set(kk[st + max(0, c - SLOTS):st + c].tolist())
+        kn, pn = u64(k), u64(p)
+        bk = pn // SLOTS
+        msk = sel[bk.astype(np.int64)]
+        got = {b: set() for b in sample.tolist()}
+        for key, b in zip(kn[msk].tolist(), bk[msk].tolist()):
+            got[b].add(key)
+        assert got == expect
+        return torch.sort(k).values
+
+    resident = check(allk, alls)
+    # exact find, 90 % resident (recent keys), 10 % never inserted
+    rng = torch.Generator(device="cpu").manual_seed(5)
+    hits = resident[torch.randperm(resident.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
+    miss = gen.unique_keys(seed, 7, 0, batch - hits.numel(), device=dev())
+    q = gen.shuffle(torch.cat([hits, miss]), seed, 8)
+    order = torch.argsort(allk)
+    sk, ss = allk[order], alls[order]
+
+    def version(keys):
+        return ss[torch.searchsorted(sk, keys)]
+
+    nf = check_find_exact(tab, q, resident, version)
+    assert nf == hits.numel()
+    # one upsert step: 90 % resident keys re-written, 10 % new
+    step += 1
+    res = resident[torch.randperm(resident.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
+    new = gen.unique_keys(seed, 1, cursor, batch - res.numel(), device=dev())
+    uk = gen.shuffle(torch.cat([res, new]), seed, 9)
+    tab.insert_or_assign(uk, gen.values(uk, step, D), torch.full((batch,), step, dtype=torch.int64, device=dev()))
+    allk2 = torch.cat([allk, new])
+    alls2 = torch.cat([alls, torch.full((new.numel(),), step, dtype=torch.int64, device=dev())])
+    # re-written keys carry the new score
+    o2 = torch.argsort(allk2)
+    sk2, ss2 = allk2[o2], alls2[o2].clone()
+    ss2[torch.searchsorted(sk2, res)] = step
+    check(sk2, ss2)
+    tab.close()
+
+
+def test_continuous_online_dual_bucket_zipf_retention():
+    """2^27 slots, dim 64, dual bucket; keys drawn Zipf(1.05) over 2^30 ids,
+    2^20 draws per batch deduplicated, score = cumulative frequency (LFU),
+    value version = score. Warm up until size == capacity, then 200 batches.
+    Invariants after the run, exact find on a sampled batch, and top-N
+    retention >= 0.99 against the ideal top N by (frequency, key)."""
+    H = hkv()
+    cap, D, draws, n_ids = 1 << 27, 64, 1 << 20, 1 << 30
+    seed = 0x484B560000000003
+    tab = H.HashTable(cap, D, dual_bucket=True)
+    zipf = gen.Zipf(1.05, n_ids)
+    freq = torch.zeros(n_ids + 1, dtype=torch.int64, device=dev())
+    t0 = time.time()
+    b = 0
+    first_evict = None
+    steady = 0
+    ins_ms = 0.0
+    ins_keys = 0
+    size = 0
+    kernels = None
+    while steady < 200:
+        if size >= cap and kernels is None:
+            kernels = {}
+            tab.profile_start()
+        r = zipf.draw(seed, 1, b * draws, draws, device=dev())
+        uniq, cnt = torch.unique(r, return_counts=True)
+        fresh = int((freq[uniq] == 0).sum())
+        freq.index_add_(0, uniq, cnt)
+        sc = freq[uniq]
+        v = gen.values(uniq, sc, D)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tab.insert_or_assign(uniq, v, sc)
+        e1.record()
+        new_size = tab.size()
+        if first_evict is None and new_size - size < fresh:
+            first_evict = size / cap
+        if size >= cap:
+            steady += 1
+            ins_ms += e0.elapsed_time(e1)
+            ins_keys += uniq.numel()
+        size = new_size
+        assert size <= cap
+        b += 1
+        if b > 2000:
+            raise AssertionError("table never reached full capacity")
+    kernels = tab.profile_stop()
+    log("dual zipf: steady-state kernels " + ", ".join(f"{n} {v[1] / v[0]:.3f} ms" for n, v in kernels.items()))
+    log(f"dual zipf: {b} batches ({b - 200} to fill), first eviction at lambda {first_evict:.4f}, "
+        f"{time.time() - t0:.1f}s; steady-state insert_or_assign {ins_keys / ins_ms / 1e6:.3f} B-KV/s "
+        f"({ins_keys / 200:.0f} distinct keys per batch)")
+    k, v, s, p = export_all(tab)
+    check_invariants(tab, k, p, cap)
+    assert torch.equal(s, freq[k])
+    # every entry sits in one of its two candidate buckets
+    kn = u64(k)
+    b1, b2 = route_all(kn, cap, dual=True)
+    bk = u64(p) // SLOTS
+    assert np.all((bk == b1) | (bk == b2))
+    # sampled rows are the rows generated for (key, frequency)
+    pick = torch.randperm(k.numel(), device=dev())[:200000]
+    vs = torch.empty((pick.numel(), D), dtype=torch.float32, device=dev())
+    vals, found, scs = tab.find(k[pick], values_out=vs, with_scores=True)
+    assert bool(found.bool().all())
+    assert torch.equal(vals.view(torch.int32), gen.values(k[pick], freq[k[pick]], D).view(torch.int32))
+    # top-N retention: ideal = the cap highest (frequency, key) among all keys seen
+    seen = torch.nonzero(freq > 0).flatten()
+    fs = freq[seen]
+    # rank by frequency, ties by the larger key: sort by key ascending then stable by frequency
+    o = torch.argsort(seen, descending=True)
+    o = o[torch.argsort(fs[o], descending=True, stable=True)]
+    ideal = seen[o[:cap]]
+    mark = torch.zeros(n_ids + 1, dtype=torch.bool, device=dev())
+    mark[ideal] = True
+    retained = int(mark[k].sum())
+    retention = retained / cap
+    log(f"dual zipf: top-N retention {retention:.5f} (N = {cap}, {seen.numel()} distinct keys seen)")
+    assert retention >= 0.99
+    # exact find on a batch of drawn keys (resident or not)
+    q = torch.unique(zipf.draw(seed, 2, 0, draws, device=dev()))
+    check_find_exact(tab, q, torch.sort(k).values, lambda kk: freq[kk])
+    tab.close()
+
+
+def test_tiered_values_dual_bucket_zipf():
+    """Values in pinned, GPU-mapped host memory, dual bucket, dim 128, keys
+    Zipf(1.2) over 2^32 ids, LRU scores (value version = score). Capacity 2^26
+    (32 GiB of pinned rows; the workload's 2^28 needs 128 GiB). Warm cache:
+    ranks 1 .. 1.0625 * capacity in 2^19 batches from the coldest down to the
+    hottest, so that with LRU scores the hottest ranks are the most recent;
+    then 3 steps of a 2^20-draw find and a 2^19-draw upsert. Invariants and
+    exact find."""
+    H = hkv()
+    cap, D = 1 << 26, 128
+    seed = 0x484B560000000005
+    tab = H.HashTable(cap, D, dual_bucket=True, values_on_host=True)
+    t0 = time.time()
+    step = 0
+    hi = cap + cap // 16
+    while hi > 0:
+        step += 1
+        lo = max(1, hi - (1 << 19) + 1)
+        k = torch.arange(hi, lo - 1, -1, dtype=torch.int64, device=dev())
+        hi = lo - 1
+        tab.insert_or_assign(k, gen.values(k, step, D), torch.full((k.numel(),), step, dtype=torch.int64, device=dev()))
+    log(f"tiered: filled ranks {cap + cap // 16}..1 in {step} batches, size {tab.size()}, {time.time() - t0:.1f}s")
+    zipf = gen.Zipf(1.2, 1 << 32)
+    last = {}
+    f_ms, f_keys = 0.0, 0
+    for j in range(3):
+        step += 1
+        q = zipf.draw(seed, 1, j * (1 << 20), 1 << 20, device=dev())
+        k, _, s, p = export_all(tab)
+        resident = torch.sort(k).values
+        ks, ss = torch.sort(k)
+        sc_sorted = s[ss]
+
+        def version(keys):
+            return sc_sorted[torch.searchsorted(resident, keys)]
+
+        out = torch.empty((q.numel(), D), dtype=torch.float32, device=dev())
+        fnd = torch.empty(q.numel(), dtype=torch.uint8, device=dev())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tab.find(q, values_out=out, found_out=fnd)
+        e1.record()
+        torch.cuda.synchronize()
+        f_ms += e0.elapsed_time(e1)
+        f_keys += q.numel()
+        hits = check_find_exact(tab, q, resident, version)
+        log(f"tiered: step {j}: {hits}/{q.numel()} hits")
+        u = torch.unique(zipf.draw(seed, 2, j * (1 << 19), 1 << 19, device=dev()))
+        tab.insert_or_assign(u, gen.values(u, step, D), torch.full((u.numel(),), step, dtype=torch.int64, device=dev()))
+    k, _, s, p = export_all(tab)
+    check_invariants(tab, k, p, cap)
+    b1, b2 = route_all(u64(k), cap, dual=True)
+    bk = u64(p) // SLOTS
+    assert np.all((bk == b1) | (bk == b2))
+    log(f"tiered: find {f_keys / f_ms / 1e6:.4f} B-KV/s ({f_ms / 3:.2f} ms per 2^20-key batch, rows over the host link)")
+    tab.close()
