@@ -17,6 +17,8 @@ struct TableView {
   float* values;      // [nb*128*dim]  HBM, or host-mapped pinned memory
   uint32_t* occ;      // [nb]  occupied slots; slots [0, occ) are the occupied ones
   uint32_t* head;     // [nb]  inserter chain heads; all 0xFFFFFFFF between calls
+  uint64_t* bmin;     // [2*nb] dual mode: lowest (score, key) of each full bucket
+                      // as its last owner left it; key ~0 = not known
   uint64_t nb;        // number of buckets
   uint64_t nb_mask;   // nb - 1 when nb is a power of two
   uint32_t dim;

@@ -556,49 +556,45 @@ __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_
   }
 }
 
-// Lowest (score, key) of a full bucket, read-only, 16 lanes (group-uniform).
-__device__ __forceinline__ void peek_lowest(const TableView& t, uint32_t b, int lane, uint64_t* ms,
-                                            uint64_t* mk) {
-  const uint64_t base = static_cast<uint64_t>(b) * kSlots + lane * 8;
-  uint64_t sc[8];
-#pragma unroll
-  for (int u = 0; u < 8; u += 2) {
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
-    sc[u] = v.x;
-    sc[u + 1] = v.y;
+// Lowest (score, key) of a full bucket as recorded by the bucket's last owner
+// (dual mode). Read-only while inserts are probed, so every group of one
+// probe kernel sees the same values; a record that is stale (a resident key's
+// score changed since) only makes the bucket choice less good, never the
+// table inconsistent. A full bucket without a record (not produced by the
+// owner kernel, which records every bucket it leaves full) counts as lowest.
+__device__ __forceinline__ void cached_lowest(const TableView& t, uint32_t b, int lane, uint64_t* ms,
+                                              uint64_t* mk) {
+  uint64_t s = 0, k = ~0ull;
+  if (lane == 0) {
+    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.bmin + 2 * static_cast<uint64_t>(b));
+    s = c.x;
+    k = c.y;
   }
-  uint64_t ls = sc[0];
-#pragma unroll
-  for (int u = 1; u < 8; ++u) ls = sc[u] < ls ? sc[u] : ls;
-  const uint64_t gs = group_min<kInsG>(ls);
-  uint64_t lk = ~0ull;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (sc[u] == gs) {
-      const uint64_t kk = t.keys[base + u];
-      lk = kk < lk ? kk : lk;
-    }
+  s = __shfl(s, 0, kInsG);
+  k = __shfl(k, 0, kInsG);
+  if (k == ~0ull) {
+    s = 0;
+    k = 0;
   }
-  *ms = gs;
-  *mk = group_min<kInsG>(lk);
+  *ms = s;
+  *mk = k;
 }
 
 // Insert, first kernel: a group of G lanes per key probes the key's
-// candidate bucket(s).
-// Single-bucket mode: a resident key is updated in place (value row and score
-// only, no structural change, so concurrent probes stay valid); a missing key
-// is pushed onto the chain of its bucket. The updates all happen before any
-// insert of the batch, which is one of the serial orders of the batch.
-// Dual-bucket mode: the kernel writes nothing to the table, so every group
-// sees the table as it was before the batch and two copies of one key always
-// choose the same bucket. A resident key is pushed onto the chain of the
-// bucket holding it; a missing key onto the bucket Algorithm 3 picks (the
-// less-occupied one if either has room, tie: the first; else the one whose
-// lowest-ranked entry is lower).
+// candidate bucket(s). A resident key is updated in place (value row and
+// score only, no structural change, so concurrent probes stay valid). A
+// missing key is pushed onto the chain of the bucket it goes to: in
+// single-bucket mode its bucket; in dual-bucket mode the bucket Algorithm 3
+// picks: the less-occupied one if either has room (tie: the first; occupancy
+// counted from the digest lines, which this kernel never changes), else the
+// one whose recorded lowest (score, key) is lower (records are only written
+// by the owner kernel). Every input of the choice is therefore fixed for the
+// whole kernel, so two copies of one key always choose the same bucket.
 // next[i] receives the previously pushed key of that chain, kNoIdx for the
 // first one (whose group will own the bucket), kSkipIdx for keys that need
 // nothing more; target[i] the bucket, with kFullBit set when the bucket had
-// no empty slot.
+// no empty slot. The updates all happen before any insert of the batch,
+// which is one of the serial orders of the batch.
 template <int G, bool V4, bool DUAL, bool NT>
 __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
@@ -617,7 +613,7 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   }
   uint32_t o1 = 0, o2 = 0;
   const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
-  if (!DUAL && p >= 0) {
+  if (p >= 0) {
     copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
     if (lane == 0) {
       t.scores[p] = scores[i];
@@ -631,17 +627,14 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   if constexpr (DUAL) {
     const uint32_t b1 = tb;
     const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
-    if (p >= 0) {
-      tb = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
-      tocc = (tb == b1) ? o1 : o2;
-    } else if (b2 != b1) {
+    if (b2 != b1) {
       if (o1 < kSlots || o2 < kSlots) {
         tb = (o1 <= o2) ? b1 : b2;
         tocc = (o1 <= o2) ? o1 : o2;
       } else {
         uint64_t s1, k1, s2, k2;
-        peek_lowest(t, b1, lane, &s1, &k1);
-        peek_lowest(t, b2, lane, &s2, &k2);
+        cached_lowest(t, b1, lane, &s1, &k1);
+        cached_lowest(t, b2, lane, &s2, &k2);
         tb = (s2 < s1 || (s2 == s1 && k2 < k1)) ? b2 : b1;
       }
     }
@@ -828,9 +821,9 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     for (int sh = kInsG / 2; sh > 0; sh >>= 1) c += __shfl_xor(c, sh, kInsG);
     o.occ = c;
     const uint32_t occ0 = o.occ;
-    // In single-bucket mode a chain holds only keys the probe found missing,
-    // so the owner's own key, applied first, is known to be absent.
-    bucket_apply<V4>(o, t, k, score, rr, row, in_regs, !DUAL, lane);
+    // A chain holds only keys the probe found missing, so the owner's own
+    // key, applied first, is known to be absent.
+    bucket_apply<V4>(o, t, k, score, rr, row, in_regs, true, lane);
     // The chain holds at most n keys and ends at this owner's own key; the
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
@@ -842,6 +835,24 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       if (in_regs) row_regs_load(rr, rowc, t.dim, lane);
       bucket_apply<V4>(o, t, kc, scc, rr, rowc, in_regs, false, lane);
       cur = after;
+    }
+    if (DUAL && o.occ >= kSlots) {
+      // record the bucket's lowest (score, key) for later dual-bucket choices
+      if (!o.cols) bucket_load_cols(o, t, lane);
+      uint64_t ls = o.sc[0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
+      const uint64_t gs = group_min<kInsG>(ls);
+      uint64_t lk = ~0ull;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lk = (o.sc[u] == gs && o.kc[u] < lk) ? o.kc[u] : lk;
+      const uint64_t gk = group_min<kInsG>(lk);
+      if (lane == 0) {
+        ulonglong2 rec;
+        rec.x = gs;
+        rec.y = gk;
+        *reinterpret_cast<ulonglong2*>(t.bmin + 2 * static_cast<uint64_t>(o.b)) = rec;
+      }
     }
     if (lane == 0) {
       if (o.occ != occ0) t.occ[o.b] = o.occ;
@@ -927,6 +938,10 @@ __global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
     if (p < t.nb) {
       t.occ[p] = 0;
       t.head[p] = kNoIdx;
+      if (t.bmin) {
+        t.bmin[2 * p] = 0;
+        t.bmin[2 * p + 1] = ~0ull;
+      }
     }
   }
 }

@@ -150,6 +150,7 @@ void free_storage(hkv_table* t) {
   if (v.scores) (void)hipFree(v.scores);
   if (v.occ) (void)hipFree(v.occ);
   if (v.head) (void)hipFree(v.head);
+  if (v.bmin) (void)hipFree(v.bmin);
   if (t->values_host) {
     (void)hipHostFree(t->values_host);
   } else if (v.values) {
@@ -305,6 +306,7 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
             hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&t->size_dev, 8) == hipSuccess &&
+            (!o->dual_bucket || hipMalloc(&v.bmin, nb * 16) == hipSuccess) &&
             hipHostMalloc(&t->size_host, 8, hipHostMallocDefault) == hipSuccess;
   if (ok) {
     if (o->values_on_host) {
