@@ -14,6 +14,7 @@ Keys, scores, tags and positions are ``numpy.uint64``; values are
 from __future__ import annotations
 
 import ctypes
+import os
 import pathlib
 import subprocess
 
@@ -61,13 +62,18 @@ def _u32p(a):
 
 
 def lib():
-    """Load the oracle library, building it first if it is not there."""
+    """Load the oracle library, building it first if it is not there.
+    HKV_ORACLE_LIB names another build of the same source (used by the test
+    that plants mistakes in copies of the oracle)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not LIB_PATH.exists():
-        build()
-    L = ctypes.CDLL(str(LIB_PATH))
+    path = os.environ.get("HKV_ORACLE_LIB")
+    if path is None:
+        path = LIB_PATH
+        if not LIB_PATH.exists():
+            build()
+    L = ctypes.CDLL(str(path))
     u64, u32, vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
     P64 = ctypes.POINTER(ctypes.c_uint64)
     PF = ctypes.POINTER(ctypes.c_float)
