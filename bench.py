@@ -64,6 +64,8 @@ def parse_args():
     p.add_argument("--insert-steps", type=int, default=5,
                    help="extra all-new-key insert batches on the full table, reported in detail")
     p.add_argument("--find-only", action="store_true", help="time find batches only")
+    p.add_argument("--capacity-sweep", default="", metavar="LOG2S",
+                   help="only measure find on full tables of these capacities (e.g. 24,26,28) and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (counter calibration) and exit")
     return p.parse_args()
@@ -123,6 +125,56 @@ def calibrate_copy(mib: int) -> None:
     dt = (time.perf_counter() - t0) / 10
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
                       "copy_GBps": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def capacity_sweep(args) -> None:
+    """find on full single-bucket tables of several capacities: 2 warm-up and
+    10 timed 2^20-key batches (90 % resident) per capacity, kernel time from
+    the library's events. Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    dim, batch = args.dim, 1 << args.batch_log2
+    out = {}
+    for lg in [int(x) for x in args.capacity_sweep.split(",")]:
+        cap = 1 << lg
+        tab = H.HashTable(cap, dim)
+        cursor, step = 0, 0
+        while tab.size() < cap:
+            step += 1
+            k = gen.unique_keys(SEED, 70 + lg, cursor, batch, device=dev)
+            cursor += batch
+            tab.insert_or_assign(k, gen.values(k, step, dim, SEED), torch.full((batch,), step, dtype=torch.int64,
+                                                                              device=dev))
+        pool = gen.unique_keys(SEED, 70 + lg, cursor - 4 * batch, 4 * batch, device=dev)
+        n_hit = int(round(batch * args.hit_frac))
+        qs = []
+        for j in range(12):
+            perm = torch.argsort(gen.counter_words(SEED, 130 + lg, j * pool.numel(), pool.numel(), dev))
+            q = torch.cat([pool[perm[:n_hit]], gen.unique_keys(SEED, 110 + lg, j * batch, batch - n_hit, device=dev)])
+            qs.append(gen.shuffle(q, SEED, 150 + j))
+        vals = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        for q in qs[:2]:
+            tab.find(q, values_out=vals, found_out=found)
+        torch.cuda.synchronize()
+        tab.profile_start()
+        for q in qs[2:]:
+            tab.find(q, values_out=vals, found_out=found)
+        ms = tab.profile_stop()["find"]
+        avg = ms[1] / ms[0]
+        out[f"2^{lg}"] = dict(find_ms=round(avg, 5), find_bkvs=round(batch / avg / 1e6, 3),
+                              frac=round(batch * find_bytes_per_key(dim, n_hit / batch) / (avg * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4))
+        log(f"capacity 2^{lg}: {out[f'2^{lg}']}")
+        tab.close()
+        torch.cuda.empty_cache()
+    b = [v["find_bkvs"] for v in out.values()]
+    print(json.dumps({"capacity_sweep": out, "dim": dim, "variation": round((max(b) - min(b)) / max(b), 4)}),
+          flush=True)
 
 
 def fill_table(tab, lam, cap, batch, dim, seed, stream_id, device):
@@ -361,6 +413,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.capacity_sweep:
+        capacity_sweep(args)
         return
     g = run_gpu(args)
     cpu = None

@@ -318,3 +318,83 @@ def test_tiered_values_dual_bucket_zipf():
     assert np.all((bk == b1) | (bk == b2))
     log(f"tiered: find {f_keys / f_ms / 1e6:.4f} B-KV/s ({f_ms / 3:.2f} ms per 2^20-key batch, rows over the host link)")
     tab.close()
+
+
+def test_mixed_reader_updater_inserter_at_full_size():
+    """2^27 slots, dim 64, single bucket, lambda = 1: fill with distinct
+    uniform keys (score = step), then per step, in this order: a find of 2^20
+    keys (90 % resident), an assign of 2^19 resident keys (new row, score =
+    step), an insert_or_assign of 2^18 keys (half new, half resident, score =
+    step). Exact find after every step against the tracked last writes;
+    invariants at the end. Throughput of each call is logged."""
+    H = hkv()
+    cap, D = 1 << 27, 64
+    seed = 0x484B560000000004
+    tab = H.HashTable(cap, D)
+    step, cursor = 0, 0
+    while tab.size() < cap:
+        step += 1
+        k = gen.unique_keys(seed, 1, cursor, 1 << 20, device=dev())
+        cursor += 1 << 20
+        tab.insert_or_assign(k, gen.values(k, step, D), torch.full((k.numel(),), step, dtype=torch.int64, device=dev()))
+    log(f"mixed: filled with {cursor} keys in {step} batches")
+    # last-write version of every key ever written (version = score = step)
+    allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
+    allv = torch.repeat_interleave(torch.arange(1, step + 1, dtype=torch.int64, device=dev()), 1 << 20)
+    order = torch.argsort(allk)
+    sk, sv = allk[order], allv[order].clone()
+    times = {"find": 0.0, "assign": 0.0, "insert_or_assign": 0.0}
+    steps = 5
+    for j in range(steps):
+        step += 1
+        k, _, s, p = export_all(tab)
+        resident = torch.sort(k).values
+        perm = torch.randperm(resident.numel(), device=dev())
+        q = gen.shuffle(torch.cat([resident[perm[: 943718]], gen.unique_keys(seed, 2, j << 20, 104858, device=dev())]),
+                        seed, 10 + j)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        out = torch.empty((q.numel(), D), dtype=torch.float32, device=dev())
+        fnd = torch.empty(q.numel(), dtype=torch.uint8, device=dev())
+        ak = resident[perm[943718: 943718 + (1 << 19)]]
+        av = gen.values(ak, step, D)
+        asc = torch.full((ak.numel(),), step, dtype=torch.int64, device=dev())
+        new = gen.unique_keys(seed, 1, cursor, 1 << 17, device=dev())
+        cursor += 1 << 17
+        uk = gen.shuffle(torch.cat([new, resident[perm[-(1 << 17):]]]), seed, 20 + j)
+        uv = gen.values(uk, step, D)
+        usc = torch.full((uk.numel(),), step, dtype=torch.int64, device=dev())
+        torch.cuda.synchronize()
+        ev[0].record()
+        tab.find(q, values_out=out, found_out=fnd)
+        ev[1].record()
+        tab.assign(ak, av, asc)
+        ev[2].record()
+        tab.insert_or_assign(uk, uv, usc)
+        ev[3].record()
+        torch.cuda.synchronize()
+        times["find"] += ev[0].elapsed_time(ev[1])
+        times["assign"] += ev[1].elapsed_time(ev[2])
+        times["insert_or_assign"] += ev[2].elapsed_time(ev[3])
+        # the find saw the table before this step's writes
+        idx = torch.clamp(torch.searchsorted(resident, q), max=resident.numel() - 1)
+        expect = resident[idx] == q
+        assert torch.equal(fnd.bool(), expect)
+        ver = sv[torch.searchsorted(sk, q[expect])]
+        assert torch.equal(out[expect].view(torch.int32), gen.values(q[expect], ver, D).view(torch.int32))
+        # record this step's writes
+        sk = torch.cat([sk, new])
+        sv = torch.cat([sv, torch.zeros(new.numel(), dtype=torch.int64, device=dev())])
+        o = torch.argsort(sk)
+        sk, sv = sk[o], sv[o]
+        sv[torch.searchsorted(sk, ak)] = step
+        sv[torch.searchsorted(sk, uk)] = step
+    k, _, s, p = export_all(tab)
+    check_invariants(tab, k, p, cap)
+    assert torch.equal(s, sv[torch.searchsorted(sk, k)])
+    resident = torch.sort(k).values
+    check_find_exact(tab, gen.shuffle(resident[: 1 << 20], seed, 99), resident,
+                     lambda kk: sv[torch.searchsorted(sk, kk)])
+    n = {"find": 1 << 20, "assign": 1 << 19, "insert_or_assign": 1 << 18}
+    log("mixed: " + ", ".join(f"{op} {n[op] * steps / ms / 1e6:.3f} B-KV/s" for op, ms in times.items())
+        + f"; step {sum(times.values()) / steps:.3f} ms, {(1 << 20) * 1.75 * steps / sum(times.values()) / 1e6:.3f} B-KV/s")
+    tab.close()
