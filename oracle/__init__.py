@@ -97,6 +97,12 @@ def lib():
     L.oracle_insert_or_assign.restype = None
     L.oracle_assign.argtypes = [vp, u64, P64, PF, P64, P64]
     L.oracle_assign.restype = None
+    L.oracle_find_pos.argtypes = [vp, u64, P64, P8, P64]
+    L.oracle_find_pos.restype = None
+    L.oracle_insert_and_evict.argtypes = [vp, u64, P64, PF, P64, P64, P64, PF, P64, P64]
+    L.oracle_insert_and_evict.restype = u64
+    L.oracle_find_or_insert.argtypes = [vp, u64, P64, PF, P64, P64, P8]
+    L.oracle_find_or_insert.restype = None
     L.oracle_size.argtypes = [vp]
     L.oracle_size.restype = u64
     L.oracle_export.argtypes = [vp, u64, u64, P64, PF, P64, P64, P64]
@@ -226,6 +232,56 @@ class OracleTable:
         if tags is not None:
             tags = _keys(tags)
         self._lib.oracle_assign(self._h, n, _u64p(keys), _f32p(values), _u64p(tags), _u64p(scores))
+
+    def find_pos(self, keys):
+        """find* / contains: (found flags, slot positions; 2^64 - 1 on a miss)."""
+        keys = _keys(keys)
+        n = keys.size
+        found = np.zeros(n, np.uint8)
+        pos = np.zeros(n, np.uint64)
+        self._lib.oracle_find_pos(self._h, n, _u64p(keys), _u8p(found), _u64p(pos))
+        return found, pos
+
+    def contains(self, keys) -> np.ndarray:
+        return self.find_pos(keys)[0]
+
+    def insert_and_evict(self, keys, scores, values=None, tags=None):
+        """Upserts the batch; returns the entries that left or were turned away:
+        dict(keys, scores, values | tags), in the order they happened."""
+        keys = _keys(keys)
+        scores = _keys(scores)
+        n = keys.size
+        assert scores.size == n
+        ek = np.empty(n, np.uint64)
+        es = np.empty(n, np.uint64)
+        if self.tag_mode:
+            tags = _keys(tags)
+            et = np.empty(n, np.uint64)
+            m = self._lib.oracle_insert_and_evict(self._h, n, _u64p(keys), None, _u64p(tags), _u64p(scores),
+                                                  _u64p(ek), None, _u64p(et), _u64p(es))
+            return dict(keys=ek[:m], scores=es[:m], tags=et[:m])
+        values = np.ascontiguousarray(values, dtype=np.float32)
+        assert values.shape == (n, self.dim)
+        ev = np.empty((n, self.dim), np.float32)
+        m = self._lib.oracle_insert_and_evict(self._h, n, _u64p(keys), _f32p(values), None, _u64p(scores),
+                                              _u64p(ek), _f32p(ev), None, _u64p(es))
+        return dict(keys=ek[:m], scores=es[:m], values=ev[:m])
+
+    def find_or_insert(self, keys, scores, values=None, tags=None):
+        """Returns (rows or tags after the call, found flags). The caller's
+        arrays are not modified; copies are returned."""
+        keys = _keys(keys)
+        scores = _keys(scores)
+        n = keys.size
+        found = np.zeros(n, np.uint8)
+        if self.tag_mode:
+            t = np.array(_keys(tags), copy=True)
+            self._lib.oracle_find_or_insert(self._h, n, _u64p(keys), None, _u64p(t), _u64p(scores), _u8p(found))
+            return t, found
+        v = np.array(values, dtype=np.float32, copy=True, order="C")
+        assert v.shape == (n, self.dim)
+        self._lib.oracle_find_or_insert(self._h, n, _u64p(keys), _f32p(v), None, _u64p(scores), _u8p(found))
+        return v, found
 
     def size(self) -> int:
         return int(self._lib.oracle_size(self._h))

@@ -221,8 +221,37 @@ void write_slot(Table& t, uint64_t b, int s, uint64_t k, uint8_t d, const float*
   write_payload(t, p, v, tag);
 }
 
+// An entry that leaves the table, or is turned away, during an upsert.
+struct Departure {
+  uint64_t key = 0, score = 0, tag = 0;
+  std::vector<float> row;
+};
+
+void record_resident(const Table& t, uint64_t p, Departure* out) {
+  out->key = t.key[p];
+  out->score = t.score[p];
+  if (t.tag_mode) {
+    out->tag = t.tag[p];
+  } else {
+    out->row.assign(t.value.begin() + p * t.dim, t.value.begin() + (p + 1) * t.dim);
+  }
+}
+
+void record_offered(const Table& t, uint64_t k, const float* v, uint64_t tag, uint64_t sc, Departure* out) {
+  out->key = k;
+  out->score = sc;
+  if (t.tag_mode) {
+    out->tag = tag;
+  } else {
+    out->row.assign(v, v + t.dim);
+  }
+}
+
 // One key of insert_or_assign (Algorithm 2; Algorithm 3 in dual mode).
-Outcome upsert_one(Table& t, uint64_t k, const float* v, uint64_t tag, uint64_t sc) {
+// When `gone` is given it receives the entry that an eviction pushes out, or
+// the offered entry itself when admission turns it away.
+Outcome upsert_one(Table& t, uint64_t k, const float* v, uint64_t tag, uint64_t sc,
+                   Departure* gone = nullptr) {
   if (is_reserved(k)) return kSkipped;
   const Route r = route(t, k);
   uint64_t b;
@@ -267,9 +296,24 @@ Outcome upsert_one(Table& t, uint64_t k, const float* v, uint64_t tag, uint64_t 
   }
   // Admission control against the chosen victim.
   const uint64_t p = pos_of(b, s);
-  if (!rank_below(t.score[p], t.key[p], sc, k)) return kRejected;
+  if (!rank_below(t.score[p], t.key[p], sc, k)) {
+    if (gone) record_offered(t, k, v, tag, sc, gone);
+    return kRejected;
+  }
+  if (gone) record_resident(t, p, gone);
   write_slot(t, b, s, k, r.d, v, tag, sc);
   return kEvicted;
+}
+
+// Which keys of a batch are resident when the call starts.
+std::vector<char> resident_at_start(Table& t, uint64_t n, const uint64_t* keys) {
+  std::vector<char> res(n, 0);
+  for (uint64_t i = 0; i < n; ++i) {
+    uint64_t b;
+    int s;
+    res[i] = !is_reserved(keys[i]) && locate(t, keys[i], route(t, keys[i]), &b, &s, false);
+  }
+  return res;
 }
 
 }  // namespace
@@ -396,6 +440,99 @@ void oracle_assign(oracle_table* h, uint64_t n, const uint64_t* keys, const floa
     } else if (values) {
       for (uint32_t c = 0; c < t.dim; ++c) t.value[p * t.dim + c] = values[i * t.dim + c];
     }
+  }
+}
+
+// find* (the pointer-returning reader of §4.1, measured in §5.3): instead of
+// copying a resident key's value it reports where the value lives. Values are
+// addressed by position (§3.6: row address = value base + (b * 128 + slot)
+// rows), so the oracle reports the slot position; a miss (and a reserved key)
+// gives found = 0 and position 2^64 - 1. contains is the same lookup with
+// only the found flags kept.
+void oracle_find_pos(oracle_table* h, uint64_t n, const uint64_t* keys, uint8_t* found_out,
+                     uint64_t* pos_out) {
+  Table& t = *reinterpret_cast<Table*>(h);
+  for (uint64_t i = 0; i < n; ++i) {
+    const uint64_t k = keys[i];
+    uint64_t b;
+    int s;
+    const bool hit = !is_reserved(k) && locate(t, k, route(t, k), &b, &s, false);
+    if (found_out) found_out[i] = hit;
+    if (pos_out) pos_out[i] = hit ? pos_of(b, s) : ~0ull;
+  }
+}
+
+// insert_and_evict (§4.1: an inserter that also hands back what it evicts).
+// Reading of the order inside one call: the keys already resident when the
+// call starts are updated first (value and score, as insert_or_assign does),
+// then the other keys are inserted one at a time in input order (Algorithm 2,
+// Algorithm 3 in dual mode). Output, compacted in the order it happens: every
+// resident entry an insertion evicts (with the key, value or tag and score it
+// held) and every offered entry that admission turns away. So the output is
+// exactly the entries that were resident before the call or offered by it and
+// are not resident after it, each with its last written value and score.
+// Returns the number written (at most the number of keys not resident at the
+// start). Reserved keys are skipped.
+uint64_t oracle_insert_and_evict(oracle_table* h, uint64_t n, const uint64_t* keys, const float* values,
+                                 const uint64_t* tags, const uint64_t* scores, uint64_t* ev_keys,
+                                 float* ev_values, uint64_t* ev_tags, uint64_t* ev_scores) {
+  Table& t = *reinterpret_cast<Table*>(h);
+  const std::vector<char> res = resident_at_start(t, n, keys);
+  for (uint64_t i = 0; i < n; ++i) {
+    if (!res[i]) continue;
+    const float* v = t.tag_mode ? nullptr : values + i * t.dim;
+    upsert_one(t, keys[i], v, t.tag_mode ? tags[i] : 0, scores[i]);
+  }
+  uint64_t m = 0;
+  for (uint64_t i = 0; i < n; ++i) {
+    if (res[i] || is_reserved(keys[i])) continue;
+    const float* v = t.tag_mode ? nullptr : values + i * t.dim;
+    Departure d;
+    const Outcome o = upsert_one(t, keys[i], v, t.tag_mode ? tags[i] : 0, scores[i], &d);
+    if (o != kEvicted && o != kRejected) continue;
+    if (ev_keys) ev_keys[m] = d.key;
+    if (ev_scores) ev_scores[m] = d.score;
+    if (t.tag_mode) {
+      if (ev_tags) ev_tags[m] = d.tag;
+    } else if (ev_values) {
+      for (uint32_t c = 0; c < t.dim; ++c) ev_values[m * t.dim + c] = d.row[c];
+    }
+    ++m;
+  }
+  return m;
+}
+
+// find_or_insert (§4.1: lookup combined with insertion for cold starts).
+// Reading: a key resident when the call starts is a hit: found = 1, its stored
+// value (or tag) is written to the caller's row, and its score is replaced by
+// the offered one (the call is an inserter, and the access refreshes the
+// entry the way insert_or_assign's update does). Then every other key is
+// inserted with the caller's row and score, one at a time in input order,
+// exactly as insert_or_assign inserts (it may evict, or be turned away);
+// found = 0 and the caller's row is left as it was. Reserved keys: found = 0,
+// nothing else.
+void oracle_find_or_insert(oracle_table* h, uint64_t n, const uint64_t* keys, float* values_inout,
+                           uint64_t* tags_inout, const uint64_t* scores, uint8_t* found_out) {
+  Table& t = *reinterpret_cast<Table*>(h);
+  const std::vector<char> res = resident_at_start(t, n, keys);
+  for (uint64_t i = 0; i < n; ++i) {
+    if (found_out) found_out[i] = res[i];
+    if (!res[i]) continue;
+    uint64_t b;
+    int s;
+    locate(t, keys[i], route(t, keys[i]), &b, &s, false);
+    const uint64_t p = pos_of(b, s);
+    t.score[p] = scores[i];
+    if (t.tag_mode) {
+      tags_inout[i] = t.tag[p];
+    } else {
+      for (uint32_t c = 0; c < t.dim; ++c) values_inout[i * t.dim + c] = t.value[p * t.dim + c];
+    }
+  }
+  for (uint64_t i = 0; i < n; ++i) {
+    if (res[i] || is_reserved(keys[i])) continue;
+    const float* v = t.tag_mode ? nullptr : values_inout + i * t.dim;
+    upsert_one(t, keys[i], v, t.tag_mode ? tags_inout[i] : 0, scores[i]);
   }
 }
 

@@ -13,6 +13,10 @@ Embedding Storage", arXiv 2603.17168):
   outputs untouched (§3.2, Algorithm 1).
 * admission (§5.4, Table 9): a low-score burst into a loaded table displaces
   nobody; a high-score burst is admitted in full.
+* find* / contains (§4.1, §5.3): positions agree with export and routing;
+  insert_and_evict hands back exactly (resident before ∪ offered) − resident
+  after, with last-written rows and scores; find_or_insert returns stored rows
+  for hits and inserts misses as insert_or_assign does (closed form).
 * Proposition 3.1: about 0.5 false-positive key compares per miss.
 * Proposition 3.3: evicting from the bucket with the lower minimum halves the
   expected evicted score (1/(2n+1) vs 1/(n+1), n = 128).
@@ -248,6 +252,168 @@ def test_tag_mode_matches_value_mode():
     a, b = tv.export(), tt.export()
     assert np.array_equal(a["keys"], b["keys"]) and np.array_equal(a["pos"], b["pos"])
     np.testing.assert_array_equal(a["values"][:, 0], b["tags"].astype(np.float32))
+
+
+# ------------------------------------- find*, contains, insert_and_evict --
+
+def test_find_pos_and_contains_match_layout():
+    """find* reports where a resident key's row lives: its slot position (the
+    row address is the value base plus that many rows, §3.6). Positions are
+    checked against export (ascending positions, pinned above) and the key's
+    routed bucket; found flags against the closed-form resident set."""
+    rng = np.random.default_rng(12)
+    t, model = random_workload(51, 8, 3, batches=6, batch=700, key_pool=3000, tie_heavy=True)
+    res = model.resident_keys()
+    e = t.export()
+    where = dict(zip(e["keys"].tolist(), e["pos"].tolist()))
+    seen = np.fromiter(model.score.keys(), dtype=np.uint64)
+    q = np.concatenate([seen, rand_keys(rng, 300), u64([oracle.EMPTY_KEY, oracle.LOCKED_KEY])])
+    found, pos = t.find_pos(q)
+    b1 = t.route(q)[0]
+    for i, k in enumerate(q.tolist()):
+        if k in res:
+            assert found[i] == 1 and int(pos[i]) == where[k] and int(pos[i]) // SLOTS == int(b1[i])
+        else:
+            assert found[i] == 0 and int(pos[i]) == 2 ** 64 - 1
+    assert np.array_equal(t.contains(q), found)
+
+
+def test_find_pos_dual_bucket_lands_in_a_candidate():
+    rng = np.random.default_rng(13)
+    t = oracle.OracleTable(capacity=8 * SLOTS, dim=1, dual=True)
+    pool = rand_keys(rng, 4000)
+    for step in range(1, 5):
+        k = rng.choice(pool, 600, replace=False)
+        t.insert_or_assign(k, u64(np.full(600, step)), values=np.zeros((600, 1), np.float32))
+    e = t.export()
+    found, pos = t.find_pos(e["keys"])
+    assert found.all() and np.array_equal(pos, e["pos"])
+    b1, b2, _ = t.route(e["keys"])
+    assert np.all((pos // SLOTS == b1) | (pos // SLOTS == b2))
+
+
+@pytest.mark.parametrize("tie_heavy", [False, True])
+def test_insert_and_evict_returns_exactly_the_departed(tie_heavy):
+    """Single-bucket mode: what insert_and_evict hands back is the entries that
+    were resident before the call or offered by it and are not resident after
+    it (closed form via the top-128 model), each with its last written value
+    and score; the table itself ends as insert_or_assign would leave it."""
+    rng = np.random.default_rng(14 + tie_heavy)
+    B, dim = 4, 3
+    t = oracle.OracleTable(capacity=B * SLOTS, dim=dim)
+    model = TopKModel(lambda k: t.route(k)[0], dim)
+    pool = rand_keys(rng, 3000)
+    for step in range(1, 12):
+        keys = rng.choice(pool, 400, replace=False)
+        if tie_heavy:
+            sc = u64(np.full(keys.size, step))
+        else:
+            sc = u64(step * 1000 + rng.integers(0, 1000, size=keys.size))
+        vals = rng.standard_normal((keys.size, dim)).astype(np.float32)
+        before = model.resident_keys()
+        absent = sum(1 for k in keys.tolist() if k not in before)
+        out = t.insert_and_evict(keys, sc, values=vals)
+        model.insert_or_assign(keys, sc, vals)
+        after = model.resident_keys()
+        expect = (before | set(keys.tolist())) - after
+        got = out["keys"].tolist()
+        assert len(got) == len(set(got)) and set(got) == expect
+        assert len(got) <= absent
+        for k, s, v in zip(got, out["scores"].tolist(), out["values"]):
+            assert model.score[k] == s
+            np.testing.assert_array_equal(v, model.payload[k])
+        check_against_model(t, model, dim)
+
+
+def test_insert_and_evict_admission_bursts():
+    """§5.4, Table 9 on a full table: a burst scored below every resident is
+    handed back whole and changes nothing; a burst scored above every
+    resident is admitted whole and hands back the lowest-ranked residents of
+    each bucket it lands in."""
+    C = 32 * SLOTS
+    t = oracle.OracleTable(capacity=C, dim=1)
+    stream = gen.unique_keys(6, 1, 0, 4 * C).numpy().view(np.uint64)
+    i, step = 0, 10
+    while t.size() < C:
+        t.insert_or_assign(stream[i:i + 512], u64(np.full(512, step)), values=np.zeros((512, 1), np.float32))
+        i += 512
+        step += 1
+    snap = t.export()
+    low = gen.unique_keys(6, 2, 0, C // 8).numpy().view(np.uint64)
+    out = t.insert_and_evict(low, u64(np.ones(low.size)), values=np.full((low.size, 1), 3.0, np.float32))
+    assert sorted(out["keys"].tolist()) == sorted(low.tolist())
+    assert np.all(out["scores"] == 1) and np.all(out["values"] == 3.0)
+    after = t.export()
+    assert np.array_equal(after["keys"], snap["keys"]) and np.array_equal(after["scores"], snap["scores"])
+    high = gen.unique_keys(6, 3, 0, C // 8).numpy().view(np.uint64)
+    out = t.insert_and_evict(high, u64(np.full(high.size, 10 ** 9)), values=np.zeros((high.size, 1), np.float32))
+    assert out["keys"].size == high.size
+    found, _ = t.find_pos(high)
+    assert found.all()
+    # per bucket, the handed-back residents are that bucket's lowest by (score, key)
+    hb = t.route(high)[0]
+    per_bucket = {}
+    for b in hb.tolist():
+        per_bucket[b] = per_bucket.get(b, 0) + 1
+    snap_b = snap["pos"] // SLOTS
+    expect = set()
+    for b, c in per_bucket.items():
+        m = snap_b == b
+        order = np.lexsort((snap["keys"][m], snap["scores"][m]))
+        expect |= set(snap["keys"][m][order][:c].tolist())
+    assert set(out["keys"].tolist()) == expect
+
+
+def test_find_or_insert_hits_and_inserts():
+    """Hits: found = 1, the stored row comes back, the score becomes the offered
+    one, the row is unchanged. Misses: inserted with the caller's row and score
+    (insert_or_assign's admission), found = 0, the caller's row kept."""
+    rng = np.random.default_rng(15)
+    B, dim = 4, 2
+    t = oracle.OracleTable(capacity=B * SLOTS, dim=dim)
+    model = TopKModel(lambda k: t.route(k)[0], dim)
+    pool = rand_keys(rng, 2500)
+    for step in range(1, 10):
+        keys = rng.choice(pool, 350, replace=False)
+        sc = u64(np.full(keys.size, step))
+        vals = rng.standard_normal((keys.size, dim)).astype(np.float32)
+        before = model.resident_keys()
+        rows, found = t.find_or_insert(keys, sc, values=vals)
+        for i, k in enumerate(keys.tolist()):
+            if k in before:
+                assert found[i] == 1
+                np.testing.assert_array_equal(rows[i], model.payload[k])
+                model.score[k] = int(sc[i])
+            else:
+                assert found[i] == 0
+                np.testing.assert_array_equal(rows[i], vals[i])
+        miss = np.array([k not in before for k in keys.tolist()])
+        model.insert_or_assign(keys[miss], sc[miss], vals[miss])
+        check_against_model(t, model, dim)
+
+
+def test_new_operations_tag_mode_matches_value_mode():
+    rng = np.random.default_rng(16)
+    tv = oracle.OracleTable(capacity=4 * SLOTS, dim=2)
+    tt = oracle.OracleTable(capacity=4 * SLOTS, dim=2, tag_mode=True)
+    pool = rand_keys(rng, 2000)
+    for step in range(1, 7):
+        keys = rng.choice(pool, 500, replace=False)
+        sc = u64(np.full(500, step))
+        tags = u64(rng.integers(0, 1 << 24, 500))
+        vals = np.stack([tags.astype(np.float32), -tags.astype(np.float32)], 1)
+        if step % 2:
+            a = tv.insert_and_evict(keys, sc, values=vals)
+            b = tt.insert_and_evict(keys, sc, tags=tags)
+            assert np.array_equal(a["keys"], b["keys"]) and np.array_equal(a["scores"], b["scores"])
+            np.testing.assert_array_equal(a["values"][:, 0], b["tags"].astype(np.float32))
+        else:
+            ra, fa = tv.find_or_insert(keys, sc, values=vals)
+            rb, fb = tt.find_or_insert(keys, sc, tags=tags)
+            assert np.array_equal(fa, fb)
+            np.testing.assert_array_equal(ra[:, 0], rb.astype(np.float32))
+    a, b = tv.export(), tt.export()
+    assert np.array_equal(a["keys"], b["keys"]) and np.array_equal(a["pos"], b["pos"])
 
 
 # --------------------------------------------------------------- admission --

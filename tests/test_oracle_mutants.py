@@ -23,10 +23,10 @@ MUTANTS = {
     "bucket_from_high_bits": ("r.b1 = h1 % t.buckets;", "r.b1 = (h1 >> 32) % t.buckets;"),
     "second_hash_equals_first": ("fmix64(k ^ kSecondHashSalt) % t.buckets", "fmix64(k) % t.buckets"),
     "tie_break_larger_key": ("return s1 < s2 || (s1 == s2 && k1 < k2);", "return s1 < s2 || (s1 == s2 && k1 > k2);"),
-    "admission_inverted": ("if (!rank_below(t.score[p], t.key[p], sc, k)) return kRejected;",
-                           "if (rank_below(t.score[p], t.key[p], sc, k)) return kRejected;"),
-    "admission_by_score_only": ("if (!rank_below(t.score[p], t.key[p], sc, k)) return kRejected;",
-                                "if (sc < t.score[p]) return kRejected;"),
+    "admission_inverted": ("if (!rank_below(t.score[p], t.key[p], sc, k)) {",
+                           "if (rank_below(t.score[p], t.key[p], sc, k)) {"),
+    "admission_by_score_only": ("if (!rank_below(t.score[p], t.key[p], sc, k)) {",
+                                "if (sc < t.score[p]) {"),
     "victim_highest": ("if (rank_below(t.score[p], t.key[p], t.score[q], t.key[q])) m = s;",
                        "if (rank_below(t.score[q], t.key[q], t.score[p], t.key[p])) m = s;"),
     "d1_more_occupied": ("b = (o1 <= o2) ? r.b1 : r.b2;", "b = (o1 >= o2) ? r.b1 : r.b2;"),
@@ -41,6 +41,20 @@ MUTANTS = {
     "assign_inserts_scores_of_absent": ("if (is_reserved(k) || !locate(t, k, route(t, k), &b, &s, false)) continue;\n    const uint64_t p = pos_of(b, s);\n    if (scores) t.score[p] = scores[i];",
                                         "if (is_reserved(k)) continue;\n    if (!locate(t, k, route(t, k), &b, &s, false)) { b = route(t, k).b1; s = 0; }\n    const uint64_t p = pos_of(b, s);\n    if (scores) t.score[p] = scores[i];"),
     "export_off_by_one": ("for (uint64_t p = offset; p < end; ++p) {", "for (uint64_t p = offset; p + 1 < end; ++p) {"),
+    "find_pos_next_slot": ("if (pos_out) pos_out[i] = hit ? pos_of(b, s) : ~0ull;",
+                           "if (pos_out) pos_out[i] = hit ? pos_of(b, s) + 1 : ~0ull;"),
+    "evict_output_drops_rejected": ("    if (gone) record_offered(t, k, v, tag, sc, gone);\n    return kRejected;",
+                                    "    return kRejected;"),
+    "evict_output_reports_newcomer": ("  if (gone) record_resident(t, p, gone);", "  if (gone) record_offered(t, k, v, tag, sc, gone);"),
+    # one pass in input order: a resident key can be evicted before its own
+    # update, then comes back as a fresh insert
+    "evict_in_input_order": ("    if (!res[i]) continue;\n    const float* v = t.tag_mode ? nullptr : values + i * t.dim;\n"
+                             "    upsert_one(t, keys[i], v, t.tag_mode ? tags[i] : 0, scores[i]);\n  }\n  uint64_t m = 0;\n"
+                             "  for (uint64_t i = 0; i < n; ++i) {\n    if (res[i] || is_reserved(keys[i])) continue;",
+                             "    continue;\n  }\n  uint64_t m = 0;\n"
+                             "  for (uint64_t i = 0; i < n; ++i) {\n    if (is_reserved(keys[i])) continue;"),
+    "find_or_insert_keeps_score": ("    t.score[p] = scores[i];\n    if (t.tag_mode) {\n      tags_inout[i] = t.tag[p];",
+                                   "    if (t.tag_mode) {\n      tags_inout[i] = t.tag[p];"),
 }
 
 
