@@ -18,11 +18,15 @@ from ._native import (  # noqa: F401
     LOCKED_KEY,
     HkvError,
     hkv_assign,
+    hkv_contains,
     hkv_create,
     hkv_destroy,
     hkv_export_batch,
     hkv_find,
+    hkv_find_or_insert,
+    hkv_find_ptr,
     hkv_get_options,
+    hkv_insert_and_evict,
     hkv_insert_or_assign,
     hkv_profile_start,
     hkv_profile_stop,
@@ -86,8 +90,48 @@ class HashTable:
         hkv_find(self._h, keys, values_out, found_out, scores_out, stream, dim=self.dim, device=self.device)
         return values_out, found_out, scores_out
 
+    def find_ptr(self, keys, ptrs_out=None, found_out=None, scores_out=None, stream=None):
+        """find*: int64 row addresses (0 on a miss) and found flags."""
+        n = keys.numel()
+        if ptrs_out is None:
+            ptrs_out = torch.empty(n, dtype=torch.int64, device=self._dev())
+        if found_out is None:
+            found_out = torch.empty(n, dtype=torch.uint8, device=self._dev())
+        hkv_find_ptr(self._h, keys, ptrs_out, found_out, scores_out, stream, device=self.device)
+        return ptrs_out, found_out
+
+    def contains(self, keys, found_out=None, stream=None):
+        if found_out is None:
+            found_out = torch.empty(keys.numel(), dtype=torch.uint8, device=self._dev())
+        hkv_contains(self._h, keys, found_out, stream, device=self.device)
+        return found_out
+
     def insert_or_assign(self, keys, values, scores, stream=None) -> None:
         hkv_insert_or_assign(self._h, keys, values, scores, stream, dim=self.dim, device=self.device)
+
+    def insert_and_evict(self, keys, values, scores, out=None, stream=None):
+        """Upserts and returns (keys, values, scores, count) of what was handed
+        back; count is a one-element device tensor (nothing synchronizes).
+        `out` may pass preallocated (keys, values, scores, count) buffers of
+        n entries."""
+        n = keys.numel()
+        dev = self._dev()
+        if out is None:
+            out = (torch.empty(max(n, 1), dtype=torch.int64, device=dev),
+                   torch.empty((max(n, 1), self.dim), dtype=torch.float32, device=dev),
+                   torch.empty(max(n, 1), dtype=torch.int64, device=dev),
+                   torch.zeros(1, dtype=torch.int64, device=dev))
+        ek, ev, es, cnt = out
+        hkv_insert_and_evict(self._h, keys, values, scores, ek, ev, es, cnt, stream, dim=self.dim,
+                             device=self.device)
+        return ek, ev, es, cnt
+
+    def find_or_insert(self, keys, values, scores, found_out=None, stream=None):
+        """values is read and written in place (stored rows of hits)."""
+        if found_out is None:
+            found_out = torch.empty(keys.numel(), dtype=torch.uint8, device=self._dev())
+        hkv_find_or_insert(self._h, keys, values, scores, found_out, stream, dim=self.dim, device=self.device)
+        return values, found_out
 
     def assign(self, keys, values=None, scores=None, stream=None) -> None:
         hkv_assign(self._h, keys, values, scores, stream, dim=self.dim, device=self.device)

@@ -34,7 +34,11 @@ EXPORTS = (
     "hkv_destroy",
     "hkv_get_options",
     "hkv_find",
+    "hkv_find_ptr",
+    "hkv_contains",
     "hkv_insert_or_assign",
+    "hkv_insert_and_evict",
+    "hkv_find_or_insert",
     "hkv_assign",
     "hkv_size",
     "hkv_export_batch",
@@ -86,8 +90,16 @@ def _load() -> ctypes.CDLL:
     L.hkv_get_options.restype = st
     L.hkv_find.argtypes = [vp, u64, vp, vp, vp, vp, vp]
     L.hkv_find.restype = st
+    L.hkv_find_ptr.argtypes = [vp, u64, vp, vp, vp, vp, vp]
+    L.hkv_find_ptr.restype = st
+    L.hkv_contains.argtypes = [vp, u64, vp, vp, vp]
+    L.hkv_contains.restype = st
     L.hkv_insert_or_assign.argtypes = [vp, u64, vp, vp, vp, vp]
     L.hkv_insert_or_assign.restype = st
+    L.hkv_insert_and_evict.argtypes = [vp, u64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.hkv_insert_and_evict.restype = st
+    L.hkv_find_or_insert.argtypes = [vp, u64, vp, vp, vp, vp, vp]
+    L.hkv_find_or_insert.restype = st
     L.hkv_assign.argtypes = [vp, u64, vp, vp, vp, vp]
     L.hkv_assign.restype = st
     L.hkv_size.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64), vp]
@@ -164,6 +176,53 @@ def hkv_find(table, keys, values_out, found_out, scores_out=None, stream=None, *
         _ptr(values_out, (torch.float32,), n * dim, "values_out"),
         _ptr(found_out, (torch.uint8, torch.bool), n, "found_out"),
         _ptr(scores_out, _U64_DTYPES, n, "scores_out", nullable=True),
+        _stream(stream, device)))
+
+
+def hkv_find_ptr(table, keys, ptrs_out, found_out=None, scores_out=None, stream=None, *, device):
+    """ptrs_out: int64 tensor of n row addresses (0 on a miss)."""
+    n = keys.numel()
+    _check(lib.hkv_find_ptr(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(ptrs_out, _U64_DTYPES, n, "ptrs_out"),
+        _ptr(found_out, (torch.uint8, torch.bool), n, "found_out", nullable=True),
+        _ptr(scores_out, _U64_DTYPES, n, "scores_out", nullable=True),
+        _stream(stream, device)))
+
+
+def hkv_contains(table, keys, found_out, stream=None, *, device):
+    n = keys.numel()
+    _check(lib.hkv_contains(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(found_out, (torch.uint8, torch.bool), n, "found_out"),
+        _stream(stream, device)))
+
+
+def hkv_insert_and_evict(table, keys, values, scores, ev_keys, ev_values, ev_scores, ev_count, stream=None, *,
+                         dim, device):
+    n = keys.numel()
+    _check(lib.hkv_insert_and_evict(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values, (torch.float32,), n * dim, "values"),
+        _ptr(scores, _U64_DTYPES, n, "scores"),
+        _ptr(ev_keys, _U64_DTYPES, n, "evicted_keys"),
+        _ptr(ev_values, (torch.float32,), n * dim, "evicted_values", nullable=True),
+        _ptr(ev_scores, _U64_DTYPES, n, "evicted_scores", nullable=True),
+        _ptr(ev_count, _U64_DTYPES, 1, "evicted_count"),
+        _stream(stream, device)))
+
+
+def hkv_find_or_insert(table, keys, values, scores, found_out=None, stream=None, *, dim, device):
+    n = keys.numel()
+    _check(lib.hkv_find_or_insert(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values, (torch.float32,), n * dim, "values"),
+        _ptr(scores, _U64_DTYPES, n, "scores"),
+        _ptr(found_out, (torch.uint8, torch.bool), n, "found_out", nullable=True),
         _stream(stream, device)))
 
 

@@ -51,10 +51,29 @@ hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys,
                          const float* values, const uint64_t* scores, bool vec4, hipStream_t s,
                          KernelTimer* timer);
 
-// next: [n] u32 workspace; target: [n] u32 workspace (dual mode only).
-hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
-                         const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
-                         bool serial, hipStream_t s, KernelTimer* timer);
+// find* / contains: every output optional (ptrs: one u64 address per key).
+hipError_t launch_locate(const TableView& t, uint64_t n, const uint64_t* keys, uint64_t* ptrs_out,
+                         uint8_t* found_out, uint64_t* scores_out, hipStream_t s, KernelTimer* timer);
+
+// Arguments of the inserter calls. insert_or_assign: keys, values, scores.
+// find_or_insert: fetch = true, values is in/out, found optional.
+// insert_and_evict: ev_keys/ev_count set (ev_values, ev_scores optional);
+// ev_count is zeroed by the launch.
+struct InsertCall {
+  const uint64_t* keys;
+  float* values;
+  const uint64_t* scores;
+  bool fetch;
+  uint8_t* found;
+  uint64_t* ev_keys;
+  float* ev_values;
+  uint64_t* ev_scores;
+  unsigned long long* ev_count;
+};
+
+// next, target: [n] u32 workspaces (not used by insert_or_assign in serial mode).
+hipError_t launch_upsert(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next,
+                         uint32_t* target, bool vec4, bool serial, hipStream_t s, KernelTimer* timer);
 
 // Writes the number of occupied slots to *dev_out (device memory).
 hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s,

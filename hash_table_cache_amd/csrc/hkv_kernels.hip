@@ -280,6 +280,27 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
   }
 }
 
+// find* (pointer-returning find) and contains, §4.1 / §5.3: the key-side half
+// of find. A hit writes the device-accessible address of the key's value row
+// (host-mapped when values live in host memory), found = 1 and the score; a
+// miss writes a null address and found = 0. Every output is optional.
+template <int G, bool DUAL>
+__global__ __launch_bounds__(kBlock) void locate_kernel(TableView t, uint64_t n,
+                                                        const uint64_t* __restrict__ keys,
+                                                        uint64_t* __restrict__ ptrs_out,
+                                                        uint8_t* __restrict__ found,
+                                                        uint64_t* __restrict__ scores_out) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
+  if (i >= n) return;
+  const int64_t p = probe<G, DUAL, true>(t, keys[i], lane);
+  if (lane != 0) return;
+  if (found) found[i] = p >= 0 ? 1 : 0;
+  if (ptrs_out)
+    ptrs_out[i] = p >= 0 ? reinterpret_cast<uint64_t>(t.values + static_cast<uint64_t>(p) * t.dim) : 0ull;
+  if (scores_out && p >= 0) scores_out[i] = t.scores[p];
+}
+
 __global__ __launch_bounds__(kBlock) void size_kernel(const uint32_t* __restrict__ occ, uint64_t nb,
                                                       unsigned long long* out) {
   __shared__ unsigned long long part[kBlock / 64];
@@ -475,6 +496,36 @@ __device__ __forceinline__ void row_regs_store(const RowRegs& r, float* dst, uin
   }
 }
 
+// Output of insert_and_evict: entries handed back, compacted through an
+// atomic counter (keys == nullptr: nothing is handed back).
+struct Evicted {
+  uint64_t* keys;
+  float* values;
+  uint64_t* scores;
+  unsigned long long* count;
+};
+
+// Hands back one entry with the 16 lanes of a group: lane 0 reserves the
+// output index, the group copies the row from `src` (or from registers).
+template <bool V4>
+__device__ __forceinline__ void emit_entry(const Evicted& ev, const TableView& t, uint64_t k, uint64_t score,
+                                           const float* src, const RowRegs* regs, int lane) {
+  unsigned long long j = 0;
+  if (lane == 0) {
+    j = atomicAdd(ev.count, 1ull);
+    ev.keys[j] = k;
+    if (ev.scores) ev.scores[j] = score;
+  }
+  j = __shfl(j, 0, kInsG);
+  if (!ev.values) return;
+  float* dst = ev.values + j * t.dim;
+  if (regs) {
+    row_regs_store(*regs, dst, t.dim, lane);
+  } else {
+    copy_row<kInsG, V4, true>(dst, src, t.dim, lane);
+  }
+}
+
 // Algorithm 2 for one key against an owned bucket: update if present, else
 // the lowest empty slot, else evict the lowest-ranked entry if the key ranks
 // higher, else reject. Empty slots are [occ, 128) because nothing is erased.
@@ -484,7 +535,7 @@ __device__ __forceinline__ void row_regs_store(const RowRegs& r, float* dst, uin
 // in registers.
 template <bool V4>
 __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_t k, const float* row,
-                                           uint64_t score, int lane) {
+                                           uint64_t score, const Evicted& ev, int lane) {
   const bool in_regs = V4 && t.dim <= 8 * kInsG;
   RowRegs rr;
   if (in_regs) row_regs_load(rr, row, t.dim, lane);
@@ -551,8 +602,11 @@ __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_
   if (score > gs || (score == gs && k > gk)) {
     const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
     const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
+    if (ev.keys) emit_entry<V4>(ev, t, gk, gs, table_rows + static_cast<uint64_t>(vs) * t.dim, nullptr, lane);
     own_write_slot(o, t, vs, k, d, score, lane);
     write_row(vs);
+  } else if (ev.keys) {
+    emit_entry<V4>(ev, t, k, score, row, nullptr, lane);
   }
 }
 
@@ -595,30 +649,48 @@ __device__ __forceinline__ void cached_lowest(const TableView& t, uint32_t b, in
 // nothing more; target[i] the bucket, with kFullBit set when the bucket had
 // no empty slot. The updates all happen before any insert of the batch,
 // which is one of the serial orders of the batch.
-template <int G, bool V4, bool DUAL, bool NT>
+// FETCH (find_or_insert): a resident key's stored row is copied out to the
+// caller's row instead, its score replaced, and found[i] (if given) tells
+// hits from misses. link = false (serial inserter follows): missing keys are
+// only marked (next[i] = kNoIdx) and no chain is built.
+template <int G, bool V4, bool DUAL, bool NT, bool FETCH>
 __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
-                                                              const float* __restrict__ values,
+                                                              float* __restrict__ values,
                                                               const uint64_t* __restrict__ scores,
+                                                              uint8_t* __restrict__ found,
                                                               uint32_t* __restrict__ next,
-                                                              uint32_t* __restrict__ target) {
+                                                              uint32_t* __restrict__ target, bool link) {
   static_assert(!DUAL || G == kInsG, "dual-bucket selection works on 16-lane groups");
   const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
   const uint64_t k = keys[i];
   if (is_reserved(k)) {
-    if (lane == 0) next[i] = kSkipIdx;
+    if (lane == 0) {
+      next[i] = kSkipIdx;
+      if (FETCH && found) found[i] = 0;
+    }
     return;
   }
   uint32_t o1 = 0, o2 = 0;
   const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
   if (p >= 0) {
-    copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    if constexpr (FETCH) {
+      copy_row<G, V4, NT>(values + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
+    } else {
+      copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    }
     if (lane == 0) {
       t.scores[p] = scores[i];
       next[i] = kSkipIdx;
+      if (FETCH && found) found[i] = 1;
     }
+    return;
+  }
+  if (FETCH && found && lane == 0) found[i] = 0;
+  if (!link) {
+    if (lane == 0) next[i] = kNoIdx;
     return;
   }
   const uint64_t h = fmix64(k);
@@ -703,10 +775,10 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
 // Algorithm 2 for one key against the owned bucket, with the input row already
 // loaded. `fresh`: the key is known to be absent (a chain's first key, which
 // the probe kernel found missing, before anything was inserted).
-template <bool V4>
+template <bool V4, bool EVICT>
 __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint64_t k, uint64_t score,
                                              const RowRegs& rr, const float* row, bool in_regs, bool fresh,
-                                             int lane) {
+                                             const Evicted& ev, int lane) {
   const uint32_t d = digest_of(fmix64(k));
   float* const rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
   auto write_row = [&](int s) {
@@ -760,8 +832,13 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
   if (score > gs || (score == gs && k > gk)) {
     const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
     const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
+    // the victim's row is read (by the lanes that wrote it, if this kernel
+    // did) before the new row overwrites it
+    if constexpr (EVICT) emit_entry<V4>(ev, t, gk, gs, rows + static_cast<uint64_t>(vs) * t.dim, nullptr, lane);
     bucket_write(o, t, vs, true, k, d, score, lane);
     write_row(vs);
+  } else if constexpr (EVICT) {
+    emit_entry<V4>(ev, t, k, score, row, in_regs ? &rr : nullptr, lane);
   }
 }
 
@@ -776,13 +853,14 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
 // costing one round trip for its inputs), writes the occupancy and resets the
 // chain head. With distinct keys any order within a chain gives the same
 // bucket contents.
-template <bool V4, bool DUAL>
+template <bool V4, bool DUAL, bool EVICT>
 __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
                                                               const float* __restrict__ values,
                                                               const uint64_t* __restrict__ scores,
                                                               const uint32_t* __restrict__ next,
-                                                              const uint32_t* __restrict__ target) {
+                                                              const uint32_t* __restrict__ target,
+                                                              Evicted ev) {
   const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) & ~uint64_t(kInsG - 1);
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (first >= n) return;
@@ -823,7 +901,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     const uint32_t occ0 = o.occ;
     // A chain holds only keys the probe found missing, so the owner's own
     // key, applied first, is known to be absent.
-    bucket_apply<V4>(o, t, k, score, rr, row, in_regs, true, lane);
+    bucket_apply<V4, EVICT>(o, t, k, score, rr, row, in_regs, true, ev, lane);
     // The chain holds at most n keys and ends at this owner's own key; the
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
@@ -833,7 +911,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       const uint64_t scc = scores[cur];
       const float* rowc = values + static_cast<uint64_t>(cur) * t.dim;
       if (in_regs) row_regs_load(rr, rowc, t.dim, lane);
-      bucket_apply<V4>(o, t, kc, scc, rr, rowc, in_regs, false, lane);
+      bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, ev, lane);
       cur = after;
     }
     if (DUAL && o.occ >= kSlots) {
@@ -862,17 +940,22 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
 }
 
 // Serial inserter: one 16-lane group applies the whole batch in input order
-// (Algorithm 2, or Algorithm 3 in dual mode, one key at a time).
+// (Algorithm 2, or Algorithm 3 in dual mode, one key at a time). With `skip`
+// (the marks of a probe pass that already updated the resident keys), only
+// the keys marked kNoIdx are applied. ev.keys != nullptr: evicted and
+// turned-away entries are handed back.
 template <bool V4, bool DUAL>
 __global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t n,
                                                            const uint64_t* __restrict__ keys,
                                                            const float* __restrict__ values,
-                                                           const uint64_t* __restrict__ scores) {
+                                                           const uint64_t* __restrict__ scores,
+                                                           const uint32_t* __restrict__ skip, Evicted ev) {
   if (threadIdx.x >= kInsG) return;
   const int lane = static_cast<int>(threadIdx.x);
   for (uint64_t i = 0; i < n; ++i) {
     const uint64_t k = keys[i];
     if (is_reserved(k)) continue;
+    if (skip && skip[i] != kNoIdx) continue;
     const float* row = values + i * t.dim;
     const uint64_t score = scores[i];
     const uint64_t h = fmix64(k);
@@ -884,7 +967,7 @@ __global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t
     own_load(o1, t, b1, lane);
     if (!DUAL || b2 == b1) {
       const uint32_t occ0 = o1.occ;
-      own_upsert<V4>(o1, t, k, row, score, lane);
+      own_upsert<V4>(o1, t, k, row, score, ev, lane);
       if (o1.occ != occ0) own_store_occ(o1, t, lane);
       continue;
     }
@@ -920,8 +1003,13 @@ __global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t
     const uint64_t ms = second ? ms2 : ms1, mk = second ? mk2 : mk1;
     const int vs = second ? v2 : v1;
     if (score > ms || (score == ms && k > mk)) {
+      if (ev.keys)
+        emit_entry<V4>(ev, t, mk, ms, t.values + (static_cast<uint64_t>(o.b) * kSlots + vs) * t.dim, nullptr,
+                       lane);
       own_write_slot(o, t, vs, k, d, score, lane);
       own_write_row<V4>(o, t, vs, row, lane);
+    } else if (ev.keys) {
+      emit_entry<V4>(ev, t, k, score, row, nullptr, lane);
     }
   }
 }
@@ -984,16 +1072,26 @@ hipError_t assign_g(const TableView& t, uint64_t n, const uint64_t* keys, const 
   return hipGetLastError();
 }
 
-template <int G, bool V4, bool DUAL>
-hipError_t insert_g(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
-                    const uint64_t* scores, uint32_t* next, uint32_t* target, hipStream_t s,
-                    KernelTimer* tm) {
-  HKV_LAUNCH(tm, "upsert_probe", (upsert_probe_kernel<G, V4, DUAL, true>), dim3(grid_for(n * G)),
-             dim3(kBlock), s, t, n, keys, values, scores, next, target);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL>), dim3(grid_for(n)), dim3(kBlock), s, t, n,
-             keys, values, scores, next, target);
+template <int G, bool V4, bool DUAL, bool FETCH>
+hipError_t probe_g(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next, uint32_t* target,
+                   bool link, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, FETCH ? "probe_fetch" : "upsert_probe", (upsert_probe_kernel<G, V4, DUAL, true, FETCH>),
+             dim3(grid_for(n * G)), dim3(kBlock), s, t, n, c.keys, c.values, c.scores, c.found, next, target,
+             link);
+  return hipGetLastError();
+}
+
+template <bool V4, bool DUAL>
+hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const uint32_t* next,
+                   const uint32_t* target, hipStream_t s, KernelTimer* tm) {
+  const Evicted ev{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
+  if (c.ev_keys) {
+    HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true>), dim3(grid_for(n)), dim3(kBlock), s,
+               t, n, c.keys, c.values, c.scores, next, target, ev);
+  } else {
+    HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false>), dim3(grid_for(n)), dim3(kBlock), s,
+               t, n, c.keys, c.values, c.scores, next, target, ev);
+  }
   return hipGetLastError();
 }
 
@@ -1017,24 +1115,55 @@ hipError_t assign_d(const TableView& t, uint64_t n, const uint64_t* keys, const 
   }
 }
 
-template <bool V4, bool DUAL>
-hipError_t insert_d(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
-                    const uint64_t* scores, uint32_t* next, uint32_t* target, bool serial,
-                    hipStream_t s, KernelTimer* tm) {
-  if (serial) {
-    HKV_LAUNCH(tm, "upsert_serial", (upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), s, t, n, keys,
-               values, scores);
-    return hipGetLastError();
-  }
+template <bool V4, bool DUAL, bool FETCH>
+hipError_t probe_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next, uint32_t* target,
+                   bool link, hipStream_t s, KernelTimer* tm) {
   if constexpr (DUAL) {
-    return insert_g<kInsG, V4, true>(t, n, keys, values, scores, next, target, s, tm);
+    return probe_g<kInsG, V4, true, FETCH>(t, n, c, next, target, link, s, tm);
   } else {
     switch (lanes_for(t)) {
-      case 4: return insert_g<4, V4, false>(t, n, keys, values, scores, next, target, s, tm);
-      case 8: return insert_g<8, V4, false>(t, n, keys, values, scores, next, target, s, tm);
-      default: return insert_g<16, V4, false>(t, n, keys, values, scores, next, target, s, tm);
+      case 4: return probe_g<4, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
+      case 8: return probe_g<8, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
+      default: return probe_g<16, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
     }
   }
+}
+
+// Parallel: the probe kernel (updates of resident keys, chains of the
+// others), then the owner kernel. Serial: insert_or_assign runs the serial
+// kernel alone in input order; find_or_insert and insert_and_evict first run
+// the probe kernel without chains (updates / stored rows of resident keys,
+// marks of the others), then the serial kernel over the marked keys.
+template <bool V4, bool DUAL>
+hipError_t upsert_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next, uint32_t* target,
+                    bool serial, hipStream_t s, KernelTimer* tm) {
+  hipError_t e = hipSuccess;
+  if (c.ev_count) {
+    HKV_LAUNCH(tm, "zero", zero_u64_kernel, dim3(1), dim3(1), s, c.ev_count);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (n == 0) return hipSuccess;
+  const bool two_phase = c.fetch || c.ev_keys;
+  if (!serial || two_phase) {
+    e = c.fetch ? probe_d<V4, DUAL, true>(t, n, c, next, target, !serial, s, tm)
+                : probe_d<V4, DUAL, false>(t, n, c, next, target, !serial, s, tm);
+    if (e != hipSuccess) return e;
+  }
+  if (serial) {
+    const Evicted ev{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
+    HKV_LAUNCH(tm, "upsert_serial", (upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), s, t, n, c.keys,
+               c.values, c.scores, two_phase ? next : nullptr, ev);
+    return hipGetLastError();
+  }
+  return owner_l<V4, DUAL>(t, n, c, next, target, s, tm);
+}
+
+template <int G, bool DUAL>
+hipError_t locate_g(const TableView& t, uint64_t n, const uint64_t* keys, uint64_t* ptrs, uint8_t* found,
+                    uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  HKV_LAUNCH(tm, ptrs ? "find_ptr" : "contains", (locate_kernel<G, DUAL>), dim3(grid_for(n * G)), dim3(kBlock),
+             s, t, n, keys, ptrs, found, sc);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1066,14 +1195,26 @@ hipError_t launch_assign(const TableView& t, uint64_t n, const uint64_t* keys, c
               : assign_d<false, false>(t, n, keys, values, scores, s, tm);
 }
 
-hipError_t launch_insert(const TableView& t, uint64_t n, const uint64_t* keys, const float* values,
-                         const uint64_t* scores, uint32_t* next, uint32_t* target, bool vec4,
-                         bool serial, hipStream_t s, KernelTimer* tm) {
+hipError_t launch_upsert(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next,
+                         uint32_t* target, bool vec4, bool serial, hipStream_t s, KernelTimer* tm) {
   if (t.dual)
-    return vec4 ? insert_d<true, true>(t, n, keys, values, scores, next, target, serial, s, tm)
-                : insert_d<false, true>(t, n, keys, values, scores, next, target, serial, s, tm);
-  return vec4 ? insert_d<true, false>(t, n, keys, values, scores, next, target, serial, s, tm)
-              : insert_d<false, false>(t, n, keys, values, scores, next, target, serial, s, tm);
+    return vec4 ? upsert_d<true, true>(t, n, c, next, target, serial, s, tm)
+                : upsert_d<false, true>(t, n, c, next, target, serial, s, tm);
+  return vec4 ? upsert_d<true, false>(t, n, c, next, target, serial, s, tm)
+              : upsert_d<false, false>(t, n, c, next, target, serial, s, tm);
+}
+
+// Key-side probes need no row copy, so the group size does not follow dim:
+// 8 lanes (one 16-byte digest load each) unless overridden.
+hipError_t launch_locate(const TableView& t, uint64_t n, const uint64_t* keys, uint64_t* ptrs_out,
+                         uint8_t* found_out, uint64_t* scores_out, hipStream_t s, KernelTimer* tm) {
+  const int g = (t.lanes == 4 || t.lanes == 16) ? static_cast<int>(t.lanes) : 8;
+  if (t.dual) return locate_g<kInsG, true>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+  switch (g) {
+    case 4: return locate_g<4, false>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+    case 16: return locate_g<16, false>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+    default: return locate_g<8, false>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+  }
 }
 
 hipError_t launch_size(const TableView& t, unsigned long long* dev_out, hipStream_t s, KernelTimer* tm) {

@@ -259,6 +259,36 @@ hkv_status ensure_workspace(hkv_table* t, uint64_t n) {
 
 }  // namespace
 
+// Shared tail of the inserter calls (arguments already validated): workspace,
+// ordering after incompatible groups, launch, completion event.
+static hkv_status run_inserter(hkv_table* t, uint64_t n, const hkv::InsertCall& c, bool vec4, const char* what,
+                               hipStream_t stream) {
+  const bool serial = (t->opt.flags & HKV_FLAG_SERIAL_INSERT) != 0;
+  const bool needs_ws = !serial || c.fetch || c.ev_keys;
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  hkv_status st;
+  if (needs_ws && (st = ensure_workspace(t, n)) != HKV_OK) return st;
+  if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
+  const hipError_t e = hkv::launch_upsert(t->view, n, c, t->ws_next, t->ws_target, vec4, serial, stream, t->timer());
+  if (e != hipSuccess) return fail_hip(e, what);
+  return record_after(t, kInserter, stream);
+}
+
+// Shared tail of find_ptr and contains.
+static hkv_status run_locate(hkv_table* t, uint64_t n, const uint64_t* keys, uint64_t* ptrs, uint8_t* found,
+                             uint64_t* scores, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  hkv_status st;
+  if ((st = order_before(t, kReader, stream)) != HKV_OK) return st;
+  const hipError_t e = hkv::launch_locate(t->view, n, keys, ptrs, found, scores, stream, t->timer());
+  if (e != hipSuccess) return fail_hip(e, ptrs ? "find_ptr launch" : "contains launch");
+  return record_after(t, kReader, stream);
+}
+
 HKV_API const char* hkv_last_error(void) { return g_error.c_str(); }
 
 HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
@@ -373,6 +403,31 @@ HKV_API hkv_status hkv_find(hkv_table* t, uint64_t n, const uint64_t* keys, floa
   return record_after(t, kReader, stream);
 }
 
+HKV_API hkv_status hkv_find_ptr(hkv_table* t, uint64_t n, const uint64_t* keys, float** values_ptr_out,
+                                uint8_t* found_out, uint64_t* scores_out, hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values_ptr_out, n * sizeof(float*), "values_ptr_out")) != HKV_OK) return st;
+  if (found_out && (st = check_buffer(t, found_out, n, "found_out")) != HKV_OK) return st;
+  if (scores_out && (st = check_buffer(t, scores_out, n * 8, "scores_out")) != HKV_OK) return st;
+  static_assert(sizeof(float*) == sizeof(uint64_t), "64-bit addresses");
+  return run_locate(t, n, keys, reinterpret_cast<uint64_t*>(values_ptr_out), found_out, scores_out, stream);
+}
+
+HKV_API hkv_status hkv_contains(hkv_table* t, uint64_t n, const uint64_t* keys, uint8_t* found_out,
+                                hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, found_out, n, "found_out")) != HKV_OK) return st;
+  return run_locate(t, n, keys, nullptr, found_out, nullptr, stream);
+}
+
 HKV_API hkv_status hkv_insert_or_assign(hkv_table* t, uint64_t n, const uint64_t* keys,
                                         const float* values, const uint64_t* scores,
                                         hipStream_t stream) {
@@ -385,17 +440,66 @@ HKV_API hkv_status hkv_insert_or_assign(hkv_table* t, uint64_t n, const uint64_t
   if ((st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
   if ((st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
   const bool vec4 = dim % 4 == 0 && aligned16(values);
-  const bool serial = (t->opt.flags & HKV_FLAG_SERIAL_INSERT) != 0;
-  std::lock_guard<std::mutex> lk(t->mu);
-  DeviceGuard dg(t->opt.device);
-  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
-  if (!serial && (st = ensure_workspace(t, n)) != HKV_OK) return st;
-  if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
-  const hipError_t e =
-      hkv::launch_insert(t->view, n, keys, values, scores, t->ws_next, t->ws_target, vec4, serial, stream,
-                         t->timer());
-  if (e != hipSuccess) return fail_hip(e, "insert_or_assign launch");
-  return record_after(t, kInserter, stream);
+  hkv::InsertCall c{};
+  c.keys = keys;
+  c.values = const_cast<float*>(values);  // read only: fetch and eviction output are off
+  c.scores = scores;
+  return run_inserter(t, n, c, vec4, "insert_or_assign", stream);
+}
+
+HKV_API hkv_status hkv_insert_and_evict(hkv_table* t, uint64_t n, const uint64_t* keys, const float* values,
+                                        const uint64_t* scores, uint64_t* evicted_keys, float* evicted_values,
+                                        uint64_t* evicted_scores, uint64_t* evicted_count,
+                                        hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, evicted_count, 8, "evicted_count")) != HKV_OK) return st;
+  if (n == 0) {
+    // only the count is written (zero), in inserter order like any other call
+    hkv::InsertCall c{};
+    c.ev_keys = evicted_keys;
+    c.ev_count = reinterpret_cast<unsigned long long*>(evicted_count);
+    return run_inserter(t, 0, c, false, "insert_and_evict", stream);
+  }
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
+  if ((st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
+  if ((st = check_buffer(t, evicted_keys, n * 8, "evicted_keys")) != HKV_OK) return st;
+  if (evicted_values && (st = check_buffer(t, evicted_values, n * dim * 4, "evicted_values")) != HKV_OK) return st;
+  if (evicted_scores && (st = check_buffer(t, evicted_scores, n * 8, "evicted_scores")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && aligned16(values) && (!evicted_values || aligned16(evicted_values));
+  hkv::InsertCall c{};
+  c.keys = keys;
+  c.values = const_cast<float*>(values);  // read only: fetch is off
+  c.scores = scores;
+  c.ev_keys = evicted_keys;
+  c.ev_values = evicted_values;
+  c.ev_scores = evicted_scores;
+  c.ev_count = reinterpret_cast<unsigned long long*>(evicted_count);
+  return run_inserter(t, n, c, vec4, "insert_and_evict", stream);
+}
+
+HKV_API hkv_status hkv_find_or_insert(hkv_table* t, uint64_t n, const uint64_t* keys, float* values,
+                                      const uint64_t* scores, uint8_t* found_out, hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > kMaxBatch) return fail(HKV_EINVAL, "batch of %llu keys exceeds the limit", static_cast<unsigned long long>(n));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
+  if ((st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
+  if (found_out && (st = check_buffer(t, found_out, n, "found_out")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && aligned16(values);
+  hkv::InsertCall c{};
+  c.keys = keys;
+  c.values = values;
+  c.scores = scores;
+  c.fetch = true;
+  c.found = found_out;
+  return run_inserter(t, n, c, vec4, "find_or_insert", stream);
 }
 
 HKV_API hkv_status hkv_assign(hkv_table* t, uint64_t n, const uint64_t* keys, const float* values,

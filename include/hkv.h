@@ -9,9 +9,12 @@
  *   - §3.3, Algorithm 2: a full bucket resolves an upsert in place by evicting
  *     its lowest-score entry or by refusing admission to the incoming key.
  *   - §3.4, Algorithm 3: optional score-based dual-bucket selection.
- *   - §3.5, Table 4: readers (find, size, export), updaters (assign) and
- *     inserters (insert_or_assign); readers may overlap readers and updaters
- *     may overlap updaters, every other pair is exclusive.
+ *   - §3.5, Table 4: readers (find, find*, contains, size, export), updaters
+ *     (assign) and inserters (insert_or_assign, insert_and_evict,
+ *     find_or_insert); readers may overlap readers and updaters may overlap
+ *     updaters, every other pair is exclusive.
+ *   - §4.1: the cache-specific calls find* (pointer-returning find),
+ *     contains, insert_and_evict and find_or_insert.
  *   - §3.6 and §4.2: optional placement of value rows in pinned host memory
  *     mapped into the GPU address space, keys/digests/scores staying in HBM.
  *
@@ -34,8 +37,8 @@
  *   - Arguments are validated synchronously; on any error nothing is enqueued,
  *     the call returns a negative status and hkv_last_error() describes it.
  *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 3 keys.
- *   - The reserved keys HKV_EMPTY_KEY and HKV_LOCKED_KEY always miss in find
- *     and are skipped by insert_or_assign and assign.
+ *   - The reserved keys HKV_EMPTY_KEY and HKV_LOCKED_KEY always miss in the
+ *     readers and are skipped by the updaters and inserters.
  *   - No C++ exception crosses this boundary.
  */
 #ifndef HKV_H_
@@ -148,6 +151,75 @@ hkv_status hkv_assign(hkv_table* table, uint64_t n, const uint64_t* keys, const 
                       const uint64_t* scores, hipStream_t stream);
 
 /*
+ * hkv_find_ptr - reader, the pointer-returning find* of §4.1 (measured in
+ * §5.3). For each i < n: if keys[i] is resident, values_ptr_out[i] = the
+ * address of its value row (device memory, or the GPU-mapped address of the
+ * host row when values live in host memory; rows are addressed by position,
+ * §3.6), found_out[i] = 1 and scores_out[i] = its score; otherwise
+ * values_ptr_out[i] = NULL, found_out[i] = 0 and scores_out[i] is untouched.
+ * A returned address stays the key's row until the next inserter call on the
+ * table (which may evict the key and reuse the slot); updaters change the
+ * row's contents in place.
+ *   keys           [n] uint64, input
+ *   values_ptr_out [n] float*, output
+ *   found_out      [n] uint8, output, nullable
+ *   scores_out     [n] uint64, output, nullable
+ */
+hkv_status hkv_find_ptr(hkv_table* table, uint64_t n, const uint64_t* keys, float** values_ptr_out,
+                        uint8_t* found_out, uint64_t* scores_out, hipStream_t stream);
+
+/*
+ * hkv_contains - reader (§3.5, §4.1): found_out[i] = 1 iff keys[i] is
+ * resident, else 0. Nothing else is read or written.
+ *   keys      [n] uint64, input
+ *   found_out [n] uint8, output
+ */
+hkv_status hkv_contains(hkv_table* table, uint64_t n, const uint64_t* keys, uint8_t* found_out,
+                        hipStream_t stream);
+
+/*
+ * hkv_insert_and_evict - inserter (§4.1): insert_or_assign that also hands
+ * back what leaves. Order inside the call: keys resident when the call starts
+ * are updated first (row and score), then the other keys are inserted as by
+ * insert_or_assign. Handed back, compacted in unspecified order: every
+ * resident entry an insertion evicts (with the key, row and score it held) and
+ * every offered entry that admission turns away (with the offered row and
+ * score). So the output is exactly the entries that were resident before the
+ * call or offered by it and are not resident after it. *evicted_count (a
+ * device-accessible uint64, reset by the call itself) receives how many; it is
+ * at most the number of keys not resident at the start, so outputs of n
+ * entries always suffice. Same distinct-key and determinism rules as
+ * insert_or_assign.
+ *   keys             [n] uint64, input
+ *   values           [n*dim] float32, input
+ *   scores           [n] uint64, input, required
+ *   evicted_keys     [n] uint64, output
+ *   evicted_values   [n*dim] float32, output, nullable
+ *   evicted_scores   [n] uint64, output, nullable
+ *   evicted_count    [1] uint64, output
+ * Uses the same table-owned workspace as insert_or_assign.
+ */
+hkv_status hkv_insert_and_evict(hkv_table* table, uint64_t n, const uint64_t* keys, const float* values,
+                                const uint64_t* scores, uint64_t* evicted_keys, float* evicted_values,
+                                uint64_t* evicted_scores, uint64_t* evicted_count, hipStream_t stream);
+
+/*
+ * hkv_find_or_insert - inserter (§3.5, §4.1): lookup combined with insertion
+ * for cold starts. A key resident when the call starts is a hit: its stored
+ * row is written to values[i*dim ..), its score is replaced by scores[i] and
+ * found_out[i] = 1. Every other key is inserted with the caller's row and
+ * score exactly as insert_or_assign inserts it (it may evict, or be turned
+ * away); found_out[i] = 0 and its row in values is left as it was.
+ *   keys      [n] uint64, input
+ *   values    [n*dim] float32, input and output
+ *   scores    [n] uint64, input, required
+ *   found_out [n] uint8, output, nullable
+ * Uses the same table-owned workspace as insert_or_assign.
+ */
+hkv_status hkv_find_or_insert(hkv_table* table, uint64_t n, const uint64_t* keys, float* values,
+                              const uint64_t* scores, uint8_t* found_out, hipStream_t stream);
+
+/*
  * hkv_size - reader (§3.5): number of resident entries. Enqueues the count on
  * `stream`, synchronizes that stream, and stores the result in *out_host.
  */
@@ -173,7 +245,8 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
  * the elapsed time between them.
  */
 typedef struct hkv_kernel_stat {
-  char name[32];      /* find, assign, upsert_probe, upsert_owner, upsert_serial, size, export, zero */
+  char name[32];      /* find, find_ptr, contains, assign, upsert_probe, probe_fetch, upsert_owner,
+                         owner_evict, upsert_serial, size, export, zero */
   uint64_t launches;  /* timed launches of that kernel */
   double total_ms;    /* sum of their times */
   double max_ms;      /* longest one */

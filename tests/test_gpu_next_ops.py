@@ -1,0 +1,334 @@
+"""Parity of find*, contains, insert_and_evict and find_or_insert (the
+cache-specific calls of the paper's §4.1) with the CPU oracle, through the C ABI.
+
+Bar: found flags, scores and rows bit-exact; find* addresses equal to one
+value base plus the slot position times the row size, with the positions of
+export (and, in serial mode, of the oracle); insert_and_evict's hand-back
+equal to the oracle's as a set of (key, score, row) in single-bucket mode and
+in identical order in serial mode; table contents equal after every call.
+Dual-bucket parallel mode: the hand-back and the table together hold exactly
+what was resident or offered, nothing twice.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import hkv_inputs as gen
+import oracle
+from conftest import gpu_available
+from helpers import SLOTS
+from test_gpu_parity import (NAN_BITS, SENTINEL_SCORE, assert_same_contents, dev, hkv, mixed_queries, np_u64,
+                             sample_present, to_dev)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def fill(tab, o, C, D, seed, stream, lam=1.0, batch=1 << 12):
+    step, start = 0, 0
+    target = int(round(lam * C))
+    while o.size() < target:
+        step += 1
+        n = batch if lam >= 1.0 else min(batch, target - o.size())
+        keys = gen.unique_keys(seed, stream, start, n, device=dev())
+        start += n
+        vals = gen.values(keys, step, D)
+        sc = torch.full((n,), step, dtype=torch.int64, device=dev())
+        tab.insert_or_assign(keys, vals, sc)
+        o.insert_or_assign(np_u64(keys), np_u64(sc), values=vals.cpu().numpy())
+    return step, start
+
+
+def check_find_ptr(tab, o, q):
+    n = q.numel()
+    ptrs = torch.full((n,), -1, dtype=torch.int64, device=dev())
+    found = torch.full((n,), 7, dtype=torch.uint8, device=dev())
+    scores = torch.full((n,), SENTINEL_SCORE, dtype=torch.int64, device=dev())
+    tab.find_ptr(q, ptrs_out=ptrs, found_out=found, scores_out=scores)
+    contains = tab.contains(q)
+    torch.cuda.synchronize()
+    qk = np_u64(q)
+    ofound, opos = o.find_pos(qk)
+    osc = np.full(n, SENTINEL_SCORE, np.uint64)
+    o.find(qk, scores_out=osc)
+    f = found.cpu().numpy()
+    assert np.array_equal(f, ofound)
+    assert np.array_equal(contains.cpu().numpy(), ofound)
+    assert np.array_equal(np_u64(scores), osc)
+    p = ptrs.cpu().numpy().view(np.uint64)
+    assert np.all(p[f == 0] == 0)
+    # every hit's address is one common base plus its slot position in rows,
+    # the position being where export lists the key
+    k, _, _, pos = tab.export_batch(with_values=False)
+    where = dict(zip(np_u64(k).tolist(), np_u64(pos).tolist()))
+    hit = np.flatnonzero(f)
+    gpos = np.array([where[int(x)] for x in qk[hit]], dtype=np.uint64)
+    row = np.uint64(4 * tab.dim)
+    base = p[hit] - gpos * row
+    assert hit.size == 0 or np.all(base == base[0])
+    return p, hit, gpos, opos
+
+
+def test_find_ptr_and_contains_single_bucket():
+    """The small single-bucket workload's table (512 buckets x 128, dim 16) at
+    lambda = 1: find* and contains on half resident, half absent keys plus
+    reserved keys."""
+    H = hkv()
+    C, D = 1 << 16, 16
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    fill(tab, o, C, D, 0x484B560000000001, 1, batch=16384)
+    q = mixed_queries(o, 16384, 0.5, 3, 55)
+    q = torch.cat([q, to_dev(np.array([oracle.EMPTY_KEY, oracle.LOCKED_KEY], dtype=np.uint64))])
+    _, hit, _, _ = check_find_ptr(tab, o, q)
+    assert hit.size == 8192
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_find_ptr_serial_positions_equal_oracle(dual):
+    """Serial inserts place keys in the oracle's slots, so find* addresses give
+    exactly the oracle's positions; dual-bucket rows lie in a candidate bucket."""
+    H = hkv()
+    C, D = 16 * SLOTS, 5
+    tab = H.HashTable(C, D, dual_bucket=dual, serial_insert=True)
+    o = oracle.OracleTable(C, D, dual=dual)
+    fill(tab, o, C, D, 9, 2, batch=700)
+    q = mixed_queries(o, 3000, 0.7, 4, 56)
+    p, hit, gpos, opos = check_find_ptr(tab, o, q)
+    assert np.array_equal(gpos, opos[hit])
+    if dual:
+        b1, b2, _ = o.route(np_u64(q)[hit])
+        assert np.all((gpos // SLOTS == b1) | (gpos // SLOTS == b2))
+
+
+def test_find_ptr_parallel_dual_and_tiered():
+    H = hkv()
+    C, D = 64 * SLOTS, 8
+    for host in (False, True):
+        tab = H.HashTable(C, D, dual_bucket=True, values_on_host=host)
+        o = oracle.OracleTable(C, D, dual=True)
+        keys = gen.unique_keys(12, 1, 0, C, device=dev())
+        vals = gen.values(keys, 1, D)
+        sc = torch.ones(C, dtype=torch.int64, device=dev())
+        tab.insert_or_assign(keys, vals, sc)
+        k, _, _, pos = tab.export_batch(with_values=False)
+        q = torch.cat([k[:4000], gen.unique_keys(12, 2, 0, 1000, device=dev())])
+        ptrs, found = tab.find_ptr(q)
+        torch.cuda.synchronize()
+        f = found.cpu().numpy()
+        assert f[:4000].all() and not f[4000:].any()
+        p = ptrs.cpu().numpy().view(np.uint64)
+        assert np.all(p[4000:] == 0)
+        base = p[:4000] - np_u64(pos[:4000]) * np.uint64(4 * D)
+        assert np.all(base == base[0])
+        tab.close()
+
+
+def evict_sets(ek, ev, es, cnt):
+    torch.cuda.synchronize()
+    m = int(cnt.item())
+    k = np_u64(ek[:m])
+    order = np.argsort(k)
+    return k[order], np_u64(es[:m])[order], ev[:m].cpu().numpy()[order]
+
+
+def oracle_evict_sets(out):
+    order = np.argsort(out["keys"])
+    return out["keys"][order], out["scores"][order], out["values"][order]
+
+
+def test_insert_and_evict_single_bucket_exact():
+    """lambda = 1 table (2^14 slots, dim 8). Batches of half resident, half new
+    keys with rising scores (evictions), then a low-score burst (everything
+    turned away, table unchanged) and a high-score burst (admitted whole)."""
+    H = hkv()
+    C, D = 1 << 14, 8
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    step, _ = fill(tab, o, C, D, 21, 1)
+    for t in range(5):
+        step += 1
+        fresh = gen.unique_keys(21, 2, t * 2048, 2048).numpy().view(np.uint64)
+        old = sample_present(o, 2048, 50 + t)
+        k = np.random.default_rng(t).permutation(np.concatenate([fresh, old]))
+        kt = to_dev(k)
+        v = gen.values(kt, 100 + step, D)
+        sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+        got = evict_sets(*tab.insert_and_evict(kt, v, sc))
+        want = oracle_evict_sets(o.insert_and_evict(k, np_u64(sc), values=v.cpu().numpy()))
+        assert want[0].size > 0
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+        assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        assert_same_contents(tab, o)
+    for burst_score, stream in ((0, 3), (10 ** 6, 4)):
+        k = gen.unique_keys(21, stream, 0, 1024, device=dev())
+        v = gen.values(k, 7, D)
+        sc = torch.full((1024,), burst_score, dtype=torch.int64, device=dev())
+        got = evict_sets(*tab.insert_and_evict(k, v, sc))
+        want = oracle_evict_sets(o.insert_and_evict(np_u64(k), np_u64(sc), values=v.cpu().numpy()))
+        assert got[0].size == 1024
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+        assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        if burst_score == 0:
+            assert np.array_equal(got[0], np.sort(np_u64(k)))
+        assert_same_contents(tab, o)
+
+
+def test_insert_and_evict_without_optional_outputs_and_empty():
+    H = hkv()
+    C, D = 8 * SLOTS, 4
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    fill(tab, o, C, D, 22, 1, batch=512)
+    k = gen.unique_keys(22, 2, 0, 600, device=dev())
+    v = gen.values(k, 3, D)
+    sc = torch.full((600,), 99, dtype=torch.int64, device=dev())
+    ek = torch.empty(600, dtype=torch.int64, device=dev())
+    cnt = torch.full((1,), 12345, dtype=torch.int64, device=dev())
+    hkv().hkv_insert_and_evict(tab.handle, k, v, sc, ek, None, None, cnt, dim=D, device=0)
+    want = o.insert_and_evict(np_u64(k), np_u64(sc), values=v.cpu().numpy())
+    torch.cuda.synchronize()
+    m = int(cnt.item())
+    assert np.array_equal(np.sort(np_u64(ek[:m])), np.sort(want["keys"]))
+    # an empty batch only resets the count
+    cnt.fill_(777)
+    empty = torch.empty(0, dtype=torch.int64, device=dev())
+    hkv().hkv_insert_and_evict(tab.handle, empty, torch.empty((0, D), device=dev()), empty, ek, None, None, cnt,
+                               dim=D, device=0)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0
+    assert_same_contents(tab, o)
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_insert_and_evict_serial_same_order_and_positions(dual):
+    H = hkv()
+    C, D = 16 * SLOTS, 3
+    tab = H.HashTable(C, D, dual_bucket=dual, serial_insert=True)
+    o = oracle.OracleTable(C, D, dual=dual)
+    rng = np.random.default_rng(23)
+    pool = rng.integers(1, 1 << 62, size=6000, dtype=np.int64)
+    for step in range(1, 12):
+        k = rng.permutation(np.unique(rng.choice(pool, 700, replace=False)))
+        kt = torch.from_numpy(k).to(dev())
+        sc = torch.from_numpy(step * 4 + rng.integers(0, 4, size=k.size)).to(dev())
+        v = gen.values(kt, step, D)
+        ek, ev, es, cnt = tab.insert_and_evict(kt, v, sc)
+        want = o.insert_and_evict(k.view(np.uint64), np_u64(sc), values=v.cpu().numpy())
+        torch.cuda.synchronize()
+        m = int(cnt.item())
+        assert np.array_equal(np_u64(ek[:m]), want["keys"])
+        assert np.array_equal(np_u64(es[:m]), want["scores"])
+        assert np.array_equal(ev[:m].cpu().numpy().view(np.uint32), want["values"].view(np.uint32))
+        gk, _, _, gp = tab.export_batch(with_values=False)
+        e = o.export()
+        order = np.argsort(np_u64(gp))
+        assert np.array_equal(np_u64(gp)[order], e["pos"]) and np.array_equal(np_u64(gk)[order], e["keys"])
+    assert_same_contents(tab, o)
+
+
+def test_insert_and_evict_dual_parallel_conserves_entries():
+    """Dual-bucket parallel mode under a Zipf stream with frequency scores:
+    hand-back and table together hold exactly what was resident or offered,
+    nothing twice, every handed-back row is that key's last written row."""
+    H = hkv()
+    C, D = 1 << 14, 4
+    tab = H.HashTable(C, D, dual_bucket=True)
+    z = gen.Zipf(1.05, 1 << 18)
+    freq = {}
+    resident = set()
+    for b in range(16):
+        r = z.draw(78, 1, b * 4096, 4096).numpy()
+        uniq, cnt_ = np.unique(r, return_counts=True)
+        for x, c in zip(uniq.tolist(), cnt_.tolist()):
+            freq[x] = freq.get(x, 0) + c
+        keys = uniq.astype(np.uint64)
+        sc = np.array([freq[x] for x in uniq.tolist()], dtype=np.uint64)
+        kt, st = to_dev(keys), to_dev(sc)
+        v = gen.values(kt, st, D)
+        ek, ev, es, cnt = tab.insert_and_evict(kt, v, st)
+        torch.cuda.synchronize()
+        m = int(cnt.item())
+        out = np_u64(ek[:m])
+        gk, _, _, _ = tab.export_batch(with_values=False)
+        after = set(np_u64(gk).tolist())
+        assert np.unique(out).size == m
+        assert not (set(out.tolist()) & after)
+        assert set(out.tolist()) | after == resident | set(keys.tolist())
+        assert m <= len(set(keys.tolist()) - resident)
+        assert all(freq[x] == s for x, s in zip(out.tolist(), np_u64(es[:m]).tolist()))
+        assert torch.equal(ev[:m], gen.values(ek[:m], es[:m], D))
+        resident = after
+
+
+def test_find_or_insert_single_bucket_exact():
+    """lambda = 1 table (2^14 slots, dim 8): batches of half resident, half new
+    keys; found flags, returned rows (stored rows of hits, untouched rows of
+    misses) and table contents exact."""
+    H = hkv()
+    C, D = 1 << 14, 8
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    step, _ = fill(tab, o, C, D, 24, 1)
+    for t in range(5):
+        step += 1
+        fresh = gen.unique_keys(24, 2, t * 2048, 2048).numpy().view(np.uint64)
+        old = sample_present(o, 2048, 60 + t)
+        k = np.random.default_rng(t).permutation(np.concatenate([fresh, old]))
+        kt = to_dev(k)
+        v = gen.values(kt, 100 + step, D)
+        v0 = v.cpu().numpy()
+        sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+        rows, found = tab.find_or_insert(kt, v, sc)
+        orows, ofound = o.find_or_insert(k, np_u64(sc), values=v0)
+        torch.cuda.synchronize()
+        assert np.array_equal(found.cpu().numpy(), ofound)
+        assert ofound.sum() == 2048
+        assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        assert_same_contents(tab, o)
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_find_or_insert_serial_positions(dual):
+    H = hkv()
+    C, D = 16 * SLOTS, 4
+    tab = H.HashTable(C, D, dual_bucket=dual, serial_insert=True)
+    o = oracle.OracleTable(C, D, dual=dual)
+    rng = np.random.default_rng(25)
+    pool = rng.integers(1, 1 << 62, size=5000, dtype=np.int64)
+    for step in range(1, 10):
+        k = rng.permutation(np.unique(rng.choice(pool, 600, replace=False)))
+        kt = torch.from_numpy(k).to(dev())
+        sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+        v = gen.values(kt, step, D)
+        v0 = v.cpu().numpy()
+        rows, found = tab.find_or_insert(kt, v, sc)
+        orows, ofound = o.find_or_insert(k.view(np.uint64), np_u64(sc), values=v0)
+        torch.cuda.synchronize()
+        assert np.array_equal(found.cpu().numpy(), ofound)
+        assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        gk, _, _, gp = tab.export_batch(with_values=False)
+        e = o.export()
+        order = np.argsort(np_u64(gp))
+        assert np.array_equal(np_u64(gp)[order], e["pos"]) and np.array_equal(np_u64(gk)[order], e["keys"])
+    assert_same_contents(tab, o)
+
+
+def test_find_or_insert_odd_dim_and_reserved_keys():
+    H = hkv()
+    C, D = 8 * SLOTS, 3
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    fill(tab, o, C, D, 26, 1, batch=500)
+    k = np.concatenate([sample_present(o, 300, 1), gen.unique_keys(26, 2, 0, 300).numpy().view(np.uint64),
+                        np.array([oracle.EMPTY_KEY, oracle.LOCKED_KEY], dtype=np.uint64)])
+    kt = to_dev(k)
+    v = gen.values(kt, 50, D)
+    v0 = v.cpu().numpy()
+    sc = torch.full((k.size,), 50, dtype=torch.int64, device=dev())
+    rows, found = tab.find_or_insert(kt, v, sc)
+    orows, ofound = o.find_or_insert(k, np_u64(sc), values=v0)
+    torch.cuda.synchronize()
+    assert np.array_equal(found.cpu().numpy(), ofound)
+    assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+    assert_same_contents(tab, o)
