@@ -64,6 +64,8 @@ def parse_args():
     p.add_argument("--insert-steps", type=int, default=5,
                    help="extra all-new-key insert batches on the full table, reported in detail")
     p.add_argument("--find-only", action="store_true", help="time find batches only")
+    p.add_argument("--no-extra-ops", dest="extra_ops", action="store_false",
+                   help="skip the find*/contains/insert_and_evict/find_or_insert measurements")
     p.add_argument("--capacity-sweep", default="", metavar="LOG2S",
                    help="only measure find on full tables of these capacities (e.g. 24,26,28) and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -109,6 +111,33 @@ def probe_bytes_per_key(dim: int, f: float) -> float:
 
 def owner_bytes_per_key(dim: int, f: float, e: float) -> float:
     return 4 + (1 - f) * (8 + 8 + 4 * dim + 4 + 4 + 128 + 4 + 8 + 1 + 8 + 4 * dim + e * (1024 + 8))
+
+
+def locate_bytes_per_key(h: float, with_ptr: bool) -> float:
+    """find* / contains: 8 key + 128 digest line + 4 false-positive keys
+    + h 8 key + 1 found flag (+ 8 address for find*)."""
+    return 8 + 128 + 4 + h * 8 + 1 + (8 if with_ptr else 0)
+
+
+def copy_bandwidth(mib: int = 2048, reps: int = 10) -> float:
+    """Device-to-device copy rate (read + write bytes / s) on this GPU: the
+    streaming bandwidth the hash-table kernels are compared against."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def calibrate_copy(mib: int) -> None:
@@ -354,11 +383,97 @@ def run_gpu(args):
         insert_new = dict(batches=args.insert_steps, bkvs=round(args.insert_steps * batch / dt / 1e9, 3),
                           kernel_avg_ms={n: round(v[1] / v[0], 5) for n, v in ks.items()},
                           lambda_end=round(tab.size() / cap, 4))
+    extra_ops = run_extra_ops(args, tables, batch, dim, hit) if args.extra_ops else None
     for T in tables:
         T["tab"].close()
     return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
                 dominant=dominant, h=h_avg, find_ms_events=sum(find_ms_all) / len(find_ms_all),
-                insert_new=insert_new)
+                insert_new=insert_new, extra_ops=extra_ops)
+
+
+def run_extra_ops(args, tables, batch, dim, hit):
+    """The other calls of the paper's §4.1 on the same tables, after the timed
+    region (reported in detail only): find* and contains on the step's find
+    batches; insert_and_evict, then find_or_insert, on fresh batches of the
+    upsert mix (90 % resident, 10 % new keys). Per call: median of HIP-event
+    times around the call; per kernel: the library's event times."""
+    import torch
+
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    reps = min(args.steps, 10)
+    out = {}
+    for li, T in enumerate(tables):
+        tab = T["tab"]
+        lam = T["lam"]
+        r = {}
+        ptrs = torch.empty(batch, dtype=torch.int64, device=dev)
+        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        for name in ("find_ptr", "contains"):
+            ms = []
+            tab.profile_start()
+            for s in range(reps + 2):
+                q = T["finds"][s % len(T["finds"])]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if name == "find_ptr":
+                    tab.find_ptr(q, ptrs_out=ptrs, found_out=found)
+                else:
+                    tab.contains(q, found_out=found)
+                e1.record()
+                ms.append((e0, e1))
+            ks = tab.profile_stop()
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) for a, b in ms[2:])[len(ms[2:]) // 2]
+            kn = ks[name]
+            kavg = kn[1] / kn[0]
+            byts = batch * locate_bytes_per_key(hit[lam], name == "find_ptr")
+            r[name] = dict(call_ms_median=round(t, 5), bkvs=round(batch / t / 1e6, 3), kernel_avg_ms=round(kavg, 5),
+                           achieved_GBps=round(byts / (kavg * 1e-3) / 1e9, 1),
+                           frac=round(byts / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        # write calls on fresh batches of the upsert mix
+        n_new = int(round(batch * args.new_frac))
+        k_all, _, _, _ = tab.export_batch(with_values=False)
+        evk = torch.empty(batch, dtype=torch.int64, device=dev)
+        evv = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+        evs = torch.empty(batch, dtype=torch.int64, device=dev)
+        cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+        score0 = 1 << 30
+        batches = []
+        for j in range(2 * (reps + 2)):
+            pick = torch.argsort(gen.counter_words(SEED, 500 + li, j * k_all.numel(), k_all.numel(), dev))
+            res = k_all[pick[:batch - n_new]]
+            new = gen.unique_keys(SEED, 520 + li, j * batch, n_new, device=dev)
+            uk = gen.shuffle(torch.cat([res, new]), SEED, 540 + li * 1000 + j)
+            batches.append((uk, gen.values(uk, 7000 + j, dim),
+                            torch.full((batch,), score0 + j, dtype=torch.int64, device=dev)))
+        torch.cuda.synchronize()
+        for name, part in (("insert_and_evict", batches[:reps + 2]), ("find_or_insert", batches[reps + 2:])):
+            ms = []
+            handed = []
+            tab.profile_start()
+            for uk, uv, usc in part:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if name == "insert_and_evict":
+                    tab.insert_and_evict(uk, uv, usc, out=(evk, evv, evs, cnt))
+                else:
+                    tab.find_or_insert(uk, uv, usc, found_out=found)
+                e1.record()
+                ms.append((e0, e1))
+                if name == "insert_and_evict":
+                    handed.append(cnt.clone())
+            ks = tab.profile_stop()
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) for a, b in ms[2:])[len(ms[2:]) // 2]
+            r[name] = dict(call_ms_median=round(t, 5), bkvs=round(batch / t / 1e6, 3),
+                           kernel_avg_ms={k: round(v[1] / v[0], 5) for k, v in ks.items()})
+            if handed:
+                r[name]["handed_back_per_call"] = round(sum(int(c.item()) for c in handed[2:]) / len(handed[2:]), 1)
+        out[str(lam)] = r
+        log(f"lambda={lam}: other calls {r}")
+    return out
 
 
 def run_cpu_baseline(args):
@@ -418,6 +533,8 @@ def main():
         capacity_sweep(args)
         return
     g = run_gpu(args)
+    g["copy_GBps"] = copy_bandwidth()
+    log(f"device copy bandwidth {g['copy_GBps']:.1f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline")
@@ -479,6 +596,9 @@ def main():
             "per_lambda": g["detail"],
             "find_lambda_variation": round(g["find_var"], 4),
             "insert_all_new_at_lambda_1": g["insert_new"],
+            "other_calls_per_lambda": g["extra_ops"],
+            "copy_GBps": round(g["copy_GBps"], 1),
+            "dominant_frac_of_copy": round(g["kernels"][g["dominant"]]["achieved_GBps"] / g["copy_GBps"], 4),
             "hit_rate": round(g["h"], 4),
         },
     }

@@ -69,6 +69,13 @@ struct InsertCall {
   float* ev_values;
   uint64_t* ev_scores;
   unsigned long long* ev_count;
+  // insert_and_evict, parallel inserter: staging of n entries (kind [n] u8,
+  // keys and scores [n] u64, rows [n*dim] f32)
+  uint8_t* st_kind;
+  uint64_t* st_keys;
+  uint64_t* st_scores;
+  float* st_rows;
+  uint32_t* chunk_count;  // [ceil(n / 1024)]
 };
 
 // next, target: [n] u32 workspaces (not used by insert_or_assign in serial mode).

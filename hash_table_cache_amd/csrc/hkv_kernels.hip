@@ -505,6 +505,21 @@ struct Evicted {
   unsigned long long* count;
 };
 
+// Staging of insert_and_evict's hand-back in the parallel inserter. Chain key
+// i causes at most one departure; the owner kernel records it at index i and
+// a compaction kernel moves the recorded entries to the output, one counter
+// reservation per block instead of one contended atomic per entry.
+//   kind[i]: 0 nothing left, 1 a resident was evicted (its key, score and row
+//   are staged at i), 2 key i itself was turned away (key and score staged,
+//   its row is the input row). Written for every chain key; keys outside the
+//   chains (next[i] == kSkipIdx) are never read.
+struct EvictStage {
+  uint8_t* kind;
+  uint64_t* keys;
+  uint64_t* scores;
+  float* rows;
+};
+
 // Hands back one entry with the 16 lanes of a group: lane 0 reserves the
 // output index, the group copies the row from `src` (or from registers).
 template <bool V4>
@@ -778,7 +793,7 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
 template <bool V4, bool EVICT>
 __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint64_t k, uint64_t score,
                                              const RowRegs& rr, const float* row, bool in_regs, bool fresh,
-                                             const Evicted& ev, int lane) {
+                                             const EvictStage& st, uint32_t idx, int lane) {
   const uint32_t d = digest_of(fmix64(k));
   float* const rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
   auto write_row = [&](int s) {
@@ -805,6 +820,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
   if (hit >= 0) {
     bucket_write(o, t, hit, false, k, d, score, lane);
     write_row(hit);
+    if (EVICT && lane == 0) st.kind[idx] = 0;
     return;
   }
   if (o.occ < kSlots) {
@@ -812,6 +828,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
     bucket_write(o, t, s, true, k, d, score, lane);
     write_row(s);
     o.occ += 1;
+    if (EVICT && lane == 0) st.kind[idx] = 0;
     return;
   }
   if (!o.cols) bucket_load_cols(o, t, lane);
@@ -832,13 +849,25 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
   if (score > gs || (score == gs && k > gk)) {
     const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
     const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
-    // the victim's row is read (by the lanes that wrote it, if this kernel
-    // did) before the new row overwrites it
-    if constexpr (EVICT) emit_entry<V4>(ev, t, gk, gs, rows + static_cast<uint64_t>(vs) * t.dim, nullptr, lane);
+    if constexpr (EVICT) {
+      // the victim's row is staged (read by the lanes that wrote it, if this
+      // kernel did) before the new row overwrites it
+      copy_row<kInsG, V4, false>(st.rows + static_cast<uint64_t>(idx) * t.dim,
+                                 rows + static_cast<uint64_t>(vs) * t.dim, t.dim, lane);
+      if (lane == 0) {
+        st.keys[idx] = gk;
+        st.scores[idx] = gs;
+        st.kind[idx] = 1;
+      }
+    }
     bucket_write(o, t, vs, true, k, d, score, lane);
     write_row(vs);
   } else if constexpr (EVICT) {
-    emit_entry<V4>(ev, t, k, score, row, in_regs ? &rr : nullptr, lane);
+    if (lane == 0) {
+      st.keys[idx] = k;
+      st.scores[idx] = score;
+      st.kind[idx] = 2;
+    }
   }
 }
 
@@ -860,7 +889,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
                                                               const uint64_t* __restrict__ scores,
                                                               const uint32_t* __restrict__ next,
                                                               const uint32_t* __restrict__ target,
-                                                              Evicted ev) {
+                                                              EvictStage st) {
   const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) & ~uint64_t(kInsG - 1);
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (first >= n) return;
@@ -901,7 +930,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     const uint32_t occ0 = o.occ;
     // A chain holds only keys the probe found missing, so the owner's own
     // key, applied first, is known to be absent.
-    bucket_apply<V4, EVICT>(o, t, k, score, rr, row, in_regs, true, ev, lane);
+    bucket_apply<V4, EVICT>(o, t, k, score, rr, row, in_regs, true, st, i, lane);
     // The chain holds at most n keys and ends at this owner's own key; the
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
@@ -911,7 +940,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       const uint64_t scc = scores[cur];
       const float* rowc = values + static_cast<uint64_t>(cur) * t.dim;
       if (in_regs) row_regs_load(rr, rowc, t.dim, lane);
-      bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, ev, lane);
+      bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, st, cur, lane);
       cur = after;
     }
     if (DUAL && o.occ >= kSlots) {
@@ -936,6 +965,106 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       if (o.occ != occ0) t.occ[o.b] = o.occ;
       __hip_atomic_store(t.head + o.b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+// insert_and_evict, parallel inserter: the staged departures are compacted
+// in batch-index order without atomics. A chunk is 1024 consecutive batch
+// indices (256 threads x 4); the count kernel writes each chunk's number of
+// departures, the write kernel sums the counts of the chunks before its own
+// (a few KB, cached), ranks its departures with wave ballots and copies them
+// out, 16 lanes per row; the last chunk writes the total.
+constexpr int kChunk = 4 * kBlock;
+
+__device__ __forceinline__ bool departs(uint64_t i, uint64_t n, const uint32_t* next, const EvictStage& st,
+                                        uint32_t* kd) {
+  *kd = 0;
+  if (i < n && next[i] != kSkipIdx) *kd = st.kind[i];
+  return *kd != 0;
+}
+
+__global__ __launch_bounds__(kBlock) void evict_count_kernel(uint64_t n, const uint32_t* __restrict__ next,
+                                                             EvictStage st, uint32_t* __restrict__ chunk_count) {
+  __shared__ uint32_t part[kBlock / 64];
+  const uint64_t c0 = static_cast<uint64_t>(blockIdx.x) * kChunk;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t kd;
+    cnt += departs(c0 + r * kBlock + threadIdx.x, n, next, st, &kd) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (wave_lane() == 0) part[threadIdx.x / 64] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) total += part[w];
+    chunk_count[blockIdx.x] = total;
+  }
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kBlock) void evict_write_kernel(TableView t, uint64_t n,
+                                                             const uint32_t* __restrict__ next, EvictStage st,
+                                                             const float* __restrict__ values,
+                                                             const uint32_t* __restrict__ chunk_count,
+                                                             Evicted out) {
+  __shared__ unsigned long long red[kBlock / 64];
+  __shared__ uint32_t cnt[4][kBlock / 64];
+  __shared__ uint32_t src[kChunk];
+  const int w = static_cast<int>(threadIdx.x / 64);
+  const int lane = wave_lane();
+  // departures of the chunks before this one
+  unsigned long long before = 0;
+  for (uint32_t c = threadIdx.x; c < blockIdx.x; c += kBlock) before += chunk_count[c];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+  if (lane == 0) red[w] = before;
+  const uint64_t c0 = static_cast<uint64_t>(blockIdx.x) * kChunk;
+  uint32_t kd[4];
+  uint64_t bal[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool d = departs(c0 + r * kBlock + threadIdx.x, n, next, st, &kd[r]);
+    bal[r] = __ballot(d);
+    if (lane == 0) cnt[r][w] = static_cast<uint32_t>(__popcll(bal[r]));
+  }
+  __syncthreads();
+  unsigned long long base = 0;
+#pragma unroll
+  for (int v = 0; v < kBlock / 64; ++v) base += red[v];
+  // rank = departures at smaller indices in this chunk: order (r, wave, lane)
+  uint32_t total = 0;
+  uint32_t rank[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t off = total;
+#pragma unroll
+    for (int v = 0; v < kBlock / 64; ++v) off += v < w ? cnt[r][v] : 0u;
+    rank[r] = off + static_cast<uint32_t>(__popcll(bal[r] & ((1ull << lane) - 1)));
+#pragma unroll
+    for (int v = 0; v < kBlock / 64; ++v) total += cnt[r][v];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *out.count = base + total;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (kd[r] == 0) continue;
+    const uint64_t i = c0 + r * kBlock + threadIdx.x;
+    out.keys[base + rank[r]] = st.keys[i];
+    if (out.scores) out.scores[base + rank[r]] = st.scores[i];
+    src[rank[r]] = static_cast<uint32_t>(r * kBlock + threadIdx.x) | (kd[r] == 1 ? 0x80000000u : 0u);
+  }
+  if (!out.values) return;
+  __syncthreads();
+  const int g = static_cast<int>(threadIdx.x / kInsG);
+  const int gl = static_cast<int>(threadIdx.x & (kInsG - 1));
+  for (uint32_t e = g; e < total; e += kBlock / kInsG) {
+    const uint32_t sv = src[e];
+    const uint64_t j = c0 + (sv & 0x7FFFFFFFu);
+    const float* from = (sv & 0x80000000u) ? st.rows + j * t.dim : values + j * t.dim;
+    copy_row<kInsG, V4, true>(out.values + (base + e) * t.dim, from, t.dim, gl);
   }
 }
 
@@ -1084,14 +1213,22 @@ hipError_t probe_g(const TableView& t, uint64_t n, const InsertCall& c, uint32_t
 template <bool V4, bool DUAL>
 hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const uint32_t* next,
                    const uint32_t* target, hipStream_t s, KernelTimer* tm) {
-  const Evicted ev{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
-  if (c.ev_keys) {
-    HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true>), dim3(grid_for(n)), dim3(kBlock), s,
-               t, n, c.keys, c.values, c.scores, next, target, ev);
-  } else {
+  const EvictStage st{c.st_kind, c.st_keys, c.st_scores, c.st_rows};
+  if (!c.ev_keys) {
     HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false>), dim3(grid_for(n)), dim3(kBlock), s,
-               t, n, c.keys, c.values, c.scores, next, target, ev);
+               t, n, c.keys, c.values, c.scores, next, target, st);
+    return hipGetLastError();
   }
+  HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true>), dim3(grid_for(n)), dim3(kBlock), s, t,
+             n, c.keys, c.values, c.scores, next, target, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const Evicted out{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
+  const uint32_t chunks = static_cast<uint32_t>((n + kChunk - 1) / kChunk);
+  HKV_LAUNCH(tm, "evict_count", evict_count_kernel, dim3(chunks), dim3(kBlock), s, n, next, st, c.chunk_count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  HKV_LAUNCH(tm, "evict_write", (evict_write_kernel<V4>), dim3(chunks), dim3(kBlock), s, t, n, next, st,
+             c.values, c.chunk_count, out);
   return hipGetLastError();
 }
 
@@ -1138,7 +1275,8 @@ template <bool V4, bool DUAL>
 hipError_t upsert_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next, uint32_t* target,
                     bool serial, hipStream_t s, KernelTimer* tm) {
   hipError_t e = hipSuccess;
-  if (c.ev_count) {
+  if (c.ev_count && (serial || n == 0)) {
+    // (the parallel path's last compaction block writes the count itself)
     HKV_LAUNCH(tm, "zero", zero_u64_kernel, dim3(1), dim3(1), s, c.ev_count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -132,6 +132,12 @@ struct hkv_table {
   uint32_t* ws_next = nullptr;  // inserter workspace
   uint32_t* ws_target = nullptr;
   uint64_t ws_cap = 0;
+  uint8_t* ev_kind = nullptr;  // insert_and_evict staging (parallel inserter)
+  uint64_t* ev_keys = nullptr;
+  uint64_t* ev_scores = nullptr;
+  float* ev_rows = nullptr;
+  uint32_t* ev_chunks = nullptr;
+  uint64_t ev_cap = 0;
   unsigned long long* size_dev = nullptr;
   unsigned long long* size_host = nullptr;  // pinned
   std::mutex mu;
@@ -158,6 +164,11 @@ void free_storage(hkv_table* t) {
   }
   if (t->ws_next) (void)hipFree(t->ws_next);
   if (t->ws_target) (void)hipFree(t->ws_target);
+  if (t->ev_kind) (void)hipFree(t->ev_kind);
+  if (t->ev_keys) (void)hipFree(t->ev_keys);
+  if (t->ev_scores) (void)hipFree(t->ev_scores);
+  if (t->ev_rows) (void)hipFree(t->ev_rows);
+  if (t->ev_chunks) (void)hipFree(t->ev_chunks);
   if (t->size_dev) (void)hipFree(t->size_dev);
   if (t->size_host) (void)hipHostFree(t->size_host);
   for (auto& list : t->last)
@@ -257,11 +268,44 @@ hkv_status ensure_workspace(hkv_table* t, uint64_t n) {
   return HKV_OK;
 }
 
+// Staging for insert_and_evict's hand-back: 17 + 4*dim bytes per batch key
+// plus 4 bytes per 1024 keys, grown on demand like the inserter workspace.
+hkv_status ensure_evict_stage(hkv_table* t, uint64_t n) {
+  if (n <= t->ev_cap) return HKV_OK;
+  hkv_status st = drain_group(t, kInserter);
+  if (st != HKV_OK) return st;
+  uint64_t cap = t->ev_cap ? t->ev_cap : 1024;
+  while (cap < n) cap *= 2;
+  if (cap > kMaxBatch) cap = kMaxBatch;
+  auto release = [t]() {
+    void* p[5] = {t->ev_kind, t->ev_keys, t->ev_scores, t->ev_rows, t->ev_chunks};
+    for (void* q : p)
+      if (q) (void)hipFree(q);
+    t->ev_kind = nullptr;
+    t->ev_keys = t->ev_scores = nullptr;
+    t->ev_rows = nullptr;
+    t->ev_chunks = nullptr;
+    t->ev_cap = 0;
+  };
+  release();
+  const uint64_t dim = t->opt.dim;
+  const uint64_t chunks = (cap + 1023) / 1024;
+  if (hipMalloc(&t->ev_kind, cap) != hipSuccess || hipMalloc(&t->ev_keys, cap * 8) != hipSuccess ||
+      hipMalloc(&t->ev_scores, cap * 8) != hipSuccess || hipMalloc(&t->ev_rows, cap * dim * 4) != hipSuccess ||
+      hipMalloc(&t->ev_chunks, chunks * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    release();
+    return fail(HKV_ENOMEM, "insert_and_evict staging of %llu entries", static_cast<unsigned long long>(cap));
+  }
+  t->ev_cap = cap;
+  return HKV_OK;
+}
+
 }  // namespace
 
 // Shared tail of the inserter calls (arguments already validated): workspace,
 // ordering after incompatible groups, launch, completion event.
-static hkv_status run_inserter(hkv_table* t, uint64_t n, const hkv::InsertCall& c, bool vec4, const char* what,
+static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool vec4, const char* what,
                                hipStream_t stream) {
   const bool serial = (t->opt.flags & HKV_FLAG_SERIAL_INSERT) != 0;
   const bool needs_ws = !serial || c.fetch || c.ev_keys;
@@ -270,6 +314,14 @@ static hkv_status run_inserter(hkv_table* t, uint64_t n, const hkv::InsertCall& 
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   hkv_status st;
   if (needs_ws && (st = ensure_workspace(t, n)) != HKV_OK) return st;
+  if (c.ev_keys && !serial && n > 0) {
+    if ((st = ensure_evict_stage(t, n)) != HKV_OK) return st;
+    c.st_kind = t->ev_kind;
+    c.st_keys = t->ev_keys;
+    c.st_scores = t->ev_scores;
+    c.st_rows = t->ev_rows;
+    c.chunk_count = t->ev_chunks;
+  }
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
   const hipError_t e = hkv::launch_upsert(t->view, n, c, t->ws_next, t->ws_target, vec4, serial, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, what);

@@ -197,7 +197,8 @@ hkv_status hkv_contains(hkv_table* table, uint64_t n, const uint64_t* keys, uint
  *   evicted_values   [n*dim] float32, output, nullable
  *   evicted_scores   [n] uint64, output, nullable
  *   evicted_count    [1] uint64, output
- * Uses the same table-owned workspace as insert_or_assign.
+ * Uses the same table-owned workspace as insert_or_assign plus a staging area
+ * of (17 + 4*dim)*n bytes, both grown on demand.
  */
 hkv_status hkv_insert_and_evict(hkv_table* table, uint64_t n, const uint64_t* keys, const float* values,
                                 const uint64_t* scores, uint64_t* evicted_keys, float* evicted_values,
