@@ -25,6 +25,7 @@ struct TableView {
   uint32_t pow2;      // nb is a power of two
   uint32_t dual;      // dual-bucket mode
   uint32_t lanes;     // lanes per key of find/assign/insert probes; 0 = by dim
+  uint32_t keys_per_group;  // keys each group of the key-side probes serves (1, 2 or 4)
 };
 
 // Optional per-kernel timing: when a timer is passed, each launch is

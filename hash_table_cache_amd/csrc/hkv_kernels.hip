@@ -171,39 +171,68 @@ __device__ __forceinline__ uint32_t candidate_mask(const uint32_t (&w)[NW], uint
 // candidate in the same lane is rare (about 1 in 4000 lanes) and is looped.
 // NT: the first two loads are nontemporal (readers only). Returns the table
 // position of the matching slot or -1.
+// The candidate-key check split in two so that several keys' loads can be
+// in flight together: cand_issue picks the first two candidate positions and
+// loads their keys, cand_finish compares them and loops over any further
+// candidates.
+struct Cand {
+  uint32_t m1, m2;
+  uint64_t base1, base2;
+  uint64_t p0, p1;
+  uint64_t k0, k1;
+  bool h0, h1;
+};
+
+template <bool NT>
+__device__ __forceinline__ void cand_issue(Cand& c, const uint64_t* __restrict__ keys, uint32_t m1,
+                                           uint64_t base1, uint32_t m2, uint64_t base2) {
+  // candidate positions in order: the bits of m1 (over base1), then of m2
+  c.h0 = (m1 | m2) != 0;
+  c.h1 = __builtin_popcount(m1) + __builtin_popcount(m2) >= 2;
+  c.p0 = 0;
+  c.p1 = 0;
+  if (c.h0) {
+    c.p0 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
+    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
+  }
+  if (c.h1) {
+    c.p1 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
+    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
+  }
+  c.k0 = 0;
+  c.k1 = 0;
+  if (c.h0) c.k0 = NT ? __builtin_nontemporal_load(keys + c.p0) : keys[c.p0];
+  if (c.h1) c.k1 = NT ? __builtin_nontemporal_load(keys + c.p1) : keys[c.p1];
+  c.m1 = m1;
+  c.m2 = m2;
+  c.base1 = base1;
+  c.base2 = base2;
+}
+
+__device__ __forceinline__ int64_t cand_finish(Cand& c, const uint64_t* __restrict__ keys, uint64_t k) {
+  int64_t hit = -1;
+  if (c.h0 && c.k0 == k) hit = static_cast<int64_t>(c.p0);
+  if (c.h1 && c.k1 == k) hit = static_cast<int64_t>(c.p1);
+  while (c.m1) {
+    const uint64_t p = c.base1 + __builtin_ctz(c.m1);
+    c.m1 &= c.m1 - 1;
+    if (keys[p] == k) hit = static_cast<int64_t>(p);
+  }
+  while (c.m2) {
+    const uint64_t p = c.base2 + __builtin_ctz(c.m2);
+    c.m2 &= c.m2 - 1;
+    if (keys[p] == k) hit = static_cast<int64_t>(p);
+  }
+  return hit;
+}
+
 template <bool NT>
 __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__ keys, uint64_t k,
                                                     uint32_t m1, uint64_t base1, uint32_t m2,
                                                     uint64_t base2) {
-  // candidate positions in order: the bits of m1 (over base1), then of m2
-  const bool h0 = (m1 | m2) != 0;
-  const bool h1 = __builtin_popcount(m1) + __builtin_popcount(m2) >= 2;
-  uint64_t p0 = 0, p1 = 0;
-  if (h0) {
-    p0 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
-    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
-  }
-  if (h1) {
-    p1 = m1 ? base1 + __builtin_ctz(m1) : base2 + __builtin_ctz(m2);
-    if (m1) m1 &= m1 - 1; else m2 &= m2 - 1;
-  }
-  uint64_t k0 = 0, k1 = 0;
-  if (h0) k0 = NT ? __builtin_nontemporal_load(keys + p0) : keys[p0];
-  if (h1) k1 = NT ? __builtin_nontemporal_load(keys + p1) : keys[p1];
-  int64_t hit = -1;
-  if (h0 && k0 == k) hit = static_cast<int64_t>(p0);
-  if (h1 && k1 == k) hit = static_cast<int64_t>(p1);
-  while (m1) {
-    const uint64_t p = base1 + __builtin_ctz(m1);
-    m1 &= m1 - 1;
-    if (keys[p] == k) hit = static_cast<int64_t>(p);
-  }
-  while (m2) {
-    const uint64_t p = base2 + __builtin_ctz(m2);
-    m2 &= m2 - 1;
-    if (keys[p] == k) hit = static_cast<int64_t>(p);
-  }
-  return hit;
+  Cand c;
+  cand_issue<NT>(c, keys, m1, base1, m2, base2);
+  return cand_finish(c, keys, k);
 }
 
 // Occupied slots counted from a group's digest words: slots fill in order and
@@ -256,6 +285,47 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
   return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
 }
 
+// probe() for K keys per group with their memory round trips overlapped: all
+// K digest lines are requested before any is used, then all K keys'
+// candidate keys. hit[j] is group-uniform.
+template <int G, bool DUAL, int K>
+__device__ __forceinline__ void probe_many(const TableView& t, const uint64_t (&k)[K], int lane,
+                                           int64_t (&hit)[K]) {
+  constexpr int NW = kSlots / G / 4;
+  uint32_t w1[K][NW], w2[K][NW];
+  uint32_t b1[K], b2[K], pat[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint64_t h = fmix64(k[j]);
+    pat[j] = digest_of(h) * 0x01010101u;
+    b1[j] = bucket_of(t, h);
+    b2[j] = b1[j];
+    load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1[j]) * kSlots, lane, w1[j]);
+    if constexpr (DUAL) {
+      b2[j] = bucket_of(t, fmix64(k[j] ^ kSecondSalt));
+      if (b2[j] != b1[j]) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2[j]) * kSlots, lane, w2[j]);
+    }
+  }
+  const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
+  Cand c[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    uint32_t m1 = is_reserved(k[j]) ? 0u : candidate_mask<NW>(w1[j], pat[j]);
+    uint32_t m2 = 0;
+    if constexpr (DUAL) {
+      if (b2[j] != b1[j] && !is_reserved(k[j])) m2 = candidate_mask<NW>(w2[j], pat[j]);
+    }
+    cand_issue<true>(c[j], t.keys, m1, static_cast<uint64_t>(b1[j]) * kSlots + off, m2,
+                     static_cast<uint64_t>(b2[j]) * kSlots + off);
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int64_t hj = cand_finish(c[j], t.keys, k[j]);
+    const uint64_t bits = group_bits<G>(__ballot(hj >= 0));
+    hit[j] = bits == 0 ? -1 : __shfl(hj, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
+  }
+}
+
 // ---------------------------------------------------------------- readers --
 
 template <int G, bool V4, bool DUAL, bool NT>
@@ -284,21 +354,33 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
 // of find. A hit writes the device-accessible address of the key's value row
 // (host-mapped when values live in host memory), found = 1 and the score; a
 // miss writes a null address and found = 0. Every output is optional.
-template <int G, bool DUAL>
+// A group serves K consecutive keys (probe_many), which multiplies the
+// round trips each wave has in flight; a key past n is probed as a reserved
+// key and writes nothing.
+template <int G, bool DUAL, int K>
 __global__ __launch_bounds__(kBlock) void locate_kernel(TableView t, uint64_t n,
                                                         const uint64_t* __restrict__ keys,
                                                         uint64_t* __restrict__ ptrs_out,
                                                         uint8_t* __restrict__ found,
                                                         uint64_t* __restrict__ scores_out) {
-  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G * K;
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
-  if (i >= n) return;
-  const int64_t p = probe<G, DUAL, true>(t, keys[i], lane);
+  if (i0 >= n) return;
+  uint64_t k[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) k[j] = i0 + j < n ? keys[i0 + j] : ~0ull;
+  int64_t p[K];
+  probe_many<G, DUAL, K>(t, k, lane, p);
   if (lane != 0) return;
-  if (found) found[i] = p >= 0 ? 1 : 0;
-  if (ptrs_out)
-    ptrs_out[i] = p >= 0 ? reinterpret_cast<uint64_t>(t.values + static_cast<uint64_t>(p) * t.dim) : 0ull;
-  if (scores_out && p >= 0) scores_out[i] = t.scores[p];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint64_t i = i0 + j;
+    if (i >= n) break;
+    if (found) found[i] = p[j] >= 0 ? 1 : 0;
+    if (ptrs_out)
+      ptrs_out[i] = p[j] >= 0 ? reinterpret_cast<uint64_t>(t.values + static_cast<uint64_t>(p[j]) * t.dim) : 0ull;
+    if (scores_out && p[j] >= 0) scores_out[i] = t.scores[p[j]];
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void size_kernel(const uint32_t* __restrict__ occ, uint64_t nb,
@@ -1299,8 +1381,20 @@ hipError_t upsert_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_
 template <int G, bool DUAL>
 hipError_t locate_g(const TableView& t, uint64_t n, const uint64_t* keys, uint64_t* ptrs, uint8_t* found,
                     uint64_t* sc, hipStream_t s, KernelTimer* tm) {
-  HKV_LAUNCH(tm, ptrs ? "find_ptr" : "contains", (locate_kernel<G, DUAL>), dim3(grid_for(n * G)), dim3(kBlock),
-             s, t, n, keys, ptrs, found, sc);
+  const char* name = ptrs ? "find_ptr" : "contains";
+  switch (t.keys_per_group) {
+    case 1:
+      HKV_LAUNCH(tm, name, (locate_kernel<G, DUAL, 1>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n, keys, ptrs,
+                 found, sc);
+      break;
+    case 4:
+      HKV_LAUNCH(tm, name, (locate_kernel<G, DUAL, 4>), dim3(grid_for((n + 3) / 4 * G)), dim3(kBlock), s, t, n,
+                 keys, ptrs, found, sc);
+      break;
+    default:
+      HKV_LAUNCH(tm, name, (locate_kernel<G, DUAL, 2>), dim3(grid_for((n + 1) / 2 * G)), dim3(kBlock), s, t, n,
+                 keys, ptrs, found, sc);
+  }
   return hipGetLastError();
 }
 

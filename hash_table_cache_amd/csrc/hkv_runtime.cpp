@@ -381,9 +381,12 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   v.nb_mask = v.pow2 ? nb - 1 : 0;
   v.dim = o->dim;
   v.dual = o->dual_bucket;
-  // Tuning override of the lanes serving one key (4, 8 or 16); anything else
-  // keeps the default chosen from dim.
+  // Tuning overrides: lanes serving one key (4, 8 or 16; anything else keeps
+  // the default chosen from dim) and keys per group of the key-side probes of
+  // find* and contains (1, 2 or 4; default 2).
   if (const char* g = std::getenv("HKV_GROUP_LANES")) v.lanes = static_cast<uint32_t>(std::atoi(g));
+  v.keys_per_group = 2;
+  if (const char* g = std::getenv("HKV_KEYS_PER_GROUP")) v.keys_per_group = static_cast<uint32_t>(std::atoi(g));
   const uint64_t value_bytes = cap * o->dim * sizeof(float);
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
