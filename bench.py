@@ -68,6 +68,8 @@ def parse_args():
                    help="skip the find*/contains/insert_and_evict/find_or_insert measurements")
     p.add_argument("--capacity-sweep", default="", metavar="LOG2S",
                    help="only measure find on full tables of these capacities (e.g. 24,26,28) and exit")
+    p.add_argument("--hybrid", default="", metavar="FRACS",
+                   help="value-placement sweep at these HBM fractions of the value rows, e.g. 1.0,0.5,0.0")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (counter calibration) and exit")
     return p.parse_args()
@@ -203,6 +205,70 @@ def capacity_sweep(args) -> None:
         torch.cuda.empty_cache()
     b = [v["find_bkvs"] for v in out.values()]
     print(json.dumps({"capacity_sweep": out, "dim": dim, "variation": round((max(b) - min(b)) / max(b), 4)}),
+          flush=True)
+
+
+def hybrid_sweep(args) -> None:
+    """Value placement (the HBM watermark): full single-bucket tables of
+    2^capacity_log2 slots whose value rows are all in HBM, half in HBM and half
+    in pinned host memory, or all on the host. Per placement: find*, contains
+    and find (value copy) on 2^batch_log2-key batches, 90 % resident; 2 warm-up
+    and 10 timed batches, library event times. Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap, dim, batch = 1 << args.capacity_log2, args.dim, 1 << args.batch_log2
+    row = 4 * dim
+    n_hit = int(round(batch * args.hit_frac))
+    out = {}
+    for frac in [float(x) for x in args.hybrid.split(",")]:
+        t0 = time.perf_counter()
+        tab = H.HashTable(cap, dim, values_on_host=frac < 1.0, hbm_value_bytes=int(frac * cap * row))
+        cursor, step = 0, 0
+        while tab.size() < cap:
+            step += 1
+            k = gen.unique_keys(SEED, 80, cursor, batch, device=dev)
+            cursor += batch
+            tab.insert_or_assign(k, gen.values(k, step, dim, SEED),
+                                 torch.full((batch,), step, dtype=torch.int64, device=dev))
+        pool = gen.unique_keys(SEED, 80, cursor - 2 * batch, 2 * batch, device=dev)
+        qs = []
+        for j in range(12):
+            perm = torch.argsort(gen.counter_words(SEED, 180, j * pool.numel(), pool.numel(), dev))
+            q = torch.cat([pool[perm[:n_hit]], gen.unique_keys(SEED, 181, j * batch, batch - n_hit, device=dev)])
+            qs.append(gen.shuffle(q, SEED, 190 + j))
+        vals = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        ptrs = torch.empty(batch, dtype=torch.int64, device=dev)
+        r = dict(fill_s=round(time.perf_counter() - t0, 1))
+        for name in ("find_ptr", "contains", "find"):
+            call = {"find_ptr": lambda q: tab.find_ptr(q, ptrs, found),
+                    "contains": lambda q: tab.contains(q, found),
+                    "find": lambda q: tab.find(q, vals, found)}[name]
+            for q in qs[:2]:
+                call(q)
+            torch.cuda.synchronize()
+            tab.profile_start()
+            for q in qs[2:]:
+                call(q)
+            st = tab.profile_stop()[name]
+            avg = st[1] / st[0]
+            r[name] = dict(kernel_avg_ms=round(avg, 5), bkvs=round(batch / avg / 1e6, 3))
+        if frac < 1.0:
+            r["host_link_GBps_find"] = round(batch * args.hit_frac * (1 - frac) * row / (r["find"]["kernel_avg_ms"]
+                                                                                       * 1e-3) / 1e9, 1)
+        out[f"hbm_fraction_{frac}"] = r
+        log(f"hbm fraction {frac}: {r}")
+        tab.close()
+        torch.cuda.empty_cache()
+    base = out.get("hbm_fraction_1.0")
+    if base:
+        for k, r in out.items():
+            r["find_ptr_retained"] = round(r["find_ptr"]["bkvs"] / base["find_ptr"]["bkvs"], 4)
+    print(json.dumps({"hybrid": out, "capacity": cap, "dim": dim, "batch": batch, "hit_frac": args.hit_frac}),
           flush=True)
 
 
@@ -531,6 +597,9 @@ def main():
         return
     if args.capacity_sweep:
         capacity_sweep(args)
+        return
+    if args.hybrid:
+        hybrid_sweep(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()

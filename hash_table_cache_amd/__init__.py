@@ -41,19 +41,20 @@ class HashTable:
 
     capacity: slots (a multiple of 128); dim: float32 values per row;
     dual_bucket: score-based dual-bucket mode; values_on_host: value rows in
-    pinned host memory mapped into the GPU; serial_insert: apply inserts one key
+    pinned host memory mapped into the GPU, except the first hbm_value_bytes'
+    worth of buckets, which stay in HBM; serial_insert: apply inserts one key
     at a time in input order (deterministic placement, slow).
     """
 
     def __init__(self, capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
-                 device: int = 0, serial_insert: bool = False):
+                 device: int = 0, serial_insert: bool = False, hbm_value_bytes: int = 0):
         self.capacity = int(capacity)
         self.dim = int(dim)
         self.dual_bucket = bool(dual_bucket)
         self.values_on_host = bool(values_on_host)
         self.device = int(device)
         flags = HKV_FLAG_SERIAL_INSERT if serial_insert else 0
-        self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags)
+        self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags, hbm_value_bytes)
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:

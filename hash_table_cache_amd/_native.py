@@ -57,6 +57,7 @@ class HkvOptions(ctypes.Structure):
         ("values_on_host", ctypes.c_uint32),
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("hbm_value_bytes", ctypes.c_uint64),
     ]
 
 
@@ -150,9 +151,9 @@ def _stream(stream, device: int):
 
 
 def hkv_create(capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
-               device: int = 0, flags: int = 0) -> ctypes.c_void_p:
+               device: int = 0, flags: int = 0, hbm_value_bytes: int = 0) -> ctypes.c_void_p:
     opt = HkvOptions(int(capacity), int(dim), BUCKET_SLOTS, int(bool(dual_bucket)),
-                     int(bool(values_on_host)), int(device), int(flags))
+                     int(bool(values_on_host)), int(device), int(flags), int(hbm_value_bytes))
     h = ctypes.c_void_p()
     _check(lib.hkv_create(ctypes.byref(opt), ctypes.byref(h)))
     return h

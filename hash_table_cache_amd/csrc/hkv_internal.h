@@ -9,12 +9,15 @@
 namespace hkv {
 
 // Device-side view of one table. Slot s of bucket b is position p = b*128 + s
-// in digests/keys/scores and row p of values (row-major, dim floats).
+// in digests/keys/scores and value row p (dim floats).
 struct TableView {
   uint8_t* digests;   // [nb*128]  one-byte digest per slot; 0 marks an empty slot
   uint64_t* keys;     // [nb*128]
   uint64_t* scores;   // [nb*128]
-  float* values;      // [nb*128*dim]  HBM, or host-mapped pinned memory
+  float* values;      // rows [0, split): HBM, or host-mapped pinned memory
+  float* values_hi;   // rows [split, nb*128): host-mapped pinned memory, base
+                      // offset by -split rows (row p at values_hi + p*dim)
+  uint64_t split;     // first position whose row is in the second region
   uint32_t* occ;      // [nb]  occupied slots; slots [0, occ) are the occupied ones
   uint32_t* head;     // [nb]  inserter chain heads; all 0xFFFFFFFF between calls
   uint64_t* bmin;     // [2*nb] dual mode: lowest (score, key) of each full bucket

@@ -69,6 +69,15 @@ __device__ __forceinline__ uint32_t digest_of(uint64_t h) {
   return d == 0 ? 1u : d;
 }
 
+// Address of value row p. Rows are addressed by position (§3.6); positions
+// below t.split live in the first region (HBM, or all rows), the others in the
+// second (pinned host memory), whose base t.values_hi is offset by -split rows
+// so that both use the same arithmetic. split is a multiple of 128, so one
+// bucket's rows are contiguous in one region.
+__device__ __forceinline__ float* row_of(const TableView& t, uint64_t p) {
+  return (p < t.split ? t.values : t.values_hi) + p * t.dim;
+}
+
 // 0x80 in every byte of x that is zero, 0 in the others. Exact: the low seven
 // bits are summed separately so no carry crosses a byte.
 __device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
     if (lane == 0) found[i] = 0;
     return;
   }
-  copy_row<G, V4, NT>(out + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
+  copy_row<G, V4, NT>(out + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
   if (lane == 0) {
     found[i] = 1;
     if (scores_out) scores_out[i] = t.scores[p];
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void locate_kernel(TableView t, uint64_t n,
     if (i >= n) break;
     if (found) found[i] = p[j] >= 0 ? 1 : 0;
     if (ptrs_out)
-      ptrs_out[i] = p[j] >= 0 ? reinterpret_cast<uint64_t>(t.values + static_cast<uint64_t>(p[j]) * t.dim) : 0ull;
+      ptrs_out[i] = p[j] >= 0 ? reinterpret_cast<uint64_t>(row_of(t, static_cast<uint64_t>(p[j]))) : 0ull;
     if (scores_out && p[j] >= 0) scores_out[i] = t.scores[p[j]];
   }
 }
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(kBlock) void export_kernel(TableView t, uint64_t be
   keys_out[j] = t.keys[p];
   if (scores_out) scores_out[j] = t.scores[p];
   if (pos_out) pos_out[j] = p;
-  if (values_out) copy_row<1, V4, false>(values_out + j * t.dim, t.values + p * t.dim, t.dim, 0);
+  if (values_out) copy_row<1, V4, false>(values_out + j * t.dim, row_of(t, p), t.dim, 0);
 }
 
 // --------------------------------------------------------------- updaters --
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(TableView t, uint64_t n,
   const int64_t p = probe<G, DUAL, true>(t, keys[i], lane);
   if (p < 0) return;
   if (values)
-    copy_row<G, V4, true>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+    copy_row<G, V4, true>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
   if (scores && lane == 0) t.scores[p] = scores[i];
 }
 
@@ -547,7 +556,7 @@ __device__ __forceinline__ void own_write_score(Owned& o, const TableView& t, in
 template <bool V4>
 __device__ __forceinline__ void own_write_row(const Owned& o, const TableView& t, int s,
                                               const float* row, int lane) {
-  copy_row<kInsG, V4, true>(t.values + (static_cast<uint64_t>(o.b) * kSlots + s) * t.dim, row, t.dim,
+  copy_row<kInsG, V4, true>(row_of(t, static_cast<uint64_t>(o.b) * kSlots + s), row, t.dim,
                             lane);
 }
 
@@ -638,7 +647,7 @@ __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_
   if (in_regs) row_regs_load(rr, row, t.dim, lane);
   const uint64_t h = fmix64(k);
   const uint32_t d = digest_of(h);
-  float* const table_rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
+  float* const table_rows = row_of(t, static_cast<uint64_t>(o.b) * kSlots);
   auto write_row = [&](int s) {
     if (in_regs) {
       row_regs_store(rr, table_rows + static_cast<uint64_t>(s) * t.dim, t.dim, lane);
@@ -774,9 +783,9 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
   if (p >= 0) {
     if constexpr (FETCH) {
-      copy_row<G, V4, NT>(values + i * t.dim, t.values + static_cast<uint64_t>(p) * t.dim, t.dim, lane);
+      copy_row<G, V4, NT>(values + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
     } else {
-      copy_row<G, V4, NT>(t.values + static_cast<uint64_t>(p) * t.dim, values + i * t.dim, t.dim, lane);
+      copy_row<G, V4, NT>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
     }
     if (lane == 0) {
       t.scores[p] = scores[i];
@@ -877,7 +886,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
                                              const RowRegs& rr, const float* row, bool in_regs, bool fresh,
                                              const EvictStage& st, uint32_t idx, int lane) {
   const uint32_t d = digest_of(fmix64(k));
-  float* const rows = t.values + static_cast<uint64_t>(o.b) * kSlots * t.dim;
+  float* const rows = row_of(t, static_cast<uint64_t>(o.b) * kSlots);
   auto write_row = [&](int s) {
     if (in_regs) {
       row_regs_store(rr, rows + static_cast<uint64_t>(s) * t.dim, t.dim, lane);
@@ -1215,7 +1224,7 @@ __global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t
     const int vs = second ? v2 : v1;
     if (score > ms || (score == ms && k > mk)) {
       if (ev.keys)
-        emit_entry<V4>(ev, t, mk, ms, t.values + (static_cast<uint64_t>(o.b) * kSlots + vs) * t.dim, nullptr,
+        emit_entry<V4>(ev, t, mk, ms, row_of(t, static_cast<uint64_t>(o.b) * kSlots + vs), nullptr,
                        lane);
       own_write_slot(o, t, vs, k, d, score, lane);
       own_write_row<V4>(o, t, vs, row, lane);

@@ -128,7 +128,8 @@ class Profiler final : public hkv::KernelTimer {
 struct hkv_table {
   hkv_options opt{};
   hkv::TableView view{};
-  void* values_host = nullptr;  // hipHostMalloc base when values live in host memory
+  void* values_host = nullptr;  // hipHostMalloc base of the host-resident rows
+  float* values_dev = nullptr;  // hipMalloc base of the HBM-resident rows
   uint32_t* ws_next = nullptr;  // inserter workspace
   uint32_t* ws_target = nullptr;
   uint64_t ws_cap = 0;
@@ -157,11 +158,8 @@ void free_storage(hkv_table* t) {
   if (v.occ) (void)hipFree(v.occ);
   if (v.head) (void)hipFree(v.head);
   if (v.bmin) (void)hipFree(v.bmin);
-  if (t->values_host) {
-    (void)hipHostFree(t->values_host);
-  } else if (v.values) {
-    (void)hipFree(v.values);
-  }
+  if (t->values_host) (void)hipHostFree(t->values_host);
+  if (t->values_dev) (void)hipFree(t->values_dev);
   if (t->ws_next) (void)hipFree(t->ws_next);
   if (t->ws_target) (void)hipFree(t->ws_target);
   if (t->ev_kind) (void)hipFree(t->ev_kind);
@@ -387,26 +385,39 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (const char* g = std::getenv("HKV_GROUP_LANES")) v.lanes = static_cast<uint32_t>(std::atoi(g));
   v.keys_per_group = 2;
   if (const char* g = std::getenv("HKV_KEYS_PER_GROUP")) v.keys_per_group = static_cast<uint32_t>(std::atoi(g));
-  const uint64_t value_bytes = cap * o->dim * sizeof(float);
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
             hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&t->size_dev, 8) == hipSuccess &&
             (!o->dual_bucket || hipMalloc(&v.bmin, nb * 16) == hipSuccess) &&
             hipHostMalloc(&t->size_host, 8, hipHostMallocDefault) == hipSuccess;
+  // Value rows: the first `split` positions in HBM, the rest in pinned host
+  // memory mapped into the GPU (§3.6, §4.2 watermark); split is whole buckets.
+  const uint64_t row_bytes = static_cast<uint64_t>(o->dim) * sizeof(float);
+  uint64_t split = cap;
+  if (o->values_on_host) {
+    const uint64_t hbm_buckets = o->hbm_value_bytes / (kSlots * row_bytes);
+    split = hbm_buckets >= nb ? cap : hbm_buckets * kSlots;
+  }
+  v.split = split;
+  if (ok && split > 0) ok = hipMalloc(&t->values_dev, split * row_bytes) == hipSuccess;
+  float* host_dev = nullptr;
+  if (ok && split < cap)
+    ok = hipHostMalloc(&t->values_host, (cap - split) * row_bytes, hipHostMallocMapped) == hipSuccess &&
+         hipHostGetDevicePointer(reinterpret_cast<void**>(&host_dev), t->values_host, 0) == hipSuccess;
   if (ok) {
-    if (o->values_on_host) {
-      ok = hipHostMalloc(&t->values_host, value_bytes, hipHostMallocMapped) == hipSuccess &&
-           hipHostGetDevicePointer(reinterpret_cast<void**>(&v.values), t->values_host, 0) == hipSuccess;
-    } else {
-      ok = hipMalloc(&v.values, value_bytes) == hipSuccess;
-    }
+    v.values = split > 0 ? t->values_dev : host_dev;
+    // second-region base, offset so that row p sits at values_hi + p * dim
+    v.values_hi = split < cap ? reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(host_dev) -
+                                                         split * row_bytes)
+                              : v.values;
   }
   if (!ok) {
     (void)hipGetLastError();
     free_storage(t);
     delete t;
-    return fail(HKV_ENOMEM, "table storage for capacity %llu, dim %u (%s values)",
-                static_cast<unsigned long long>(cap), o->dim, o->values_on_host ? "host" : "device");
+    return fail(HKV_ENOMEM, "table storage for capacity %llu, dim %u (%llu rows in HBM, %llu on the host)",
+                static_cast<unsigned long long>(cap), o->dim, static_cast<unsigned long long>(split),
+                static_cast<unsigned long long>(cap - split));
   }
   e = hkv::launch_init(v, nullptr);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);

@@ -16,7 +16,9 @@
  *   - §4.1: the cache-specific calls find* (pointer-returning find),
  *     contains, insert_and_evict and find_or_insert.
  *   - §3.6 and §4.2: optional placement of value rows in pinned host memory
- *     mapped into the GPU address space, keys/digests/scores staying in HBM.
+ *     mapped into the GPU address space, keys/digests/scores staying in HBM,
+ *     with an HBM watermark: rows up to the budget stay in HBM, the rest
+ *     spill to host memory; a row's address follows from its position.
  *
  * Types: keys and scores are uint64_t, values are float32 rows of `dim`
  * elements stored row-major (n x dim for batches). A full table is the normal
@@ -77,15 +79,23 @@ typedef struct hkv_options {
   uint32_t dim;             /* float32 elements per value row, >= 1 */
   uint32_t bucket_slots;    /* must be 128 (or 0, meaning 128) */
   uint32_t dual_bucket;     /* 0: single-bucket (§3.2); 1: score-based dual-bucket (§3.4) */
-  uint32_t values_on_host;  /* 0: value rows in HBM; 1: in pinned, GPU-mapped host memory (§3.6) */
+  uint32_t values_on_host;  /* 0: value rows in HBM; 1: in pinned, GPU-mapped host memory (§3.6),
+                               except the first hbm_value_bytes' worth (§4.2 watermark) */
   int32_t device;           /* HIP device ordinal that owns the table */
   uint32_t flags;           /* HKV_FLAG_* */
+  uint64_t hbm_value_bytes; /* values_on_host == 1 only: HBM budget for value rows (the §4.2
+                               watermark). The rows of the first
+                               floor(hbm_value_bytes / (128 * 4 * dim)) buckets live in HBM,
+                               the rest in pinned host memory; 0 = all rows on the host,
+                               >= 4 * dim * capacity = all in HBM. Ignored when values_on_host
+                               == 0 (all rows in HBM). */
 } hkv_options;
 
 /*
  * hkv_create - allocate an empty table (§3.2 layout, §4.2 placement).
  * Storage per slot: key 8 B + score 8 B + digest 1 B in HBM (§5.1, memory
- * overhead), plus a value row of 4*dim bytes in HBM or in pinned host memory.
+ * overhead), plus a value row of 4*dim bytes in HBM or in pinned host memory
+ * (split at a bucket boundary by hbm_value_bytes, see hkv_options).
  * Every slot starts empty. The table owns all of its storage.
  * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128,
  * dim == 0, bucket_slots not 128, bad device), HKV_ENOMEM, HKV_EHIP.

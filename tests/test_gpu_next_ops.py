@@ -39,7 +39,7 @@ def fill(tab, o, C, D, seed, stream, lam=1.0, batch=1 << 12):
     return step, start
 
 
-def check_find_ptr(tab, o, q):
+def check_find_ptr(tab, o, q, split=None):
     n = q.numel()
     ptrs = torch.full((n,), -1, dtype=torch.int64, device=dev())
     found = torch.full((n,), 7, dtype=torch.uint8, device=dev())
@@ -64,8 +64,12 @@ def check_find_ptr(tab, o, q):
     hit = np.flatnonzero(f)
     gpos = np.array([where[int(x)] for x in qk[hit]], dtype=np.uint64)
     row = np.uint64(4 * tab.dim)
-    base = p[hit] - gpos * row
-    assert hit.size == 0 or np.all(base == base[0])
+    # with an HBM watermark, rows at and above `split` have a base of their own
+    cut = np.uint64(tab.capacity if split is None else split)
+    lo = gpos < cut
+    for m, first in ((lo, np.uint64(0)), (~lo, cut)):
+        base = p[hit][m] - (gpos[m] - first) * row
+        assert base.size == 0 or np.all(base == base[0])
     return p, hit, gpos, opos
 
 
@@ -332,3 +336,71 @@ def test_find_or_insert_odd_dim_and_reserved_keys():
     assert np.array_equal(found.cpu().numpy(), ofound)
     assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
     assert_same_contents(tab, o)
+
+
+# ------------------------------------------------ HBM watermark value split --
+
+def _memory_type(addr):
+    """hipPointerGetAttributes(...).type of a device-visible address: 1 host, 2 device."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    buf = (ctypes.c_int32 * 16)()
+    assert hip.hipPointerGetAttributes(buf, ctypes.c_void_p(int(addr))) == 0
+    return int(buf[0])
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_hbm_watermark_split_exact(dual):
+    """values_on_host with an HBM budget of 20 buckets' rows (plus change):
+    the first 20 buckets' rows are in HBM, the rest in pinned host memory.
+    Contents, find and find* must match the oracle exactly (single mode; dual
+    mode serial), and find* addresses must lie in device memory below the
+    split and in host memory above it."""
+    H = hkv()
+    B, D = 64, 8
+    C = B * SLOTS
+    budget = 20 * SLOTS * 4 * D + 100
+    split = 20 * SLOTS
+    tab = H.HashTable(C, D, dual_bucket=dual, values_on_host=True, hbm_value_bytes=budget, serial_insert=dual)
+    o = oracle.OracleTable(C, D, dual=dual)
+    fill(tab, o, C, D, 27, 1, batch=1500)
+    assert_same_contents(tab, o)
+    q = mixed_queries(o, 4000, 0.8, 7, 57)
+    from test_gpu_parity import check_find
+
+    check_find(tab, o, q)
+    p, hit, gpos, _ = check_find_ptr(tab, o, q, split=split)
+    lo, hi = hit[gpos < split], hit[gpos >= split]
+    assert lo.size > 100 and hi.size > 100
+    row = np.uint64(4 * D)
+    base_lo = p[lo] - gpos[gpos < split] * row
+    base_hi = p[hi] - (gpos[gpos >= split] - np.uint64(split)) * row
+    assert np.all(base_lo == base_lo[0]) and np.all(base_hi == base_hi[0])
+    assert _memory_type(p[lo][0]) == 2 and _memory_type(p[hi][0]) == 1
+    # updates and an eviction-heavy round go through the split too
+    k = gen.unique_keys(27, 9, 0, 2000, device=dev())
+    v = gen.values(k, 99, D)
+    sc = torch.full((2000,), 10 ** 6, dtype=torch.int64, device=dev())
+    got = evict_sets(*tab.insert_and_evict(k, v, sc))
+    want = oracle_evict_sets(o.insert_and_evict(np_u64(k), np_u64(sc), values=v.cpu().numpy()))
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+    assert_same_contents(tab, o)
+
+
+def test_hbm_watermark_extremes():
+    """Budget 0 keeps every row on the host, a budget of the whole table keeps
+    every row in HBM, values_on_host = 0 ignores the budget."""
+    H = hkv()
+    C, D = 8 * SLOTS, 4
+    for host, budget, want in ((True, 0, 1), (True, C * 4 * D, 2), (False, 123, 2)):
+        tab = H.HashTable(C, D, values_on_host=host, hbm_value_bytes=budget)
+        o = oracle.OracleTable(C, D)
+        fill(tab, o, C, D, 28, 1, batch=512)
+        assert_same_contents(tab, o)
+        k, _, _, _ = tab.export_batch(with_values=False)
+        ptrs, found = tab.find_ptr(k[:64])
+        torch.cuda.synchronize()
+        assert found.all()
+        assert {_memory_type(x) for x in ptrs.cpu().numpy().view(np.uint64).tolist()} == {want}
+        tab.close()
