@@ -68,6 +68,9 @@ def parse_args():
                    help="skip the find*/contains/insert_and_evict/find_or_insert measurements")
     p.add_argument("--capacity-sweep", default="", metavar="LOG2S",
                    help="only measure find on full tables of these capacities (e.g. 24,26,28) and exit")
+    p.add_argument("--mixed", default="", metavar="MIXES",
+                   help="concurrency ablation over these thread mixes, e.g. " + ",".join(MIXES))
+    p.add_argument("--mixed-batches", type=int, default=200, help="batches per thread in --mixed")
     p.add_argument("--hybrid", default="", metavar="FRACS",
                    help="value-placement sweep at these HBM fractions of the value rows, e.g. 1.0,0.5,0.0")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -270,6 +273,89 @@ def hybrid_sweep(args) -> None:
             r["find_ptr_retained"] = round(r["find_ptr"]["bkvs"] / base["find_ptr"]["bkvs"], 4)
     print(json.dumps({"hybrid": out, "capacity": cap, "dim": dim, "batch": batch, "hit_frac": args.hit_frac}),
           flush=True)
+
+
+MIXES = {
+    "1U": "U", "2U": "UU", "5U": "UUUUU", "10U": "UUUUUUUUUU",
+    "4F/5U/1I": "FFFFUUUUUI", "4F/2U/4I": "FFFFUUIIII", "8F/1U/1I": "FFFFFFFFUI",
+}
+
+
+def mixed_sweep(args) -> None:
+    """Concurrency ablation (the paper's §5.4): host threads share one table,
+    each issuing back-to-back batches of one role (F find, U assign,
+    I insert_or_assign) on its own stream through the native multi-threaded
+    driver; the table orders the calls either by the three groups (readers
+    with readers, updaters with updaters) or, with HKV_FLAG_RW_LOCK, as a
+    reader/writer lock (only readers overlap). Single-bucket table of
+    2^capacity_log2 slots at lambda 0.75, dim from --dim (16 in the paper's
+    runs), batches of 2^16 keys: finds and assigns of resident keys, inserts
+    of half resident, half new keys; --mixed-batches per thread, median of
+    three timed runs. value = keys of all threads / wall time. Prints one
+    JSON line."""
+    import ctypes
+
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+    from hash_table_cache_amd import build as hb
+
+    lib = ctypes.CDLL(str(hb.MIXED_LIB_PATH))
+    P = ctypes.c_void_p
+    lib.hkv_mixed_run.argtypes = [P, ctypes.c_uint32, P, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint32,
+                                  P, P, P, P, P, ctypes.POINTER(ctypes.c_double)]
+    lib.hkv_mixed_run.restype = ctypes.c_int32
+    dev = torch.device("cuda", 0)
+    cap, dim = 1 << args.capacity_log2, args.dim
+    batch, pool, nb = 1 << 16, 4, args.mixed_batches
+    out = {}
+    for mix in args.mixed.split(","):
+        roles = MIXES[mix]
+        res = {}
+        for mode in ("triple_group", "rw_lock"):
+            flags = H.HKV_FLAG_RW_LOCK if mode == "rw_lock" else 0
+            tab = H.HashTable(cap, dim, flags=flags)
+            fill_table(tab, 0.75, cap, 1 << 20, dim, SEED, 300, dev)
+            k_all, _, _, _ = tab.export_batch(with_values=False)
+            bufs, ptrs = [], {n: [] for n in ("keys", "values", "scores", "out", "found")}
+            for j, r in enumerate(roles):
+                pick = torch.argsort(gen.counter_words(SEED, 310 + j, 0, k_all.numel(), dev))[:pool * batch]
+                k = k_all[pick]
+                if r == "I":
+                    k = k.view(pool, batch)
+                    fresh = gen.unique_keys(SEED, 330 + j, 0, pool * batch // 2, device=dev).view(pool, -1)
+                    k = torch.cat([k[:, :batch // 2], fresh], 1).reshape(-1).contiguous()
+                v = gen.values(k, 900 + j, dim, SEED)
+                sc = torch.full((pool * batch,), 1 << 20, dtype=torch.int64, device=dev)
+                o = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+                f = torch.empty(batch, dtype=torch.uint8, device=dev)
+                bufs.append((k, v, sc, o, f))
+                for n, t in zip(("keys", "values", "scores", "out", "found"), (k, v, sc, o, f)):
+                    ptrs[n].append(t.data_ptr())
+            torch.cuda.synchronize()
+            arr = {n: (ctypes.c_void_p * len(roles))(*v) for n, v in ptrs.items()}
+            role_ids = (ctypes.c_int32 * len(roles))(*["FUI".index(r) for r in roles])
+            secs = ctypes.c_double(0)
+            # one short untimed pass, then three timed ones (median)
+            times = []
+            for timed_batches in (4, nb, nb, nb):
+                st = lib.hkv_mixed_run(tab.handle, len(roles), role_ids, timed_batches, batch, pool,
+                                       arr["keys"], arr["values"], arr["scores"], arr["out"], arr["found"],
+                                       ctypes.byref(secs))
+                if st != 0:
+                    raise RuntimeError(f"hkv_mixed_run status {st}")
+                times.append(secs.value)
+            t = sorted(times[1:])[1]
+            res[mode] = dict(seconds=round(t, 5), bkvs=round(len(roles) * nb * batch / t / 1e9, 3))
+            del bufs
+            tab.close()
+            torch.cuda.empty_cache()
+        res["ratio"] = round(res["triple_group"]["bkvs"] / res["rw_lock"]["bkvs"], 3)
+        log(f"mix {mix}: {res}")
+        out[mix] = res
+    print(json.dumps({"mixed": out, "capacity": cap, "dim": dim, "batch": batch, "batches_per_thread": nb,
+                      "lambda": 0.75}), flush=True)
 
 
 def fill_table(tab, lam, cap, batch, dim, seed, stream_id, device):
@@ -600,6 +686,9 @@ def main():
         return
     if args.hybrid:
         hybrid_sweep(args)
+        return
+    if args.mixed:
+        mixed_sweep(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()

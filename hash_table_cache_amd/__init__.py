@@ -14,6 +14,7 @@ from . import _native
 from ._native import (  # noqa: F401
     BUCKET_SLOTS,
     EMPTY_KEY,
+    HKV_FLAG_RW_LOCK,
     HKV_FLAG_SERIAL_INSERT,
     LOCKED_KEY,
     HkvError,
@@ -33,7 +34,8 @@ from ._native import (  # noqa: F401
     hkv_size,
 )
 
-__all__ = ["HashTable", "HkvError", "BUCKET_SLOTS", "EMPTY_KEY", "LOCKED_KEY", "HKV_FLAG_SERIAL_INSERT"]
+__all__ = ["HashTable", "HkvError", "BUCKET_SLOTS", "EMPTY_KEY", "LOCKED_KEY", "HKV_FLAG_SERIAL_INSERT",
+           "HKV_FLAG_RW_LOCK"]
 
 
 class HashTable:
@@ -43,17 +45,18 @@ class HashTable:
     dual_bucket: score-based dual-bucket mode; values_on_host: value rows in
     pinned host memory mapped into the GPU, except the first hbm_value_bytes'
     worth of buckets, which stay in HBM; serial_insert: apply inserts one key
-    at a time in input order (deterministic placement, slow).
+    at a time in input order (deterministic placement, slow); flags: further
+    HKV_FLAG_* bits (HKV_FLAG_RW_LOCK: reader/writer call ordering).
     """
 
     def __init__(self, capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
-                 device: int = 0, serial_insert: bool = False, hbm_value_bytes: int = 0):
+                 device: int = 0, serial_insert: bool = False, hbm_value_bytes: int = 0, flags: int = 0):
         self.capacity = int(capacity)
         self.dim = int(dim)
         self.dual_bucket = bool(dual_bucket)
         self.values_on_host = bool(values_on_host)
         self.device = int(device)
-        flags = HKV_FLAG_SERIAL_INSERT if serial_insert else 0
+        flags = int(flags) | (HKV_FLAG_SERIAL_INSERT if serial_insert else 0)
         self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags, hbm_value_bytes)
 
     def close(self) -> None:

@@ -18,6 +18,10 @@ BUILD_DIR = PKG / "_build"
 LIB_PATH = PKG / "_lib" / "libhkv.so"
 
 SOURCES = [CSRC / "hkv_kernels.hip", CSRC / "hkv_runtime.cpp"]
+# multi-threaded driver of the mixed reader/updater/inserter benchmark, a
+# library of its own on top of the C ABI
+MIXED_SOURCE = CSRC / "hkv_mixed_driver.cpp"
+MIXED_LIB_PATH = PKG / "_lib" / "libhkv_mixed.so"
 ARCH = "gfx950"
 
 
@@ -59,6 +63,14 @@ def build(verbose: bool = False) -> pathlib.Path:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     tmp.replace(LIB_PATH)
+    obj = BUILD_DIR / (MIXED_SOURCE.name + ".o")
+    cmd = [hipcc(), *compile_flags(), "-c", str(MIXED_SOURCE), "-o", str(obj)]
+    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+    tmp = MIXED_LIB_PATH.with_suffix(".so.tmp")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), str(obj),
+           f"-L{LIB_PATH.parent}", "-lhkv", "-Wl,-rpath,$ORIGIN", "-pthread"]
+    subprocess.run(cmd, check=True)
+    tmp.replace(MIXED_LIB_PATH)
     return LIB_PATH
 
 

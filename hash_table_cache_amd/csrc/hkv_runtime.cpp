@@ -32,7 +32,12 @@ constexpr uint32_t kMaxDim = 1u << 20;
 
 enum Group { kReader = 0, kUpdater = 1, kInserter = 2 };
 
-bool groups_conflict(int a, int b) { return !(a == b && a != kInserter); }
+// Table 4: readers overlap readers, updaters overlap updaters. Under the
+// reader/writer baseline only readers overlap.
+bool groups_conflict(int a, int b, bool rw_lock) {
+  if (rw_lock) return !(a == kReader && b == kReader);
+  return !(a == b && a != kInserter);
+}
 
 thread_local std::string g_error;
 
@@ -207,7 +212,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // that was issued on another stream. Caller holds t->mu.
 hkv_status order_before(hkv_table* t, int g, hipStream_t s) {
   for (int h = 0; h < 3; ++h) {
-    if (!groups_conflict(g, h)) continue;
+    if (!groups_conflict(g, h, (t->opt.flags & HKV_FLAG_RW_LOCK) != 0)) continue;
     for (auto& r : t->last[h]) {
       if (r.stream == s) continue;
       const hipError_t q = hipEventQuery(r.event);
@@ -354,7 +359,7 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (o->bucket_slots != 0 && o->bucket_slots != kSlots)
     return fail(HKV_EINVAL, "bucket_slots %u: only 128-slot buckets exist", o->bucket_slots);
   if (o->dual_bucket > 1 || o->values_on_host > 1) return fail(HKV_EINVAL, "dual_bucket/values_on_host must be 0 or 1");
-  if (o->flags & ~HKV_FLAG_SERIAL_INSERT) return fail(HKV_EINVAL, "unknown flags 0x%x", o->flags);
+  if (o->flags & ~(HKV_FLAG_SERIAL_INSERT | HKV_FLAG_RW_LOCK)) return fail(HKV_EINVAL, "unknown flags 0x%x", o->flags);
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
   if (e != hipSuccess || ndev == 0) {
@@ -419,8 +424,19 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
                 static_cast<unsigned long long>(cap), o->dim, static_cast<unsigned long long>(split),
                 static_cast<unsigned long long>(cap - split));
   }
-  e = hkv::launch_init(v, nullptr);
-  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  // Initialise on a private non-blocking stream: the legacy null stream
+  // would also synchronize with (and be checked against) every other stream
+  // of the process. A stale error of an earlier, unrelated call on this
+  // thread is cleared first so that it is not reported as the launch's.
+  (void)hipGetLastError();
+  hipStream_t init_stream = nullptr;
+  e = hipStreamCreateWithFlags(&init_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) {
+    e = hkv::launch_init(v, init_stream);
+    const hipError_t e2 = hipStreamSynchronize(init_stream);
+    if (e == hipSuccess) e = e2;
+    (void)hipStreamDestroy(init_stream);
+  }
   if (e != hipSuccess) {
     free_storage(t);
     delete t;

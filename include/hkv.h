@@ -73,6 +73,10 @@ typedef int32_t hkv_status;
  * group of lanes. Slow; gives run-to-run identical slot placement and, in
  * dual-bucket mode, exactly Algorithm 3's sequential decisions. */
 #define HKV_FLAG_SERIAL_INSERT 0x1u
+/* Conventional reader/writer ordering instead of the three groups (the
+ * baseline of the paper's concurrency ablation, §5.4): readers may overlap
+ * readers, every updater and inserter call is exclusive. */
+#define HKV_FLAG_RW_LOCK 0x2u
 
 typedef struct hkv_options {
   uint64_t capacity;        /* slots; a positive multiple of 128 (§3.2). B = capacity / 128 buckets */

@@ -404,3 +404,70 @@ def test_hbm_watermark_extremes():
         assert found.all()
         assert {_memory_type(x) for x in ptrs.cpu().numpy().view(np.uint64).tolist()} == {want}
         tab.close()
+
+
+# --------------------------------- concurrent reader/updater/inserter threads --
+
+@pytest.mark.parametrize("rw_lock", [False, True])
+def test_mixed_threads_keep_the_table_consistent(rw_lock):
+    """The native multi-threaded driver: 3 finders, 3 updaters and 2 inserters
+    on streams of their own, 30 batches each, on one table ordered by the
+    three groups (or the reader/writer baseline). Afterwards: no key twice,
+    at most 128 per bucket, every key in its own bucket, every row the
+    generated row of a version written for that key, every score one that
+    was written."""
+    import ctypes
+
+    from hash_table_cache_amd import build as hb
+
+    H = hkv()
+    C, D, batch, pool, nb = 64 * SLOTS, 8, 1024, 3, 30
+    tab = H.HashTable(C, D, flags=H.HKV_FLAG_RW_LOCK if rw_lock else 0)
+    o = oracle.OracleTable(C, D)
+    fill(tab, o, C, D, 29, 1, lam=0.75, batch=2048)
+    k_all, _, _, _ = tab.export_batch(with_values=False)
+    roles = "FFFUUUII"
+    bufs, ptrs = [], {n: [] for n in ("keys", "values", "scores", "out", "found")}
+    for j, r in enumerate(roles):
+        pick = torch.argsort(gen.counter_words(29, 40 + j, 0, k_all.numel(), dev()))[:pool * batch]
+        k = k_all[pick]
+        if r == "I":
+            fresh = gen.unique_keys(29, 60 + j, 0, pool * batch // 2, device=dev())
+            k = torch.cat([k[:pool * batch // 2], fresh]).contiguous()
+        ver = torch.full((pool * batch,), 1000 + j, dtype=torch.int64, device=dev())
+        v = gen.values(k, ver, D)
+        sc = torch.full((pool * batch,), 10 ** 6, dtype=torch.int64, device=dev())
+        o_, f_ = torch.empty((batch, D), device=dev()), torch.empty(batch, dtype=torch.uint8, device=dev())
+        bufs.append((k, v, sc, o_, f_))
+        for n, t in zip(("keys", "values", "scores", "out", "found"), (k, v, sc, o_, f_)):
+            ptrs[n].append(t.data_ptr())
+    torch.cuda.synchronize()
+    lib = ctypes.CDLL(str(hb.MIXED_LIB_PATH))
+    P = ctypes.c_void_p
+    lib.hkv_mixed_run.argtypes = [P, ctypes.c_uint32, P, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint32,
+                                  P, P, P, P, P, ctypes.POINTER(ctypes.c_double)]
+    arr = {n: (ctypes.c_void_p * len(roles))(*v) for n, v in ptrs.items()}
+    role_ids = (ctypes.c_int32 * len(roles))(*["FUI".index(r) for r in roles])
+    secs = ctypes.c_double(0)
+    st = lib.hkv_mixed_run(tab.handle, len(roles), role_ids, nb, batch, pool, arr["keys"], arr["values"],
+                           arr["scores"], arr["out"], arr["found"], ctypes.byref(secs))
+    assert st == 0 and secs.value > 0
+    gk, gv, gs, gp = tab.export_batch()
+    ku, pu = np_u64(gk), np_u64(gp)
+    assert np.unique(ku).size == ku.size and tab.size() == ku.size <= C
+    assert np.bincount((pu // SLOTS).astype(np.int64)).max() <= SLOTS
+    b1 = o.route(ku)[0]
+    assert np.array_equal(pu // SLOTS, b1)
+    # versions written: 1 (fill) or 1000 + j of the updater / inserter threads
+    kt = gk
+    ok = torch.zeros(ku.size, dtype=torch.bool, device=dev())
+    for ver in [None] + [1000 + j for j, r in enumerate(roles) if r != "F"]:
+        if ver is None:
+            cand = torch.stack([gen.values(kt, s, D) for s in range(1, 5)])  # fill steps
+            ok |= (cand == gv.unsqueeze(0)).all(-1).any(0)
+        else:
+            ok |= (gen.values(kt, torch.full_like(kt, ver), D) == gv).all(-1)
+    assert bool(ok.all())
+    # scores: the fill's step or the threads' 10^6
+    s_ = np_u64(gs)
+    assert np.all((s_ == 10 ** 6) | (s_ <= 4))

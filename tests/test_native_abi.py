@@ -40,6 +40,14 @@ def test_library_exports_every_declared_symbol():
     assert {n for n in exported if n.startswith("hkv")} == set(declared_functions())
 
 
+def test_mixed_driver_library_exports_its_entry_point():
+    from hash_table_cache_amd import build as hb
+
+    out = subprocess.run(["nm", "-D", "--defined-only", str(hb.MIXED_LIB_PATH)], check=True,
+                         capture_output=True, text=True).stdout
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == {"hkv_mixed_run"}
+
+
 def test_oracle_library_exports():
     import oracle
 
