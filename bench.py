@@ -8,10 +8,14 @@ insert_or_assign of 2^20 keys (90 % resident keys refreshed with new rows and
 the current step as score, 10 % new keys). Inputs are generated on the GPU
 before the timed region. value = keys processed by all calls / wall time.
 
-Every kernel launch in the timed region is timed with HIP events recorded
-on its stream by the library (hkv_profile_start/stop); the kernel with the
+The K timed steps issue nothing but the calls. They are followed by K more
+steps of the same workload in which every kernel launch is timed with a pair
+of HIP events that the kernel's own dispatch records (the library launches
+with hipExtLaunchKernelGGL while hkv_profile_start/stop is on; this adds
+about 6 % to a step, so it stays out of the value); the kernel with the
 largest total time is the dominant one and gets the roofline figure:
 algorithmic bytes per launch / average launch time, against 8 TB/s.
+Per-lambda call times are the table's kernel times per call.
 Algorithmic bytes per key (D = dim, h = hit fraction, f = resident fraction
 of an upsert batch, e = fraction of new keys that evict, i.e. land in a full
 bucket):
@@ -390,7 +394,9 @@ def run_gpu(args):
     batch = 1 << args.batch_log2
     dim = args.dim
     lams = [float(x) for x in args.lambdas.split(",")]
-    total_steps = args.warmup + args.steps
+    # warm-up, the timed steps (nothing but the calls), then as many again
+    # with kernel timing on (per-kernel times, roofline, per-lambda rates)
+    total_steps = args.warmup + 2 * args.steps
     tables = []
     for li, lam in enumerate(lams):
         t0 = time.perf_counter()
@@ -423,37 +429,37 @@ def run_gpu(args):
                            lam_start=size / cap))
     torch.cuda.synchronize()
 
-    ev = []
     total_keys = 0
 
     def one_step(s, timed):
-        # warm-up steps run exactly the same calls as timed ones
+        # warm-up steps run exactly the same calls as timed ones; nothing but
+        # the calls is queued (kernel times come from the dispatches' events)
         nonlocal total_keys
         for T in tables:
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record()
             T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"][s])
-            e1.record()
             if not args.find_only:
                 uk, sc = T["ups"][s]
                 T["tab"].insert_or_assign(uk, T["vals"][s % 2], sc)
-            e2.record()
             if timed:
-                ev.append((T["lam"], e0, e1, e2))
                 total_keys += batch * (1 if args.find_only else 2)
 
     for s in range(args.warmup):
         one_step(s, False)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, args.warmup + args.steps):
+        one_step(s, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     for T in tables:
         T["size0"] = T["tab"].size()
         T["tab"].profile_start()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        one_step(s, True)
+    t1 = time.perf_counter()
+    for s in range(args.warmup + args.steps, total_steps):
+        one_step(s, False)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_timed_kernels = time.perf_counter() - t1
     kstats = {}
     for T in tables:
         T["kernels"] = T["tab"].profile_stop()
@@ -462,31 +468,24 @@ def run_gpu(args):
             a[0] += cnt
             a[1] += tot
 
-    per_lam = {}
-    find_ms_all = []
-    for lam, e0, e1, e2 in ev:
-        d = per_lam.setdefault(lam, dict(find_ms=[], upsert_ms=[]))
-        f = e0.elapsed_time(e1)
-        d["find_ms"].append(f)
-        find_ms_all.append(f)
-        if not args.find_only:
-            d["upsert_ms"].append(e1.elapsed_time(e2))
     hit = {}
     for T in tables:
         hits = sum(int(f.sum().item()) for f in T["found"][args.warmup:])
-        hit[T["lam"]] = hits / (batch * args.steps)
+        hit[T["lam"]] = hits / (batch * 2 * args.steps)
         T["lam_end"] = T["tab"].size() / cap
     h_avg = sum(hit.values()) / len(hit)
+    # per-lambda call times: the table's kernel times per call (find: one
+    # kernel; insert_or_assign: probe + owner)
     detail = {}
-    for lam, d in per_lam.items():
-        fm = sorted(d["find_ms"])[len(d["find_ms"]) // 2]
-        e = dict(find_ms_median=round(fm, 4), find_bkvs=round(batch / fm / 1e6, 3), hit_rate=round(hit[lam], 4))
-        if d["upsert_ms"]:
-            um = sorted(d["upsert_ms"])[len(d["upsert_ms"]) // 2]
-            e.update(upsert_ms_median=round(um, 4), upsert_bkvs=round(batch / um / 1e6, 3))
-        T = next(t for t in tables if t["lam"] == lam)
+    for T in tables:
+        ks = T["kernels"]
+        fm = ks["find"][1] / ks["find"][0]
+        e = dict(find_ms=round(fm, 5), find_bkvs=round(batch / fm / 1e6, 3), hit_rate=round(hit[T["lam"]], 4))
+        if not args.find_only:
+            um = sum(ks[k][1] / ks[k][0] for k in ("upsert_probe", "upsert_owner"))
+            e.update(upsert_ms=round(um, 5), upsert_bkvs=round(batch / um / 1e6, 3))
         e.update(lambda_start=round(T["lam_start"], 4), lambda_end=round(T["lam_end"], 4))
-        detail[str(lam)] = e
+        detail[str(T["lam"])] = e
     fb = [v["find_bkvs"] for v in detail.values()]
     find_var = (max(fb) - min(fb)) / max(fb)
     # algorithmic bytes per launch of each kernel, averaged over the tables
@@ -538,9 +537,10 @@ def run_gpu(args):
     extra_ops = run_extra_ops(args, tables, batch, dim, hit) if args.extra_ops else None
     for T in tables:
         T["tab"].close()
+    busy = sum(v[1] for v in kstats.values())
     return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
-                dominant=dominant, h=h_avg, find_ms_events=sum(find_ms_all) / len(find_ms_all),
-                insert_new=insert_new, extra_ops=extra_ops)
+                dominant=dominant, h=h_avg, gpu_busy_frac=busy / (wall_timed_kernels * 1e3),
+                wall_timed_kernels=wall_timed_kernels, insert_new=insert_new, extra_ops=extra_ops)
 
 
 def run_extra_ops(args, tables, batch, dim, hit):
@@ -750,7 +750,8 @@ def main():
         },
         "detail": {
             "kernels": g["kernels"],
-            "find_call_ms_events": round(g["find_ms_events"], 5),
+            "kernel_timing_pass_ms_per_step": round(g["wall_timed_kernels"] / args.steps * 1e3, 4),
+            "gpu_busy_frac_kernel_timing_pass": round(g["gpu_busy_frac"], 4),
             "per_lambda": g["detail"],
             "find_lambda_variation": round(g["find_var"], 4),
             "insert_all_new_at_lambda_1": g["insert_new"],

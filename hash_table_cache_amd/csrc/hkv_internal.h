@@ -31,12 +31,13 @@ struct TableView {
   uint32_t keys_per_group;  // keys each group of the key-side probes serves (1, 2 or 4)
 };
 
-// Optional per-kernel timing: when a timer is passed, each launch is
-// bracketed by begin()/end() on the launch stream (the runtime records a
-// pair of hipEvents there).
+// Optional per-kernel timing: when a timer is passed, each kernel is launched
+// with hipExtLaunchKernelGGL and a start/stop event pair taken from the timer,
+// so the timestamps are written by the dispatch itself (no extra packets on
+// the stream); launched() hands the pair back with the kernel's name.
 struct KernelTimer {
-  virtual void begin(hipStream_t s) = 0;
-  virtual void end(hipStream_t s, const char* kernel) = 0;
+  virtual bool take(hipEvent_t* start, hipEvent_t* stop) = 0;
+  virtual void launched(const char* kernel, hipEvent_t start, hipEvent_t stop) = 0;
 
  protected:
   ~KernelTimer() = default;

@@ -31,6 +31,8 @@
 // Digest encoding: the digest of a key is bits 32..39 of its hash, except that
 // the value 0 is stored as 1; 0 marks an empty slot, so empty slots never
 // produce a candidate. This only affects the filter, never a result.
+#include <hip/hip_ext.h>
+
 #include "hkv_internal.h"
 
 namespace hkv {
@@ -1268,12 +1270,16 @@ int lanes_for(const TableView& t) {
   return 16;
 }
 
-// Launch with optional timing events around the kernel (on the same stream).
-#define HKV_LAUNCH(timer, name, kernel, grid, block, stream, ...)              \
-  do {                                                                          \
-    if (timer) (timer)->begin(stream);                                          \
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);            \
-    if (timer) (timer)->end(stream, name);                                      \
+// Launch, with the timer's event pair recorded by the dispatch when timing.
+#define HKV_LAUNCH(timer, name, kernel, grid, block, stream, ...)                          \
+  do {                                                                                      \
+    hipEvent_t hkv_e0_ = nullptr, hkv_e1_ = nullptr;                                        \
+    if ((timer) && (timer)->take(&hkv_e0_, &hkv_e1_)) {                                     \
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, hkv_e0_, hkv_e1_, 0, __VA_ARGS__); \
+      (timer)->launched(name, hkv_e0_, hkv_e1_);                                            \
+    } else {                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                      \
+    }                                                                                       \
   } while (0)
 
 template <int G, bool V4, bool DUAL>

@@ -78,8 +78,8 @@ class DeviceGuard {
   hipError_t err_;
 };
 
-// Per-kernel timing (hkv_profile_start/stop): a pair of events recorded on
-// the launch stream around every kernel launch while profiling is on.
+// Per-kernel timing (hkv_profile_start/stop): while profiling is on, every
+// kernel is launched with a start/stop event pair that its dispatch records.
 class Profiler final : public hkv::KernelTimer {
  public:
   struct Rec {
@@ -87,16 +87,17 @@ class Profiler final : public hkv::KernelTimer {
     hipEvent_t start;
     hipEvent_t stop;
   };
-  void begin(hipStream_t s) override {
-    pending_ = take();
-    if (pending_) (void)hipEventRecord(pending_, s);
+  bool take(hipEvent_t* start, hipEvent_t* stop) override {
+    *start = next_event();
+    *stop = *start ? next_event() : nullptr;
+    if (*start && !*stop) {
+      pool_.push_back(*start);
+      *start = nullptr;
+    }
+    return *start != nullptr;
   }
-  void end(hipStream_t s, const char* kernel) override {
-    hipEvent_t e = take();
-    if (!pending_ || !e) return;
-    (void)hipEventRecord(e, s);
-    recs_.push_back({kernel, pending_, e});
-    pending_ = nullptr;
+  void launched(const char* kernel, hipEvent_t start, hipEvent_t stop) override {
+    recs_.push_back({kernel, start, stop});
   }
   std::vector<Rec>& records() { return recs_; }
   void give_back(hipEvent_t e) { pool_.push_back(e); }
@@ -106,14 +107,12 @@ class Profiler final : public hkv::KernelTimer {
       (void)hipEventDestroy(r.stop);
     }
     for (auto e : pool_) (void)hipEventDestroy(e);
-    if (pending_) (void)hipEventDestroy(pending_);
     recs_.clear();
     pool_.clear();
-    pending_ = nullptr;
   }
 
  private:
-  hipEvent_t take() {
+  hipEvent_t next_event() {
     if (!pool_.empty()) {
       hipEvent_t e = pool_.back();
       pool_.pop_back();
@@ -125,7 +124,6 @@ class Profiler final : public hkv::KernelTimer {
   }
   std::vector<Rec> recs_;
   std::vector<hipEvent_t> pool_;
-  hipEvent_t pending_ = nullptr;
 };
 
 }  // namespace

@@ -255,9 +255,10 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
 
 /*
  * Kernel timing (tracing aid; not part of the paper's API).
- * While profiling is on, every kernel the table launches is bracketed by two
- * timing events recorded on the stream it is launched on; a record's time is
- * the elapsed time between them.
+ * While profiling is on, every kernel the table launches carries a start and
+ * a stop event that its own dispatch records (hipExtLaunchKernelGGL), so no
+ * extra work is queued on the stream; a record's time is the elapsed time
+ * between them.
  */
 typedef struct hkv_kernel_stat {
   char name[32];      /* find, find_ptr, contains, assign, upsert_probe, probe_fetch, upsert_owner,
