@@ -964,11 +964,10 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
   }
 }
 
-// Insert, second kernel: the group of each chain's first-pushed key
-// (next == kNoIdx) owns that bucket for the whole kernel. A 16-lane group
-// covers 16 consecutive keys: one coalesced load of their next / target /
-// key / score words and a ballot find the owners among them, which are then
-// served one after the other. An owner loads, in one round trip, the bucket's
+// Insert, second kernel: the first-pushed key of each chain (next ==
+// kNoIdx) owns that bucket for the whole kernel. A block lists the owners
+// among its 256 keys in LDS and deals them out to its 16-lane groups in turn.
+// An owner loads, in one round trip, the bucket's
 // digest line, the chain head, its key's row and - when the probe kernel saw
 // the bucket full - the scores and keys of all slots; it applies its own key,
 // then the chain from its head down to itself (Algorithm 2, each chain key
@@ -983,27 +982,33 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
                                                               const uint32_t* __restrict__ next,
                                                               const uint32_t* __restrict__ target,
                                                               EvictStage st) {
-  const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) & ~uint64_t(kInsG - 1);
+  // The block's owners (keys with next == kNoIdx) are listed in LDS and dealt
+  // out to its 16 groups in turn, so that every group serves about the same
+  // number of buckets.
+  __shared__ uint32_t s_idx[kBlock];
+  __shared__ uint32_t s_tgt[kBlock];
+  __shared__ uint64_t s_key[kBlock];
+  __shared__ uint64_t s_score[kBlock];
+  __shared__ uint32_t s_count;
+  const uint64_t mine = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
-  if (first >= n) return;
-  const uint64_t mine = first + lane;
-  uint32_t my_next = kSkipIdx, my_tgt = 0;
-  uint64_t my_key = 0, my_score = 0;
-  if (mine < n) {
-    my_next = next[mine];
-    my_tgt = target[mine];
-    my_key = keys[mine];
-    my_score = scores[mine];
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  if (mine < n && next[mine] == kNoIdx) {
+    const uint32_t e = atomicAdd(&s_count, 1u);
+    s_idx[e] = static_cast<uint32_t>(mine);
+    s_tgt[e] = target[mine];
+    s_key[e] = keys[mine];
+    s_score[e] = scores[mine];
   }
-  uint64_t todo = group_bits<kInsG>(__ballot(my_next == kNoIdx));
+  __syncthreads();
+  const uint32_t owners = s_count;
   const bool in_regs = V4 && t.dim <= 8 * kInsG;
-  while (todo) {
-    const int src = __ffsll(static_cast<unsigned long long>(todo)) - 1;
-    todo &= todo - 1;
-    const uint32_t i = static_cast<uint32_t>(first + src);
-    const uint32_t tgt = __shfl(my_tgt, src, kInsG);
-    const uint64_t k = __shfl(my_key, src, kInsG);
-    const uint64_t score = __shfl(my_score, src, kInsG);
+  for (uint32_t e = threadIdx.x / kInsG; e < owners; e += kBlock / kInsG) {
+    const uint32_t i = s_idx[e];
+    const uint32_t tgt = s_tgt[e];
+    const uint64_t k = s_key[e];
+    const uint64_t score = s_score[e];
     Bucket o;
     o.b = tgt & ~kFullBit;
     o.cols = false;
