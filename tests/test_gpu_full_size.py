@@ -398,3 +398,113 @@ def test_mixed_reader_updater_inserter_at_full_size():
     log("mixed: " + ", ".join(f"{op} {n[op] * steps / ms / 1e6:.3f} B-KV/s" for op, ms in times.items())
         + f"; step {sum(times.values()) / steps:.3f} ms, {(1 << 20) * 1.75 * steps / sum(times.values()) / 1e6:.3f} B-KV/s")
     tab.close()
+
+
+def test_other_calls_at_full_size():
+    """find*, contains, insert_and_evict and find_or_insert on a full 2^26-slot
+    dim-64 single-bucket table (the benchmark's tables and batch size). find*:
+    found iff exported, address = value base + exported position * row size,
+    score = last write. insert_and_evict (90 % resident, 10 % new, higher
+    score): the hand-back is exactly (resident before ∪ offered) − resident
+    after, each entry with the row and score of its last write.
+    find_or_insert (90 % resident, 10 % new): found iff resident before, hits
+    return the stored row, misses keep theirs; afterwards every resident key
+    carries its last written score."""
+    H = hkv()
+    cap, D, batch = 1 << 26, 64, 1 << 20
+    seed = 0x484B56000000BB00
+    tab = H.HashTable(cap, D)
+    cursor, step = 0, 0
+    parts = []
+    while tab.size() < cap:
+        step += 1
+        k = gen.unique_keys(seed, 1, cursor, batch, device=dev())
+        tab.insert_or_assign(k, gen.values(k, step, D), torch.full((batch,), step, dtype=torch.int64, device=dev()))
+        parts.append((batch, step))
+        cursor += batch
+    allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
+    alls = torch.cat([torch.full((n,), st, dtype=torch.int64, device=dev()) for n, st in parts])
+    order = torch.argsort(allk)
+    sk, ss = allk[order], alls[order].clone()  # last written score (= row version) of every key seen
+
+    def last(keys):
+        return ss[torch.searchsorted(sk, keys)]
+
+    k, _, s, p = export_all(tab)
+    check_invariants(tab, k, p, cap)
+    ko = torch.argsort(k)
+    rk, rp = k[ko], p[ko]  # resident keys sorted, with their positions
+    assert torch.equal(s, last(k))
+    log(f"other calls: table full after {step} batches")
+
+    # find* and contains
+    rng = torch.Generator(device="cpu").manual_seed(11)
+    hits = rk[torch.randperm(rk.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
+    q = gen.shuffle(torch.cat([hits, gen.unique_keys(seed, 7, 0, batch - hits.numel(), device=dev())]), seed, 3)
+    ptrs = torch.full((batch,), -1, dtype=torch.int64, device=dev())
+    found = torch.empty(batch, dtype=torch.uint8, device=dev())
+    scores = torch.full((batch,), 0x5EED, dtype=torch.int64, device=dev())
+    tab.find_ptr(q, ptrs_out=ptrs, found_out=found, scores_out=scores)
+    cont = tab.contains(q)
+    torch.cuda.synchronize()
+    idx = torch.clamp(torch.searchsorted(rk, q), max=rk.numel() - 1)
+    expect = rk[idx] == q
+    assert torch.equal(found.bool(), expect) and torch.equal(cont.bool(), expect)
+    assert bool((ptrs[~expect] == 0).all()) and bool((scores[~expect] == 0x5EED).all())
+    assert torch.equal(scores[expect], last(q[expect]))
+    base = ptrs[expect] - rp[idx[expect]] * (4 * D)
+    assert bool((base == base[0]).all())
+    log("other calls: find* and contains exact")
+
+    # insert_and_evict: resident keys re-written with a higher score, new keys
+    step += 1
+    pre = rk
+    res = rk[torch.randperm(rk.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
+    new = gen.unique_keys(seed, 1, cursor, batch - res.numel(), device=dev())
+    cursor += new.numel()
+    uk = gen.shuffle(torch.cat([res, new]), seed, 4)
+    ek, ev, es, cnt = tab.insert_and_evict(uk, gen.values(uk, step, D),
+                                           torch.full((batch,), step, dtype=torch.int64, device=dev()))
+    torch.cuda.synchronize()
+    m = int(cnt.item())
+    allk = torch.cat([sk, new])
+    alls = torch.cat([ss, torch.full((new.numel(),), step, dtype=torch.int64, device=dev())])
+    order = torch.argsort(allk)
+    sk, ss = allk[order], alls[order].clone()
+    ss[torch.searchsorted(sk, res)] = step
+    k2, _, s2, p2 = export_all(tab)
+    check_invariants(tab, k2, p2, cap)
+    assert torch.equal(s2, last(k2))
+    post = torch.sort(k2).values
+    union = torch.unique(torch.cat([pre, uk]))
+    gone = union[~torch.isin(union, post)]
+    out = torch.sort(ek[:m]).values
+    assert m == gone.numel() and torch.equal(out, gone)
+    assert torch.equal(es[:m], last(ek[:m]))
+    assert torch.equal(ev[:m].view(torch.int32), gen.values(ek[:m], es[:m], D).view(torch.int32))
+    log(f"other calls: insert_and_evict handed back {m} entries, exact")
+
+    # find_or_insert
+    step += 1
+    rk2 = post
+    res = rk2[torch.randperm(rk2.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
+    new = gen.unique_keys(seed, 1, cursor, batch - res.numel(), device=dev())
+    uk = gen.shuffle(torch.cat([res, new]), seed, 5)
+    rows = gen.values(uk, step, D)
+    offered = rows.clone()
+    _, fnd = tab.find_or_insert(uk, rows, torch.full((batch,), step, dtype=torch.int64, device=dev()))
+    torch.cuda.synchronize()
+    was = torch.isin(uk, rk2)
+    assert torch.equal(fnd.bool(), was)
+    assert torch.equal(rows[was].view(torch.int32), gen.values(uk[was], last(uk[was]), D).view(torch.int32))
+    assert torch.equal(rows[~was], offered[~was])
+    allk = torch.cat([sk, new])
+    alls = torch.cat([ss, torch.full((new.numel(),), step, dtype=torch.int64, device=dev())])
+    order = torch.argsort(allk)
+    sk, ss = allk[order], alls[order].clone()
+    ss[torch.searchsorted(sk, res)] = step  # hits take the offered score
+    k3, v3, s3, p3 = export_all(tab, with_values=False)
+    check_invariants(tab, k3, p3, cap)
+    assert torch.equal(s3, last(k3))
+    log("other calls: find_or_insert exact")
+    tab.close()
