@@ -75,6 +75,8 @@ def parse_args():
     p.add_argument("--mixed", default="", metavar="MIXES",
                    help="concurrency ablation over these thread mixes, e.g. " + ",".join(MIXES))
     p.add_argument("--mixed-batches", type=int, default=200, help="batches per thread in --mixed")
+    p.add_argument("--tiered", action="store_true",
+                   help="the tiered-values workload (use with --capacity-log2 28 --dim 128)")
     p.add_argument("--hybrid", default="", metavar="FRACS",
                    help="value-placement sweep at these HBM fractions of the value rows, e.g. 1.0,0.5,0.0")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -277,6 +279,86 @@ def hybrid_sweep(args) -> None:
             r["find_ptr_retained"] = round(r["find_ptr"]["bkvs"] / base["find_ptr"]["bkvs"], 4)
     print(json.dumps({"hybrid": out, "capacity": cap, "dim": dim, "batch": batch, "hit_frac": args.hit_frac}),
           flush=True)
+
+
+def tiered_run(args) -> None:
+    """The tiered-values workload: dual-bucket table of 2^capacity_log2 slots
+    (2^28 in the paper's largest configuration) with dim --dim rows (128) in
+    pinned, GPU-mapped host memory. Warm cache: ranks 1 .. capacity * 17/16
+    inserted coldest first in 2^19-key batches, score = batch (LRU). Each step:
+    find 2^20 Zipf(1.2) draws over 2^32 ids (key = rank, not deduplicated),
+    then insert_or_assign of 2^19 draws (deduplicated), score = step;
+    --warmup + --steps steps, kernel times from the library's events. Prints
+    one JSON line: rates per call, hit rate, key-side HBM bytes/s of find and
+    the rate at which it delivers rows (a hot key's row counted at each of
+    its draws), distinct keys per batch."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap, dim = 1 << args.capacity_log2, args.dim
+    row = 4 * dim
+    t0 = time.perf_counter()
+    tab = H.HashTable(cap, dim, dual_bucket=True, values_on_host=True)
+    step = 0
+    hi = cap + cap // 16
+    while hi > 0:
+        step += 1
+        lo = max(1, hi - (1 << 19) + 1)
+        k = torch.arange(hi, lo - 1, -1, dtype=torch.int64, device=dev)
+        hi = lo - 1
+        tab.insert_or_assign(k, gen.values(k, step, dim, SEED), torch.full((k.numel(),), step, dtype=torch.int64,
+                                                                          device=dev))
+    torch.cuda.synchronize()
+    log(f"tiered: warm table size {tab.size()} after {step} batches, {time.perf_counter() - t0:.1f}s")
+    zipf = gen.Zipf(1.2, 1 << 32)
+    nsteps = args.warmup + args.steps
+    finds = [zipf.draw(SEED, 1, j * (1 << 20), 1 << 20, device=dev) for j in range(nsteps)]
+    ups = []
+    for j in range(nsteps):
+        u = torch.unique(zipf.draw(SEED, 2, j * (1 << 19), 1 << 19, device=dev))
+        ups.append((u, gen.values(u, step + 1 + j, dim, SEED),
+                    torch.full((u.numel(),), step + 1 + j, dtype=torch.int64, device=dev)))
+    out = torch.empty((1 << 20, dim), dtype=torch.float32, device=dev)
+    found = [torch.empty(1 << 20, dtype=torch.uint8, device=dev) for _ in range(nsteps)]
+    torch.cuda.synchronize()
+    for j in range(args.warmup):
+        tab.find(finds[j], values_out=out, found_out=found[j])
+        tab.insert_or_assign(*ups[j])
+    torch.cuda.synchronize()
+    tab.profile_start()
+    t1 = time.perf_counter()
+    keys = 0
+    for j in range(args.warmup, nsteps):
+        tab.find(finds[j], values_out=out, found_out=found[j])
+        tab.insert_or_assign(*ups[j])
+        keys += finds[j].numel() + ups[j][0].numel()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    ks = tab.profile_stop()
+    hits = sum(int(f.sum()) for f in found[args.warmup:]) / (args.steps * (1 << 20))
+    find_ms = ks["find"][1] / ks["find"][0]
+    up_ms = sum(ks[n][1] / ks[n][0] for n in ("upsert_probe", "upsert_owner"))
+    up_keys = sum(u[0].numel() for u in ups[args.warmup:]) / args.steps
+    key_side = 8 + 2 * 128 + 2 * 4 + hits * 8 + 1  # key, two digest lines, false positives, key, flag
+    res = dict(
+        workload=(f"tiered values: dual bucket, capacity 2^{args.capacity_log2}, dim {dim} rows in pinned host "
+                  f"memory; per step find 2^20 Zipf(1.2) draws + insert_or_assign of 2^19 draws deduplicated"),
+        combined_bkvs=round(keys / wall / 1e9, 4), find_bkvs=round((1 << 20) / find_ms / 1e6, 4),
+        upsert_bkvs=round(up_keys / up_ms / 1e6, 4), hit_rate=round(hits, 4),
+        find_kernel_ms=round(find_ms, 4), upsert_kernels_ms=round(up_ms, 4),
+        find_key_side_hbm_GBps=round((1 << 20) * (key_side + hits * row) / (find_ms * 1e-3) / 1e9, 1),
+        # rows delivered by find, repeats of hot keys counted each time
+        find_row_GBps=round((1 << 20) * hits * row / (find_ms * 1e-3) / 1e9, 1),
+        find_distinct_keys_per_batch=int(sum(torch.unique(f).numel() for f in finds[args.warmup:]) / args.steps),
+        upsert_distinct_keys_per_batch=int(up_keys),
+        upsert_row_write_GBps=round(up_keys * row / (ks["upsert_probe"][1] / ks["upsert_probe"][0] * 1e-3) / 1e9, 1),
+        kernels={n: round(v[1] / v[0], 4) for n, v in ks.items()}, size=tab.size(), capacity=cap)
+    log(f"tiered: {res}")
+    tab.close()
+    print(json.dumps({"tiered": res}), flush=True)
 
 
 MIXES = {
@@ -689,6 +771,9 @@ def main():
         return
     if args.mixed:
         mixed_sweep(args)
+        return
+    if args.tiered:
+        tiered_run(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()

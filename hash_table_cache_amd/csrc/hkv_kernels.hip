@@ -354,7 +354,13 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
     if (lane == 0) found[i] = 0;
     return;
   }
-  copy_row<G, V4, NT>(out + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+  // Host-resident rows are read with cacheable loads: repeated (hot) keys of
+  // a batch then find their rows in L2 instead of crossing the host link again.
+  if (static_cast<uint64_t>(p) >= t.split) {
+    copy_row<G, V4, false>(out + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+  } else {
+    copy_row<G, V4, NT>(out + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+  }
   if (lane == 0) {
     found[i] = 1;
     if (scores_out) scores_out[i] = t.scores[p];
@@ -785,7 +791,12 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
   if (p >= 0) {
     if constexpr (FETCH) {
-      copy_row<G, V4, NT>(values + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+      // (host-resident rows: cacheable loads, as in find)
+      if (static_cast<uint64_t>(p) >= t.split) {
+        copy_row<G, V4, false>(values + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+      } else {
+        copy_row<G, V4, NT>(values + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
+      }
     } else {
       copy_row<G, V4, NT>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
     }

@@ -471,3 +471,36 @@ def test_mixed_threads_keep_the_table_consistent(rw_lock):
     # scores: the fill's step or the threads' 10^6
     s_ = np_u64(gs)
     assert np.all((s_ == 10 ** 6) | (s_ <= 4))
+
+
+@pytest.mark.parametrize("budget_buckets", [0, 8])
+def test_host_rows_read_again_after_updates(budget_buckets):
+    """Rows on the host are read with cacheable loads. Hot keys are found many
+    times in one batch, then rewritten by assign, insert_or_assign and
+    find_or_insert between finds; every find must return the newest rows."""
+    H = hkv()
+    C, D = 32 * SLOTS, 16
+    tab = H.HashTable(C, D, values_on_host=True, hbm_value_bytes=budget_buckets * SLOTS * 4 * D)
+    o = oracle.OracleTable(C, D)
+    fill(tab, o, C, D, 31, 1, batch=1024)
+    from test_gpu_parity import check_find
+
+    hot = sample_present(o, 64, 3)
+    q = to_dev(np.repeat(hot, 64))  # every hot key 64 times in one batch
+    for r in range(4):
+        check_find(tab, o, q)
+        v = gen.values(to_dev(hot), 500 + r, D)
+        sc = torch.full((hot.size,), 100 + r, dtype=torch.int64, device=dev())
+        if r % 3 == 0:
+            tab.assign(to_dev(hot), v, sc)
+            o.assign(hot, values=v.cpu().numpy(), scores=np_u64(sc))
+        elif r % 3 == 1:
+            tab.insert_or_assign(to_dev(hot), v, sc)
+            o.insert_or_assign(hot, np_u64(sc), values=v.cpu().numpy())
+        else:
+            rows, _ = tab.find_or_insert(to_dev(hot), v.clone(), sc)
+            orows, _ = o.find_or_insert(hot, np_u64(sc), values=v.cpu().numpy())
+            torch.cuda.synchronize()
+            assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+    check_find(tab, o, q)
+    assert_same_contents(tab, o)
