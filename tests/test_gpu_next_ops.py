@@ -504,3 +504,73 @@ def test_host_rows_read_again_after_updates(budget_buckets):
             assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
     check_find(tab, o, q)
     assert_same_contents(tab, o)
+
+
+@pytest.mark.parametrize("D", [1, 5, 33])
+def test_insert_and_evict_and_find_or_insert_odd_dims(D):
+    """Rows that are not a whole number of 16-byte pieces take the scalar copy
+    paths of the staging, compaction and fetch kernels."""
+    H = hkv()
+    C = 16 * SLOTS
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    step, _ = fill(tab, o, C, D, 32, 1, batch=1000)
+    for t in range(3):
+        step += 1
+        fresh = gen.unique_keys(32, 2 + t, 0, 700).numpy().view(np.uint64)
+        k = np.random.default_rng(t).permutation(np.concatenate([fresh, sample_present(o, 500, 70 + t)]))
+        kt = to_dev(k)
+        v = gen.values(kt, 300 + step, D)
+        sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+        if t % 2 == 0:
+            got = evict_sets(*tab.insert_and_evict(kt, v, sc))
+            want = oracle_evict_sets(o.insert_and_evict(k, np_u64(sc), values=v.cpu().numpy()))
+            assert got[0].size > 0 and np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+            assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        else:
+            v0 = v.cpu().numpy()
+            rows, found = tab.find_or_insert(kt, v, sc)
+            orows, ofound = o.find_or_insert(k, np_u64(sc), values=v0)
+            torch.cuda.synchronize()
+            assert np.array_equal(found.cpu().numpy(), ofound)
+            assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        assert_same_contents(tab, o)
+
+
+def test_find_or_insert_dual_parallel_invariants():
+    """Dual-bucket parallel find_or_insert under a Zipf stream: found iff the
+    key was resident before, hits return the row of the key's last write,
+    and the table keeps its invariants (no key twice, every entry in a
+    candidate bucket, rows and scores of the last write)."""
+    H = hkv()
+    C, D = 1 << 13, 4
+    tab = H.HashTable(C, D, dual_bucket=True)
+    o = oracle.OracleTable(C, D, dual=True)
+    z = gen.Zipf(1.1, 1 << 16)
+    last = {}
+    for b in range(12):
+        keys = np.unique(z.draw(79, 1, b * 2048, 2048).numpy()).astype(np.uint64)
+        kt = to_dev(keys)
+        sc = torch.full((keys.size,), b + 1, dtype=torch.int64, device=dev())
+        rows = gen.values(kt, sc, D)
+        offered = rows.clone()
+        gk, _, _, _ = tab.export_batch(with_values=False)
+        before = set(np_u64(gk).tolist())
+        rows, found = tab.find_or_insert(kt, rows, sc)
+        torch.cuda.synchronize()
+        f = found.cpu().numpy().astype(bool)
+        assert np.array_equal(f, np.array([x in before for x in keys.tolist()]))
+        hv = torch.tensor([last[x] for x in keys[f].tolist()], dtype=torch.int64)
+        assert torch.equal(rows[torch.from_numpy(f).to(dev())].cpu(), gen.values(kt[torch.from_numpy(f).to(dev())].cpu(), hv, D))
+        assert torch.equal(rows[torch.from_numpy(~f).to(dev())], offered[torch.from_numpy(~f).to(dev())])
+        for x, hit in zip(keys.tolist(), f.tolist()):
+            if not hit:
+                last[x] = b + 1  # inserted rows are version b + 1; hits keep their row version
+        gk, gv, gs, gp = tab.export_batch()
+        ku, pu = np_u64(gk), np_u64(gp)
+        assert np.unique(ku).size == ku.size and tab.size() == ku.size <= C
+        b1, b2, _ = o.route(ku)
+        assert np.all((pu // SLOTS == b1) | (pu // SLOTS == b2))
+        ver = torch.tensor([last[x] for x in ku.tolist()], dtype=torch.int64, device=dev())
+        assert torch.equal(gv, gen.values(gk, ver, D))
+        assert np.all(np_u64(gs) >= 1)
