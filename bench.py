@@ -89,23 +89,34 @@ KERNEL_SOURCE = os.path.join(ROOT, "hash_table_cache_amd", "csrc", "hkv_kernels.
 PROFILE_NAMES = {"find": "find_kernel", "upsert_probe": "upsert_probe_kernel", "upsert_owner": "upsert_owner_kernel"}
 
 
+def kernel_code_sha256() -> str:
+    """sha256 of the kernel source with comments and white space removed: a
+    profile stays valid across comment edits, not across code changes."""
+    import hashlib
+    import re
+
+    src = open(KERNEL_SOURCE, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return hashlib.sha256("".join(src.split()).encode()).hexdigest()
+
+
 def profiled_traffic(kernel: str, dim: int, capacity_log2: int):
     """HBM bytes per launch of `kernel` from a committed rocprofv3 summary of
-    this workload, or None when no summary matches the current kernel source."""
+    this workload, or None when no summary matches the current kernel code."""
     import glob
-    import hashlib
 
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    sha = kernel_code_sha256()
     for path in sorted(glob.glob(os.path.join(PROFILE_DIR, "*.txt"))):
         fields = {}
         traffic = {}
         for line in open(path):
             parts = line.split()
-            if len(parts) == 2 and parts[0] in ("kernel_source_sha256", "workload_dim", "workload_capacity_log2"):
+            if len(parts) == 2 and parts[0] in ("kernel_code_sha256", "workload_dim", "workload_capacity_log2"):
                 fields[parts[0]] = parts[1]
             elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
                 traffic[parts[1]] = int(parts[2])
-        if (fields.get("kernel_source_sha256") == sha and fields.get("workload_dim") == str(dim)
+        if (fields.get("kernel_code_sha256") == sha and fields.get("workload_dim") == str(dim)
                 and fields.get("workload_capacity_log2") == str(capacity_log2)
                 and PROFILE_NAMES.get(kernel) in traffic):
             return traffic[PROFILE_NAMES[kernel]]

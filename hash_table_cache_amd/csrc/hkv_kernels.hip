@@ -8,6 +8,11 @@
 //   insert    - §3.3, Algorithm 2 (update / empty slot / evict-or-reject);
 //               §3.4, Algorithm 3 (dual-bucket D1/D2 selection)
 //   size, export - §3.5 readers, §4.1 export
+//   find*, contains, insert_and_evict, find_or_insert - §4.1: the key-side
+//               probe alone; the inserter with a hand-back of what leaves; the
+//               inserter with stored rows copied out for resident keys
+//   value rows - §3.6 / §4.2: addressed by position, split between HBM and
+//               pinned host memory at a bucket boundary (the HBM watermark)
 //
 // Work decomposition (wave64, CDNA4):
 //   * A "group" of G consecutive lanes of a wave serves one key. Lane l of a
@@ -19,8 +24,8 @@
 //   * Inserts need every bucket to see its keys one at a time (serializable
 //     per bucket). Instead of spin locks, a link kernel threads the batch's
 //     keys into one chain per target bucket with a single atomic exchange per
-//     key; in the second kernel the group of the chain's last element owns
-//     the bucket exclusively and applies the chain's keys one after another.
+//     key; in the second kernel the chain's first-pushed key owns the bucket
+//     exclusively and its group applies the chain's keys one after another.
 //     No two groups ever write the same bucket inside a kernel, so no lock,
 //     CAS retry or cross-XCD cache maintenance is needed; kernel boundaries
 //     publish the result.
