@@ -112,7 +112,7 @@ def profiled_traffic(kernel: str, dim: int, capacity_log2: int):
         traffic = {}
         for line in open(path):
             parts = line.split()
-            if len(parts) == 2 and parts[0] in ("kernel_code_sha256", "workload_dim", "workload_capacity_log2"):
+            if len(parts) >= 2 and parts[0] in ("kernel_code_sha256", "workload_dim", "workload_capacity_log2"):
                 fields[parts[0]] = parts[1]
             elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
                 traffic[parts[1]] = int(parts[2])
