@@ -135,6 +135,10 @@ def owner_bytes_per_key(dim: int, f: float, e: float) -> float:
     return 4 + (1 - f) * (8 + 8 + 4 * dim + 4 + 4 + 128 + 4 + 8 + 1 + 8 + 4 * dim + e * (1024 + 8))
 
 
+def batch_size(args) -> int:
+    return 1 << args.batch_log2
+
+
 def locate_bytes_per_key(h: float, with_ptr: bool) -> float:
     """find* / contains: 8 key + 128 digest line + 4 false-positive keys
     + h 8 key + 1 found flag (+ 8 address for find*)."""
@@ -160,6 +164,24 @@ def copy_bandwidth(mib: int = 2048, reps: int = 10) -> float:
     del a, b
     torch.cuda.empty_cache()
     return gbs
+
+
+def pattern_ceiling():
+    """Runs the access-pattern ceiling program (find's memory accesses on a
+    2^26-slot dim-64 table without its arithmetic, with and without the chain
+    of dependent loads) in a child process; returns its JSON or None."""
+    import subprocess
+
+    from hash_table_cache_amd import build as hb
+
+    if not hb.PATTERN_EXE.exists():
+        return None
+    try:
+        r = subprocess.run([str(hb.PATTERN_EXE)], capture_output=True, text=True, timeout=120, check=True)
+        return json.loads(r.stdout)
+    except (subprocess.SubprocessError, ValueError) as e:
+        log(f"pattern ceiling program failed: {e}")
+        return None
 
 
 def calibrate_copy(mib: int) -> None:
@@ -789,6 +811,7 @@ def main():
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()
     log(f"device copy bandwidth {g['copy_GBps']:.1f} GB/s")
+    g["pattern"] = pattern_ceiling() if args.dim == 64 and args.capacity_log2 == 26 else None
     cpu = None
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline")
@@ -853,6 +876,10 @@ def main():
             "insert_all_new_at_lambda_1": g["insert_new"],
             "other_calls_per_lambda": g["extra_ops"],
             "copy_GBps": round(g["copy_GBps"], 1),
+            "find_pattern_ceiling": g["pattern"],
+            "find_frac_of_pattern_ceiling": (round(g["pattern"]["dependent_chain"]["us_per_2p20_keys"] * 1e-3
+                                                  * batch_size(args) / (1 << 20) / g["kernels"]["find"]["avg_ms"], 4)
+                                             if g["pattern"] else None),
             "dominant_frac_of_copy": round(g["kernels"][g["dominant"]]["achieved_GBps"] / g["copy_GBps"], 4),
             "hit_rate": round(g["h"], 4),
         },

@@ -22,6 +22,9 @@ SOURCES = [CSRC / "hkv_kernels.hip", CSRC / "hkv_runtime.cpp"]
 # library of its own on top of the C ABI
 MIXED_SOURCE = CSRC / "hkv_mixed_driver.cpp"
 MIXED_LIB_PATH = PKG / "_lib" / "libhkv_mixed.so"
+# access-pattern ceiling of find (a stand-alone benchmark program)
+PATTERN_SOURCE = CSRC / "hkv_pattern_ceiling.hip"
+PATTERN_EXE = PKG / "_lib" / "hkv_pattern_ceiling"
 ARCH = "gfx950"
 
 
@@ -71,6 +74,11 @@ def build(verbose: bool = False) -> pathlib.Path:
            f"-L{LIB_PATH.parent}", "-lhkv", "-Wl,-rpath,$ORIGIN", "-pthread"]
     subprocess.run(cmd, check=True)
     tmp.replace(MIXED_LIB_PATH)
+    tmp = PATTERN_EXE.with_suffix(".tmp")
+    cmd = [hipcc(), *[f for f in compile_flags() if f != "-fvisibility=hidden"], "-x", "hip", str(PATTERN_SOURCE),
+           "-o", str(tmp)]
+    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+    tmp.replace(PATTERN_EXE)
     return LIB_PATH
 
 

@@ -1,0 +1,117 @@
+// Access-pattern ceiling of find on this GPU: a kernel that makes exactly the
+// memory accesses of find on a full single-bucket table of 2^26 slots with
+// dim-64 rows, with none of the hashing, digest matching or ballots. Per key
+// (8 lanes): the 8-byte key (sequential), a 128-byte digest line (random in
+// 64 MiB), one 8-byte candidate key (random in 512 MiB), for 90 % of keys a
+// 256-byte row (random in 16 GiB) written out (sequential) and a found byte.
+// Run twice: with every address depending on the value the previous load
+// returned (find's chain: key -> line -> candidate -> row) and with all
+// addresses computed from the key index. A benchmark tool built next to the
+// library; it does not use the table.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+#define CK(x)                                                                    \
+  do {                                                                           \
+    hipError_t e_ = (x);                                                         \
+    if (e_ != hipSuccess) {                                                      \
+      std::fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      return 1;                                                                  \
+    }                                                                            \
+  } while (0)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+// A comparison the compiler cannot fold, so the next address waits for the load.
+__device__ __forceinline__ uint64_t after(uint64_t v) { return v == 0xDEADBEEFull ? 1ull : 0ull; }
+
+template <bool CHAIN>
+__global__ __launch_bounds__(256) void pattern_kernel(const uint64_t* __restrict__ keys,
+                                                      const uint8_t* __restrict__ lines,
+                                                      const uint64_t* __restrict__ cand,
+                                                      const float* __restrict__ rows, float* __restrict__ out,
+                                                      uint8_t* __restrict__ found, uint32_t n, uint64_t nlines,
+                                                      uint64_t ncand, uint64_t nrows) {
+  const uint32_t i = (blockIdx.x * 256u + threadIdx.x) / 8;
+  const int lane = static_cast<int>(threadIdx.x & 7);
+  if (i >= n) return;
+  const uint64_t k = keys[i];
+  const uint64_t h = mix(CHAIN ? k + i : i);
+  const uint4 w = *reinterpret_cast<const uint4*>(lines + (h & (nlines - 1)) * 128 + lane * 16);
+  const int owner = static_cast<int>((h >> 40) & 7);
+  uint64_t c = 0;
+  if (lane == owner) c = __builtin_nontemporal_load(cand + (mix(h + (CHAIN ? after(w.x) : 0)) & (ncand - 1)));
+  c = __shfl(c, owner, 8);
+  if (mix(i) % 10 == 0) {
+    if (lane == 0) found[i] = 0;
+    return;
+  }
+  const uint64_t r = mix(h + 7 + (CHAIN ? after(c) : 0)) & (nrows - 1);
+  const f32x4* s4 = reinterpret_cast<const f32x4*>(rows + r * 64);
+  const f32x4 a = __builtin_nontemporal_load(s4 + lane);
+  const f32x4 b = __builtin_nontemporal_load(s4 + lane + 8);
+  f32x4* d4 = reinterpret_cast<f32x4*>(out + static_cast<uint64_t>(i) * 64);
+  __builtin_nontemporal_store(a, d4 + lane);
+  __builtin_nontemporal_store(b, d4 + lane + 8);
+  if (lane == 0) found[i] = 1;
+}
+
+__global__ void fill_keys(uint64_t* keys, uint32_t n) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < n) keys[i] = mix(0x9E3779B97F4A7C15ull + i);
+}
+
+int main() {
+  const uint64_t nlines = 1ull << 19, ncand = 1ull << 26, nrows = 1ull << 26;
+  const uint32_t n = 1u << 20;
+  uint64_t *keys = nullptr, *cand = nullptr;
+  uint8_t *lines = nullptr, *found = nullptr;
+  float *rows = nullptr, *out = nullptr;
+  CK(hipMalloc(&keys, n * 8ull));
+  CK(hipMalloc(&cand, ncand * 8));
+  CK(hipMalloc(&lines, nlines * 128));
+  CK(hipMalloc(&rows, nrows * 256));
+  CK(hipMalloc(&out, n * 256ull));
+  CK(hipMalloc(&found, n));
+  CK(hipMemset(cand, 0, ncand * 8));
+  CK(hipMemset(lines, 0, nlines * 128));
+  CK(hipMemset(rows, 0, nrows * 256));
+  hipLaunchKernelGGL(fill_keys, dim3(n / 256), dim3(256), 0, 0, keys, n);
+  CK(hipGetLastError());
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  const double bytes = n * (8 + 128 + 4 + 0.9 * (8 + 512) + 1.0);  // find's algorithmic bytes, h = 0.9
+  const dim3 grid(n * 8 / 256), block(256);
+  std::printf("{");
+  for (int chain = 1; chain >= 0; --chain) {
+    for (int w = 0; w < 3; ++w) {
+      if (chain) hipLaunchKernelGGL(pattern_kernel<true>, grid, block, 0, 0, keys, lines, cand, rows, out, found, n, nlines, ncand, nrows);
+      else hipLaunchKernelGGL(pattern_kernel<false>, grid, block, 0, 0, keys, lines, cand, rows, out, found, n, nlines, ncand, nrows);
+    }
+    CK(hipEventRecord(e0));
+    const int reps = 20;
+    for (int r = 0; r < reps; ++r) {
+      if (chain) hipLaunchKernelGGL(pattern_kernel<true>, grid, block, 0, 0, keys, lines, cand, rows, out, found, n, nlines, ncand, nrows);
+      else hipLaunchKernelGGL(pattern_kernel<false>, grid, block, 0, 0, keys, lines, cand, rows, out, found, n, nlines, ncand, nrows);
+    }
+    CK(hipEventRecord(e1));
+    CK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double us = ms * 1000.0 / reps;
+    std::printf("\"%s\": {\"us_per_2p20_keys\": %.2f, \"algorithmic_GBps\": %.1f}%s", chain ? "dependent_chain" : "independent",
+                us, bytes / (us * 1e-6) / 1e9, chain ? ", " : "");
+  }
+  std::printf("}\n");
+  CK(hipGetLastError());
+  return 0;
+}
