@@ -880,6 +880,10 @@ def main():
             "find_frac_of_pattern_ceiling": (round(g["pattern"]["dependent_chain"]["us_per_2p20_keys"] * 1e-3
                                                   * batch_size(args) / (1 << 20) / g["kernels"]["find"]["avg_ms"], 4)
                                              if g["pattern"] else None),
+            "upsert_probe_frac_of_pattern_ceiling": (
+                round(g["pattern"]["upsert_probe_dependent_chain"]["us_per_2p20_keys"] * 1e-3 * batch_size(args)
+                      / (1 << 20) / g["kernels"]["upsert_probe"]["avg_ms"], 4)
+                if g["pattern"] and "upsert_probe" in g["kernels"] else None),
             "dominant_frac_of_copy": round(g["kernels"][g["dominant"]]["achieved_GBps"] / g["copy_GBps"], 4),
             "hit_rate": round(g["h"], 4),
         },

@@ -1,7 +1,7 @@
-// Access-pattern ceiling of find on this GPU: a kernel that makes exactly the
-// memory accesses of find on a full single-bucket table of 2^26 slots with
-// dim-64 rows, with none of the hashing, digest matching or ballots. Per key
-// (8 lanes): the 8-byte key (sequential), a 128-byte digest line (random in
+// Access-pattern ceilings of find and of insert_or_assign's first kernel on
+// this GPU: kernels that make exactly their memory accesses on a full
+// single-bucket table of 2^26 slots with dim-64 rows, with none of the
+// hashing, digest matching or ballots. For find, per key (8 lanes): the 8-byte key (sequential), a 128-byte digest line (random in
 // 64 MiB), one 8-byte candidate key (random in 512 MiB), for 90 % of keys a
 // 256-byte row (random in 16 GiB) written out (sequential) and a found byte.
 // Run twice: with every address depending on the value the previous load
@@ -48,10 +48,13 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint64_t* __restrict
   const uint4 w = *reinterpret_cast<const uint4*>(lines + (h & (nlines - 1)) * 128 + lane * 16);
   const int owner = static_cast<int>((h >> 40) & 7);
   uint64_t c = 0;
-  if (lane == owner) c = __builtin_nontemporal_load(cand + (mix(h + (CHAIN ? after(w.x) : 0)) & (ncand - 1)));
+  const uint32_t wl = w.x ^ w.y ^ w.z ^ w.w;  // the whole line is used
+  if (lane == owner) c = __builtin_nontemporal_load(cand + (mix(h + (CHAIN ? after(wl) : 0)) & (ncand - 1)));
   c = __shfl(c, owner, 8);
+  // without the chain, the line and candidate values only feed the flag
+  const uint8_t sink = (!CHAIN && (k == 0xDEADBEEFull || wl == 0xDEADBEEFu || c == 0xDEADBEEFull)) ? 2 : 0;
   if (mix(i) % 10 == 0) {
-    if (lane == 0) found[i] = 0;
+    if (lane == 0) found[i] = sink;
     return;
   }
   const uint64_t r = mix(h + 7 + (CHAIN ? after(c) : 0)) & (nrows - 1);
@@ -61,7 +64,53 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint64_t* __restrict
   f32x4* d4 = reinterpret_cast<f32x4*>(out + static_cast<uint64_t>(i) * 64);
   __builtin_nontemporal_store(a, d4 + lane);
   __builtin_nontemporal_store(b, d4 + lane + 8);
-  if (lane == 0) found[i] = 1;
+  if (lane == 0) found[i] = 1 | sink;
+}
+
+// insert_or_assign's first kernel on the same table with 90 % resident keys:
+// the same chain key -> line -> candidate, then for a resident key a 256-byte
+// input row (sequential, independent of the chain) written to a random row
+// and an 8-byte score write next to the candidate's slot; for a missing key an
+// atomic exchange on a random 4-byte chain head; 8 bytes of chain words
+// (sequential) for every key.
+__global__ __launch_bounds__(256) void upsert_pattern_kernel(const uint64_t* __restrict__ keys,
+                                                             const uint8_t* __restrict__ lines,
+                                                             const uint64_t* __restrict__ cand,
+                                                             uint64_t* __restrict__ scores, float* __restrict__ rows,
+                                                             const float* __restrict__ in_rows,
+                                                             const uint64_t* __restrict__ in_scores,
+                                                             uint32_t* __restrict__ heads, uint32_t* __restrict__ next,
+                                                             uint32_t* __restrict__ target, uint32_t n, uint64_t nlines,
+                                                             uint64_t ncand, uint64_t nrows) {
+  const uint32_t i = (blockIdx.x * 256u + threadIdx.x) / 8;
+  const int lane = static_cast<int>(threadIdx.x & 7);
+  if (i >= n) return;
+  const uint64_t k = keys[i];
+  const uint64_t h = mix(k + i);
+  const uint4 w = *reinterpret_cast<const uint4*>(lines + (h & (nlines - 1)) * 128 + lane * 16);
+  const int owner = static_cast<int>((h >> 40) & 7);
+  const uint64_t slot = mix(h + after(w.x ^ w.y ^ w.z ^ w.w)) & (ncand - 1);
+  uint64_t c = 0;
+  if (lane == owner) c = __builtin_nontemporal_load(cand + slot);
+  c = __shfl(c, owner, 8);
+  if (mix(i) % 10 == 0) {
+    if (lane == 0) {
+      target[i] = static_cast<uint32_t>(slot >> 7);
+      next[i] = __hip_atomic_exchange(heads + (slot >> 7), i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  const uint64_t r = (slot + after(c)) & (nrows - 1);
+  const f32x4* s4 = reinterpret_cast<const f32x4*>(in_rows + static_cast<uint64_t>(i) * 64);
+  const f32x4 a = __builtin_nontemporal_load(s4 + lane);
+  const f32x4 b = __builtin_nontemporal_load(s4 + lane + 8);
+  f32x4* d4 = reinterpret_cast<f32x4*>(rows + r * 64);
+  __builtin_nontemporal_store(a, d4 + lane);
+  __builtin_nontemporal_store(b, d4 + lane + 8);
+  if (lane == 0) {
+    scores[slot] = in_scores[i];
+    next[i] = 0xFFFFFFFEu;
+  }
 }
 
 __global__ void fill_keys(uint64_t* keys, uint32_t n) {
@@ -111,7 +160,35 @@ int main() {
     std::printf("\"%s\": {\"us_per_2p20_keys\": %.2f, \"algorithmic_GBps\": %.1f}%s", chain ? "dependent_chain" : "independent",
                 us, bytes / (us * 1e-6) / 1e9, chain ? ", " : "");
   }
-  std::printf("}\n");
+  // the upsert pattern: 8 key + 128 line + 4 false-positive keys
+  // + 0.9 (8 key + 256 row in + 8 score in + 256 row + 8 score) + 0.1 * 8
+  uint64_t *scores = nullptr, *in_scores = nullptr;
+  uint32_t *heads = nullptr, *next = nullptr, *target = nullptr;
+  float* in_rows = out;  // n rows, read sequentially
+  CK(hipMalloc(&scores, ncand * 8));
+  CK(hipMalloc(&in_scores, n * 8ull));
+  CK(hipMalloc(&heads, (ncand / 128) * 4));
+  CK(hipMalloc(&next, n * 4ull));
+  CK(hipMalloc(&target, n * 4ull));
+  CK(hipMemset(scores, 0, ncand * 8));
+  CK(hipMemset(in_scores, 0, n * 8ull));
+  CK(hipMemset(heads, 0xFF, (ncand / 128) * 4));
+  const double ubytes = n * (8 + 128 + 4 + 0.9 * (8 + 256 + 8 + 256 + 8 + 8) + 0.1 * 8);
+  for (int w = 0; w < 3; ++w)
+    hipLaunchKernelGGL(upsert_pattern_kernel, grid, block, 0, 0, keys, lines, cand, scores, rows, in_rows, in_scores,
+                       heads, next, target, n, nlines, ncand, nrows);
+  CK(hipEventRecord(e0));
+  const int ureps = 20;
+  for (int r = 0; r < ureps; ++r)
+    hipLaunchKernelGGL(upsert_pattern_kernel, grid, block, 0, 0, keys, lines, cand, scores, rows, in_rows, in_scores,
+                       heads, next, target, n, nlines, ncand, nrows);
+  CK(hipEventRecord(e1));
+  CK(hipEventSynchronize(e1));
+  float ums = 0.f;
+  CK(hipEventElapsedTime(&ums, e0, e1));
+  const double uus = ums * 1000.0 / ureps;
+  std::printf(", \"upsert_probe_dependent_chain\": {\"us_per_2p20_keys\": %.2f, \"algorithmic_GBps\": %.1f}}\n", uus,
+              ubytes / (uus * 1e-6) / 1e9);
   CK(hipGetLastError());
   return 0;
 }
