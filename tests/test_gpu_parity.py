@@ -257,6 +257,49 @@ def test_adversarial_all_keys_one_bucket():
     check_find(tab, o, to_dev(keys))
 
 
+@pytest.mark.parametrize("hot_buckets", [1, 2, 4])
+def test_contention_few_buckets_mixed_with_updates(hot_buckets):
+    """Contention stress: every key of each batch routes to one of 1, 2 or 4
+    buckets of a 64-bucket table, batches mix new keys with updates of
+    resident ones and with keys that lose admission, and the scores jitter
+    within a step (ties broken by key). Contents exact after every batch,
+    and insert_and_evict's hand-back exact on the same stream."""
+    H = hkv()
+    C, D = 64 * SLOTS, 4
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    rng = np.random.default_rng(40 + hot_buckets)
+    cand = rng.integers(1, 1 << 62, size=400000, dtype=np.int64).view(np.uint64)
+    b1 = o.route(cand)[0]
+    hot = rng.choice(64, size=hot_buckets, replace=False)
+    keys = cand[np.isin(b1, hot)][:3000]
+    resident = []
+    for step in range(1, 9):
+        fresh = keys[(step - 1) * 300: step * 300]
+        old = rng.choice(np.array(resident, dtype=np.uint64), size=min(200, len(resident)), replace=False) \
+            if resident else np.zeros(0, np.uint64)
+        k = rng.permutation(np.concatenate([fresh, old]))
+        sc = (step * 4 + rng.integers(0, 4, size=k.size)).astype(np.uint64)
+        kt, st = to_dev(k), to_dev(sc)
+        v = gen.values(kt, step, D)
+        if step % 2:
+            tab.insert_or_assign(kt, v, st)
+            o.insert_or_assign(k, sc, values=v.cpu().numpy())
+        else:
+            ek, ev, es, cnt = tab.insert_and_evict(kt, v, st)
+            want = o.insert_and_evict(k, sc, values=v.cpu().numpy())
+            torch.cuda.synchronize()
+            m = int(cnt.item())
+            order = np.argsort(np_u64(ek[:m]))
+            wo = np.argsort(want["keys"])
+            assert np.array_equal(np_u64(ek[:m])[order], want["keys"][wo])
+            assert np.array_equal(np_u64(es[:m])[order], want["scores"][wo])
+            assert np.array_equal(ev[:m].cpu().numpy()[order].view(np.uint32), want["values"][wo].view(np.uint32))
+        assert_same_contents(tab, o)
+        resident = o.export()["keys"].tolist()
+    check_find(tab, o, to_dev(keys[:2400]))
+
+
 def test_edge_cases_reserved_empty_duplicates():
     H = hkv()
     C, D = 4 * SLOTS, 4
