@@ -785,6 +785,8 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
   const uint64_t k = keys[i];
+  // loaded with the key: stored at the end without waiting behind the row
+  const uint64_t score = scores[i];
   if (is_reserved(k)) {
     if (lane == 0) {
       next[i] = kSkipIdx;
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
       copy_row<G, V4, NT>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
     }
     if (lane == 0) {
-      t.scores[p] = scores[i];
+      t.scores[p] = score;
       next[i] = kSkipIdx;
       if (FETCH && found) found[i] = 1;
     }
