@@ -735,16 +735,10 @@ __device__ __forceinline__ void own_upsert(Owned& o, const TableView& t, uint64_
 // score changed since) only makes the bucket choice less good, never the
 // table inconsistent. A full bucket without a record (not produced by the
 // owner kernel, which records every bucket it leaves full) counts as lowest.
-__device__ __forceinline__ void cached_lowest(const TableView& t, uint32_t b, int lane, uint64_t* ms,
-                                              uint64_t* mk) {
-  uint64_t s = 0, k = ~0ull;
-  if (lane == 0) {
-    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.bmin + 2 * static_cast<uint64_t>(b));
-    s = c.x;
-    k = c.y;
-  }
-  s = __shfl(s, 0, kInsG);
-  k = __shfl(k, 0, kInsG);
+// Read by the lane that links the key (the result is only used there).
+__device__ __forceinline__ void cached_lowest(const TableView& t, uint32_t b, uint64_t* ms, uint64_t* mk) {
+  const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.bmin + 2 * static_cast<uint64_t>(b));
+  uint64_t s = c.x, k = c.y;
   if (k == ~0ull) {
     s = 0;
     k = 0;
@@ -780,7 +774,6 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
                                                               uint8_t* __restrict__ found,
                                                               uint32_t* __restrict__ next,
                                                               uint32_t* __restrict__ target, bool link) {
-  static_assert(!DUAL || G == kInsG, "dual-bucket selection works on 16-lane groups");
   const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
@@ -819,6 +812,8 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     if (lane == 0) next[i] = kNoIdx;
     return;
   }
+  // the rest (bucket choice and chain link) is the work of one lane
+  if (lane != 0) return;
   const uint64_t h = fmix64(k);
   uint32_t tb = bucket_of(t, h);
   uint32_t tocc = o1;
@@ -831,17 +826,15 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
         tocc = (o1 <= o2) ? o1 : o2;
       } else {
         uint64_t s1, k1, s2, k2;
-        cached_lowest(t, b1, lane, &s1, &k1);
-        cached_lowest(t, b2, lane, &s2, &k2);
+        cached_lowest(t, b1, &s1, &k1);
+        cached_lowest(t, b2, &s2, &k2);
         tb = (s2 < s1 || (s2 == s1 && k2 < k1)) ? b2 : b1;
       }
     }
   }
-  if (lane == 0) {
-    target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
-    next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-  }
+  target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
+  next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // State of a bucket owned by a 16-lane group in the owner kernel: its
@@ -1375,14 +1368,10 @@ hipError_t assign_d(const TableView& t, uint64_t n, const uint64_t* keys, const 
 template <bool V4, bool DUAL, bool FETCH>
 hipError_t probe_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_t* next, uint32_t* target,
                    bool link, hipStream_t s, KernelTimer* tm) {
-  if constexpr (DUAL) {
-    return probe_g<kInsG, V4, true, FETCH>(t, n, c, next, target, link, s, tm);
-  } else {
-    switch (lanes_for(t)) {
-      case 4: return probe_g<4, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
-      case 8: return probe_g<8, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
-      default: return probe_g<16, V4, false, FETCH>(t, n, c, next, target, link, s, tm);
-    }
+  switch (lanes_for(t)) {
+    case 4: return probe_g<4, V4, DUAL, FETCH>(t, n, c, next, target, link, s, tm);
+    case 8: return probe_g<8, V4, DUAL, FETCH>(t, n, c, next, target, link, s, tm);
+    default: return probe_g<16, V4, DUAL, FETCH>(t, n, c, next, target, link, s, tm);
   }
 }
 
