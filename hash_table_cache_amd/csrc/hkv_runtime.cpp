@@ -146,6 +146,9 @@ struct hkv_table {
   unsigned long long* size_host = nullptr;  // pinned
   std::mutex mu;
   std::vector<StreamEvent> last[3];  // per group: last event recorded on each stream
+  bool any_call = false;             // a call has been issued
+  bool multi_stream = false;         // calls have come from more than one stream
+  hipStream_t first_stream = nullptr;
   Profiler prof;
   bool profiling = false;
   hkv::KernelTimer* timer() { return profiling ? &prof : nullptr; }
@@ -206,9 +209,31 @@ hkv_status check_buffer(const hkv_table* t, const void* p, uint64_t bytes, const
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// While every call of a table comes from one stream, stream order alone
+// orders them and no events are recorded (an event record costs about as
+// much host time as the launch it follows). The first call from a second
+// stream finds earlier calls without events, so it waits once for the device
+// to finish its work; from then on every call records its event. Caller
+// holds t->mu.
+hkv_status enter_stream(hkv_table* t, hipStream_t s) {
+  if (t->multi_stream) return HKV_OK;
+  if (!t->any_call) {
+    t->any_call = true;
+    t->first_stream = s;
+    return HKV_OK;
+  }
+  if (s == t->first_stream) return HKV_OK;
+  const hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  t->multi_stream = true;
+  return HKV_OK;
+}
+
 // Makes stream s wait for every outstanding call of a group incompatible with g
 // that was issued on another stream. Caller holds t->mu.
 hkv_status order_before(hkv_table* t, int g, hipStream_t s) {
+  hkv_status st = enter_stream(t, s);
+  if (st != HKV_OK || !t->multi_stream) return st;
   for (int h = 0; h < 3; ++h) {
     if (!groups_conflict(g, h, (t->opt.flags & HKV_FLAG_RW_LOCK) != 0)) continue;
     for (auto& r : t->last[h]) {
@@ -223,8 +248,10 @@ hkv_status order_before(hkv_table* t, int g, hipStream_t s) {
   return HKV_OK;
 }
 
-// Records group g's completion event on stream s. Caller holds t->mu.
+// Records group g's completion event on stream s (once the table is used
+// from more than one stream). Caller holds t->mu.
 hkv_status record_after(hkv_table* t, int g, hipStream_t s) {
+  if (!t->multi_stream) return HKV_OK;
   hipEvent_t ev = nullptr;
   for (auto& r : t->last[g])
     if (r.stream == s) ev = r.event;
@@ -238,8 +265,15 @@ hkv_status record_after(hkv_table* t, int g, hipStream_t s) {
   return HKV_OK;
 }
 
-// Waits for every recorded inserter call (used before replacing the workspace).
+// Waits for every outstanding call of group g (used before replacing a
+// workspace and on destroy). Single-stream calls have no events: the device
+// is synchronized instead.
 hkv_status drain_group(hkv_table* t, int g) {
+  if (!t->multi_stream) {
+    if (!t->any_call) return HKV_OK;
+    const hipError_t e = hipDeviceSynchronize();
+    return e == hipSuccess ? HKV_OK : fail_hip(e, "hipDeviceSynchronize");
+  }
   for (auto& r : t->last[g]) {
     const hipError_t e = hipEventSynchronize(r.event);
     if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");

@@ -34,8 +34,11 @@
  *     passed the call.
  *   - Group ordering (§3.5, Table 4) is enforced with stream/event ordering:
  *     a call waits, on its own stream, for every outstanding call of an
- *     incompatible group issued earlier on another stream. The host never
- *     blocks for this. Several host threads may call concurrently.
+ *     incompatible group issued earlier on another stream. The host does not
+ *     block for this, with one exception: while all calls on a table come
+ *     from a single stream they record no events (stream order suffices), so
+ *     the first call from a second stream waits once for the device
+ *     (hipDeviceSynchronize). Several host threads may call concurrently.
  *   - Arguments are validated synchronously; on any error nothing is enqueued,
  *     the call returns a negative status and hkv_last_error() describes it.
  *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 3 keys.
