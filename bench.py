@@ -75,6 +75,8 @@ def parse_args():
     p.add_argument("--mixed", default="", metavar="MIXES",
                    help="concurrency ablation over these thread mixes, e.g. " + ",".join(MIXES))
     p.add_argument("--mixed-batches", type=int, default=200, help="batches per thread in --mixed")
+    p.add_argument("--api-sweep", action="store_true",
+                   help="every call on the pure-HBM configurations A-C at lambda 0.5")
     p.add_argument("--tiered", action="store_true",
                    help="the tiered-values workload (use with --capacity-log2 28 --dim 128)")
     p.add_argument("--hybrid", default="", metavar="FRACS",
@@ -392,6 +394,80 @@ def tiered_run(args) -> None:
     log(f"tiered: {res}")
     tab.close()
     print(json.dumps({"tiered": res}), flush=True)
+
+
+API_CONFIGS = (("A", 8, 27), ("B", 32, 27), ("C", 64, 26))  # (name, dim, log2 capacity), pure HBM
+
+
+def api_sweep(args) -> None:
+    """Every call on single-bucket tables of the paper's pure-HBM
+    configurations (A: dim 8, 2^27 slots; B: dim 32, 2^27; C: dim 64, 2^26)
+    at lambda 0.5, 2^batch_log2-key batches: find (90 % resident), find*,
+    contains, assign (resident keys), insert_or_assign, insert_and_evict and
+    find_or_insert (90 % resident, 10 % new keys). 2 warm-up and 10 timed
+    batches per call; rate = keys / kernel time per call (library events).
+    Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    batch = 1 << args.batch_log2
+    n_hit = int(round(batch * args.hit_frac))
+    n_new = int(round(batch * args.new_frac))
+    reps = 12
+    out = {}
+    for name, dim, lg in API_CONFIGS:
+        cap = 1 << lg
+        tab = H.HashTable(cap, dim)
+        cursor, step, size = fill_table(tab, 0.5, cap, batch, dim, SEED, 600, dev)
+        pool = gen.unique_keys(SEED, 600, cursor - 2 * batch, 2 * batch, device=dev)
+        finds, writes = [], []
+        for j in range(reps):
+            pick = torch.argsort(gen.counter_words(SEED, 610, j * pool.numel(), pool.numel(), dev))
+            q = torch.cat([pool[pick[:n_hit]], gen.unique_keys(SEED, 611, j * batch, batch - n_hit, device=dev)])
+            finds.append(gen.shuffle(q, SEED, 620 + j))
+        for j in range(4 * reps):
+            pick = torch.argsort(gen.counter_words(SEED, 612, j * pool.numel(), pool.numel(), dev))
+            u = torch.cat([pool[pick[:batch - n_new]], gen.unique_keys(SEED, 613, j * batch, n_new, device=dev)])
+            u = gen.shuffle(u, SEED, 700 + j)
+            writes.append((u, gen.values(u, 2000 + j, dim, SEED),
+                           torch.full((batch,), step + j, dtype=torch.int64, device=dev)))
+        vals = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+        found = torch.empty(batch, dtype=torch.uint8, device=dev)
+        ptrs = torch.empty(batch, dtype=torch.int64, device=dev)
+        ev = (torch.empty(batch, dtype=torch.int64, device=dev), torch.empty((batch, dim), device=dev),
+              torch.empty(batch, dtype=torch.int64, device=dev), torch.zeros(1, dtype=torch.int64, device=dev))
+        calls = {
+            "find": lambda j: tab.find(finds[j], values_out=vals, found_out=found),
+            "find_ptr": lambda j: tab.find_ptr(finds[j], ptrs_out=ptrs, found_out=found),
+            "contains": lambda j: tab.contains(finds[j], found_out=found),
+            "assign": lambda j: tab.assign(finds[j][:n_hit], writes[j][1][:n_hit], writes[j][2][:n_hit]),
+            "insert_or_assign": lambda j: tab.insert_or_assign(*writes[j]),
+            "insert_and_evict": lambda j: tab.insert_and_evict(*writes[reps + j], out=ev),
+            "find_or_insert": lambda j: tab.find_or_insert(writes[2 * reps + j][0], writes[2 * reps + j][1],
+                                                           writes[2 * reps + j][2], found_out=found),
+        }
+        res = {}
+        for api, call in calls.items():
+            for j in range(2):
+                call(j)
+            torch.cuda.synchronize()
+            tab.profile_start()
+            for j in range(2, reps):
+                call(j)
+            ks = tab.profile_stop()
+            per_call = sum(v[1] for v in ks.values()) / (reps - 2)
+            keys = n_hit if api == "assign" else batch
+            res[api] = round(keys / per_call / 1e6, 3)
+        res["lambda_end"] = round(tab.size() / cap, 4)
+        out[f"{name}: dim {dim}, 2^{lg} slots"] = res
+        log(f"config {name}: {res}")
+        tab.close()
+        del finds, writes
+        torch.cuda.empty_cache()
+    print(json.dumps({"api_sweep_bkvs": out, "lambda": 0.5, "batch": batch}), flush=True)
 
 
 MIXES = {
@@ -807,6 +883,9 @@ def main():
         return
     if args.tiered:
         tiered_run(args)
+        return
+    if args.api_sweep:
+        api_sweep(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()
