@@ -76,7 +76,8 @@ def parse_args():
                    help="concurrency ablation over these thread mixes, e.g. " + ",".join(MIXES))
     p.add_argument("--mixed-batches", type=int, default=200, help="batches per thread in --mixed")
     p.add_argument("--api-sweep", action="store_true",
-                   help="every call on the pure-HBM configurations A-C at lambda 0.5")
+                   help="every call on the pure-HBM configurations A-C (at --api-lambdas)")
+    p.add_argument("--api-lambdas", default="0.5", help="load factors of --api-sweep, e.g. 0.5,0.75,1.0")
     p.add_argument("--tiered", action="store_true",
                    help="the tiered-values workload (use with --capacity-log2 28 --dim 128)")
     p.add_argument("--hybrid", default="", metavar="FRACS",
@@ -402,7 +403,7 @@ API_CONFIGS = (("A", 8, 27), ("B", 32, 27), ("C", 64, 26))  # (name, dim, log2 c
 def api_sweep(args) -> None:
     """Every call on single-bucket tables of the paper's pure-HBM
     configurations (A: dim 8, 2^27 slots; B: dim 32, 2^27; C: dim 64, 2^26)
-    at lambda 0.5, 2^batch_log2-key batches: find (90 % resident), find*,
+    at each load factor of --api-lambdas, 2^batch_log2-key batches: find (90 % resident), find*,
     contains, assign (resident keys), insert_or_assign, insert_and_evict and
     find_or_insert (90 % resident, 10 % new keys). 2 warm-up and 10 timed
     batches per call; rate = keys / kernel time per call (library events).
@@ -418,10 +419,10 @@ def api_sweep(args) -> None:
     n_new = int(round(batch * args.new_frac))
     reps = 12
     out = {}
-    for name, dim, lg in API_CONFIGS:
+    for (name, dim, lg), lam in [(c, float(x)) for c in API_CONFIGS for x in args.api_lambdas.split(",")]:
         cap = 1 << lg
         tab = H.HashTable(cap, dim)
-        cursor, step, size = fill_table(tab, 0.5, cap, batch, dim, SEED, 600, dev)
+        cursor, step, size = fill_table(tab, lam, cap, batch, dim, SEED, 600, dev)
         pool = gen.unique_keys(SEED, 600, cursor - 2 * batch, 2 * batch, device=dev)
         finds, writes = [], []
         for j in range(reps):
@@ -462,12 +463,12 @@ def api_sweep(args) -> None:
             keys = n_hit if api == "assign" else batch
             res[api] = round(keys / per_call / 1e6, 3)
         res["lambda_end"] = round(tab.size() / cap, 4)
-        out[f"{name}: dim {dim}, 2^{lg} slots"] = res
-        log(f"config {name}: {res}")
+        out[f"{name}: dim {dim}, 2^{lg} slots, lambda {lam}"] = res
+        log(f"config {name} lambda {lam}: {res}")
         tab.close()
         del finds, writes
         torch.cuda.empty_cache()
-    print(json.dumps({"api_sweep_bkvs": out, "lambda": 0.5, "batch": batch}), flush=True)
+    print(json.dumps({"api_sweep_bkvs": out, "batch": batch}), flush=True)
 
 
 MIXES = {
