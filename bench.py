@@ -5,8 +5,11 @@ float32 rows, pre-filled with uniform distinct 64-bit keys (score = batch
 counter) to load factors 0.50, 0.75, 0.90 and 1.00. One step issues, on each
 table, a find of 2^20 keys (90 % resident, 10 % never inserted) followed by an
 insert_or_assign of 2^20 keys (90 % resident keys refreshed with new rows and
-the current step as score, 10 % new keys). Inputs are generated on the GPU
-before the timed region. value = keys processed by all calls / wall time.
+the current step as score, 10 % new keys). The steps of each phase run table
+by table (every step on the 0.50 table, then on the 0.75 table, ...), as the
+paper measures each load factor on its own table; --interleave-tables runs
+them step by step across the tables. Inputs are generated on the GPU before
+the timed region. value = keys processed by all calls / wall time.
 
 The K timed steps issue nothing but the calls. They are followed by K more
 steps of the same workload in which every kernel launch is timed with a pair
@@ -68,6 +71,8 @@ def parse_args():
     p.add_argument("--insert-steps", type=int, default=5,
                    help="extra all-new-key insert batches on the full table, reported in detail")
     p.add_argument("--find-only", action="store_true", help="time find batches only")
+    p.add_argument("--interleave-tables", action="store_true",
+                   help="run each step across all load-factor tables instead of table by table")
     p.add_argument("--no-extra-ops", dest="extra_ops", action="store_false",
                    help="skip the find*/contains/insert_and_evict/find_or_insert measurements")
     p.add_argument("--capacity-sweep", default="", metavar="LOG2S",
@@ -169,10 +174,11 @@ def copy_bandwidth(mib: int = 2048, reps: int = 10) -> float:
     return gbs
 
 
-def pattern_ceiling():
+def pattern_ceiling(dim: int = 64):
     """Runs the access-pattern ceiling program (find's memory accesses on a
-    2^26-slot dim-64 table without its arithmetic, with and without the chain
-    of dependent loads) in a child process; returns its JSON or None."""
+    2^26-slot table with rows of `dim` floats, without its arithmetic, with
+    and without the chain of dependent loads) in a child process; returns its
+    JSON or None."""
     import subprocess
 
     from hash_table_cache_amd import build as hb
@@ -180,7 +186,7 @@ def pattern_ceiling():
     if not hb.PATTERN_EXE.exists():
         return None
     try:
-        r = subprocess.run([str(hb.PATTERN_EXE)], capture_output=True, text=True, timeout=120, check=True)
+        r = subprocess.run([str(hb.PATTERN_EXE), str(dim)], capture_output=True, text=True, timeout=120, check=True)
         return json.loads(r.stdout)
     except (subprocess.SubprocessError, ValueError) as e:
         log(f"pattern ceiling program failed: {e}")
@@ -623,24 +629,37 @@ def run_gpu(args):
 
     total_keys = 0
 
-    def one_step(s, timed):
+    def table_step(T, s, timed):
         # warm-up steps run exactly the same calls as timed ones; nothing but
         # the calls is queued (kernel times come from the dispatches' events)
         nonlocal total_keys
-        for T in tables:
-            T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"][s])
-            if not args.find_only:
-                uk, sc = T["ups"][s]
-                T["tab"].insert_or_assign(uk, T["vals"][s % 2], sc)
-            if timed:
-                total_keys += batch * (1 if args.find_only else 2)
+        T["tab"].find(T["finds"][s], values_out=T["out"], found_out=T["found"][s])
+        if not args.find_only:
+            uk, sc = T["ups"][s]
+            T["tab"].insert_or_assign(uk, T["vals"][s % 2], sc)
+        if timed:
+            total_keys += batch * (1 if args.find_only else 2)
 
-    for s in range(args.warmup):
-        one_step(s, False)
+    def run_steps(first, count, timed):
+        # A step is one find and one insert_or_assign on every table. By
+        # default the steps of a phase are grouped by table — every step on
+        # the first load factor's table, then the next — as the paper measures
+        # each load factor on a table of its own; --interleave-tables runs
+        # step by step across the tables instead (their digest arrays then
+        # compete for the caches between consecutive batches).
+        if args.interleave_tables:
+            for s in range(first, first + count):
+                for T in tables:
+                    table_step(T, s, timed)
+        else:
+            for T in tables:
+                for s in range(first, first + count):
+                    table_step(T, s, timed)
+
+    run_steps(0, args.warmup, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        one_step(s, True)
+    run_steps(args.warmup, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for T in tables:
@@ -648,8 +667,7 @@ def run_gpu(args):
         T["tab"].profile_start()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for s in range(args.warmup + args.steps, total_steps):
-        one_step(s, False)
+    run_steps(args.warmup + args.steps, args.steps, False)
     torch.cuda.synchronize()
     wall_timed_kernels = time.perf_counter() - t1
     kstats = {}
@@ -891,7 +909,8 @@ def main():
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()
     log(f"device copy bandwidth {g['copy_GBps']:.1f} GB/s")
-    g["pattern"] = pattern_ceiling() if args.dim == 64 and args.capacity_log2 == 26 else None
+    g["pattern"] = (pattern_ceiling(args.dim) if args.dim in (32, 64, 128) and args.capacity_log2 == 26
+                    else None)
     cpu = None
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline")
