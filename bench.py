@@ -83,6 +83,8 @@ def parse_args():
     p.add_argument("--api-sweep", action="store_true",
                    help="every call on the pure-HBM configurations A-C (at --api-lambdas)")
     p.add_argument("--api-lambdas", default="0.5", help="load factors of --api-sweep, e.g. 0.5,0.75,1.0")
+    p.add_argument("--triple", action="store_true",
+                   help="the mixed find/assign/insert_or_assign workload (use with --capacity-log2 27)")
     p.add_argument("--tiered", action="store_true",
                    help="the tiered-values workload (use with --capacity-log2 28 --dim 128)")
     p.add_argument("--hybrid", default="", metavar="FRACS",
@@ -401,6 +403,99 @@ def tiered_run(args) -> None:
     log(f"tiered: {res}")
     tab.close()
     print(json.dumps({"tiered": res}), flush=True)
+
+
+def assign_bytes_per_key(dim: int) -> float:
+    """assign of a resident key: 8 key + 8 score in + 4D row in + 128 digest
+    line + 4 false-positive keys + 8 key + 4D row write + 8 score write."""
+    return 164 + 8 * dim
+
+
+def triple_run(args) -> None:
+    """The mixed reader / updater / inserter workload: one single-bucket table
+    of 2^capacity_log2 slots (2^27) with dim --dim rows (64) filled to
+    lambda = 1 with distinct uniform keys in 2^20-key batches (score = batch).
+    Each step: find 2^20 keys (90 % resident, 10 % never inserted), assign
+    2^19 distinct resident keys (new rows, score = step), insert_or_assign
+    2^18 keys (2^17 resident, 2^17 new), on one stream. --warmup steps, then
+    --steps timed steps with nothing but the calls queued (value = 1.75 * 2^20
+    keys per step / wall time), then --steps more with kernel timing (rate of
+    each call from its kernels' time). Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap, dim = 1 << args.capacity_log2, args.dim
+    nf, na, nu = 1 << 20, 1 << 19, 1 << 18
+    t0 = time.perf_counter()
+    tab = H.HashTable(cap, dim)
+    cursor, step, size = fill_table(tab, 1.0, cap, 1 << 20, dim, SEED, 800, dev)
+    torch.cuda.synchronize()
+    log(f"triple: filled to {size} with {cursor} keys in {time.perf_counter() - t0:.1f}s")
+    # the last two fill batches: resident, and the highest-ranked keys, so no
+    # insert of the measured steps evicts them
+    pool = gen.unique_keys(SEED, 800, cursor - (2 << 20), 2 << 20, device=dev)
+    n_hit = int(round(nf * 0.9))
+    total = args.warmup + 2 * args.steps
+    steps = []
+    for j in range(total):
+        pick = torch.argsort(gen.counter_words(SEED, 810, j * pool.numel(), pool.numel(), dev))
+        fk = gen.shuffle(torch.cat([pool[pick[:n_hit]], gen.unique_keys(SEED, 811, j * nf, nf - n_hit, device=dev)]),
+                         SEED, 820 + j)
+        ak = pool[pick[n_hit:n_hit + na]]
+        uk = gen.shuffle(torch.cat([pool[pick[-(nu // 2):]], gen.unique_keys(SEED, 812, j * nu, nu // 2, device=dev)]),
+                         SEED, 900 + j)
+        sc = step + 1 + j
+        steps.append((fk, ak, torch.full((na,), sc, dtype=torch.int64, device=dev), uk,
+                       torch.full((nu,), sc, dtype=torch.int64, device=dev)))
+    a_rows = gen.values(pool[:na], 3000, dim, SEED)
+    u_rows = gen.values(pool[:nu], 3001, dim, SEED)
+    out = torch.empty((nf, dim), dtype=torch.float32, device=dev)
+    found = [torch.empty(nf, dtype=torch.uint8, device=dev) for _ in range(total)]
+
+    def run(first, count):
+        for j in range(first, first + count):
+            fk, ak, asc, uk, usc = steps[j]
+            tab.find(fk, values_out=out, found_out=found[j])
+            tab.assign(ak, a_rows, asc)
+            tab.insert_or_assign(uk, u_rows, usc)
+
+    torch.cuda.synchronize()
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    tab.profile_start()
+    run(args.warmup + args.steps, args.steps)
+    ks = tab.profile_stop()
+    hits = sum(int(f.sum()) for f in found[args.warmup:]) / (2 * args.steps * nf)
+    avg = {n: v[1] / v[0] for n, v in ks.items()}
+    call_ms = {"find": avg["find"], "assign": avg["assign"],
+               "insert_or_assign": avg["upsert_probe"] + avg["upsert_owner"]}
+    per_key = {"find": find_bytes_per_key(dim, hits), "assign": assign_bytes_per_key(dim),
+               "upsert_probe": probe_bytes_per_key(dim, 0.5), "upsert_owner": owner_bytes_per_key(dim, 0.5, 1.0)}
+    n_of = {"find": nf, "assign": na, "upsert_probe": nu, "upsert_owner": nu}
+    kernels = {}
+    for n in ("find", "assign", "upsert_probe", "upsert_owner"):
+        gbs = n_of[n] * per_key[n] / (avg[n] * 1e-3) / 1e9
+        kernels[n] = dict(avg_ms=round(avg[n], 5), bytes_per_launch=round(n_of[n] * per_key[n]),
+                          achieved_GBps=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    res = dict(
+        workload=(f"mixed reader/updater/inserter: single bucket, capacity 2^{args.capacity_log2}, dim {dim}, "
+                  f"lambda 1.0; per step find 2^20 (90 % resident) + assign 2^19 resident + insert_or_assign "
+                  f"2^18 (half new)"),
+        combined_bkvs=round(1.75 * nf * args.steps / wall / 1e9, 4), ms_per_step=round(wall / args.steps * 1e3, 4),
+        call_bkvs={n: round({"find": nf, "assign": na, "insert_or_assign": nu}[n] / ms / 1e6, 3)
+                   for n, ms in call_ms.items()},
+        kernel_step_ms=round(sum(call_ms.values()), 4), kernels=kernels, hit_rate=round(hits, 4),
+        lambda_end=round(tab.size() / cap, 4), steps=args.steps, warmup=args.warmup)
+    log(f"triple: {res}")
+    tab.close()
+    print(json.dumps({"triple": res}), flush=True)
 
 
 API_CONFIGS = (("A", 8, 27), ("B", 32, 27), ("C", 64, 26))  # (name, dim, log2 capacity), pure HBM
@@ -905,6 +1000,9 @@ def main():
         return
     if args.api_sweep:
         api_sweep(args)
+        return
+    if args.triple:
+        triple_run(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()
