@@ -83,6 +83,9 @@ def parse_args():
     p.add_argument("--api-sweep", action="store_true",
                    help="every call on the pure-HBM configurations A-C (at --api-lambdas)")
     p.add_argument("--api-lambdas", default="0.5", help="load factors of --api-sweep, e.g. 0.5,0.75,1.0")
+    p.add_argument("--online", action="store_true",
+                   help="single- vs dual-bucket continuous Zipf upsert at full capacity (use --capacity-log2 27)")
+    p.add_argument("--online-modes", default="single,dual", help="bucket modes of --online")
     p.add_argument("--triple", action="store_true",
                    help="the mixed find/assign/insert_or_assign workload (use with --capacity-log2 27)")
     p.add_argument("--tiered", action="store_true",
@@ -496,6 +499,102 @@ def triple_run(args) -> None:
     log(f"triple: {res}")
     tab.close()
     print(json.dumps({"triple": res}), flush=True)
+
+
+def online_run(args) -> None:
+    """Continuous online upsert at full capacity, single- against dual-bucket
+    mode (the paper's §5.5, Table 11): a table of 2^capacity_log2 slots (2^27)
+    with dim --dim rows (64) takes a stream of Zipf(1.05) draws over 2^30 ids
+    (key = id), 2^20 draws per batch deduplicated, score = the key's
+    cumulative frequency (LFU), until it is full, then 200 more batches.
+    Before each batch's insert_or_assign, contains() looks up the batch's raw
+    draws: the cache hit ratio. Reported per mode: batches to fill,
+    load factor at the first eviction (first batch that adds fewer keys than
+    it has new ones), hit ratio and kernel-timed rates over the 200 batches,
+    and top-N retention after them (N = capacity; ideal = the N highest
+    (frequency, key) among all keys seen). Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap, dim, draws, n_ids, steady_batches = 1 << args.capacity_log2, args.dim, 1 << 20, 1 << 30, 200
+    seed = 0x484B560000000003
+    zipf = gen.Zipf(1.05, n_ids)
+    out = {}
+    for mode in args.online_modes.split(","):
+        t0 = time.perf_counter()
+        tab = H.HashTable(cap, dim, dual_bucket=mode == "dual")
+        freq = torch.zeros(n_ids + 1, dtype=torch.int64, device=dev)
+        b, size, first_evict = 0, 0, None
+        while size < cap:
+            r = zipf.draw(seed, 1, b * draws, draws, device=dev)
+            uniq, cnt = torch.unique(r, return_counts=True)
+            fresh = int((freq[uniq] == 0).sum())
+            freq.index_add_(0, uniq, cnt)
+            sc = freq[uniq]
+            tab.insert_or_assign(uniq, gen.values(uniq, sc, dim, seed), sc)
+            new_size = tab.size()
+            if first_evict is None and new_size - size < fresh:
+                first_evict = size / cap
+            size = new_size
+            b += 1
+            if b > 4000:
+                raise RuntimeError("table never reached full capacity")
+        fill_batches = b
+        # the steady-state batches, generated before the measured loop
+        batches = []
+        for j in range(steady_batches):
+            r = zipf.draw(seed, 1, (b + j) * draws, draws, device=dev)
+            uniq, cnt = torch.unique(r, return_counts=True)
+            freq.index_add_(0, uniq, cnt)
+            sc = freq[uniq]
+            batches.append((r, uniq, gen.values(uniq, sc, dim, seed), sc))
+        found = torch.empty(draws, dtype=torch.uint8, device=dev)
+        hits = torch.zeros(1, dtype=torch.int64, device=dev)
+        torch.cuda.synchronize()
+        log(f"online {mode}: full after {fill_batches} batches ({time.perf_counter() - t0:.1f}s), first eviction "
+            f"at lambda {first_evict}")
+        tab.profile_start()
+        t1 = time.perf_counter()
+        keys = 0
+        for r, uniq, v, sc in batches:
+            tab.contains(r, found_out=found)
+            hits += found.sum()
+            tab.insert_or_assign(uniq, v, sc)
+            keys += uniq.numel()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t1
+        ks = tab.profile_stop()
+        up_ms = sum(ks[n][1] for n in ("upsert_probe", "upsert_owner")) / steady_batches
+        look_ms = ks["contains"][1] / ks["contains"][0] if "contains" in ks else None
+        # top-N retention
+        k, _, _, _ = tab.export_batch(with_values=False)
+        seen = torch.nonzero(freq > 0).flatten()
+        fs = freq[seen]
+        o = torch.argsort(seen, descending=True)
+        o = o[torch.argsort(fs[o], descending=True, stable=True)]
+        mark = torch.zeros(n_ids + 1, dtype=torch.bool, device=dev)
+        mark[seen[o[:cap]]] = True
+        retention = int(mark[k].sum()) / cap
+        res = dict(fill_batches=fill_batches, first_eviction_lambda=round(first_evict, 4) if first_evict else None,
+                   hit_ratio=round(int(hits.item()) / (steady_batches * draws), 4),
+                   top_n_retention=round(retention, 5), distinct_keys_per_batch=int(keys / steady_batches),
+                   upsert_bkvs=round(keys / steady_batches / up_ms / 1e6, 3),
+                   lookup_bkvs=round(draws / look_ms / 1e6, 3) if look_ms else None,
+                   upsert_kernels_ms={n: round(ks[n][1] / ks[n][0], 4) for n in ("upsert_probe", "upsert_owner")},
+                   combined_wall_bkvs=round((keys + steady_batches * draws) / wall / 1e9, 3),
+                   size=int(k.numel()))
+        log(f"online {mode}: {res}")
+        out[mode] = res
+        tab.close()
+        del batches, freq, mark, seen, fs, o, k
+        torch.cuda.empty_cache()
+    if "dual" in out and "single" in out:
+        out["dual_over_single_upsert"] = round(out["dual"]["upsert_bkvs"] / out["single"]["upsert_bkvs"], 3)
+    print(json.dumps({"online": out, "capacity": cap, "dim": dim, "zipf_alpha": 1.05, "ids": n_ids,
+                      "draws_per_batch": draws, "steady_batches": steady_batches}), flush=True)
 
 
 API_CONFIGS = (("A", 8, 27), ("B", 32, 27), ("C", 64, 26))  # (name, dim, log2 capacity), pure HBM
@@ -1003,6 +1102,9 @@ def main():
         return
     if args.triple:
         triple_run(args)
+        return
+    if args.online:
+        online_run(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()

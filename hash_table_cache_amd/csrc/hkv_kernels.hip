@@ -1464,11 +1464,14 @@ hipError_t launch_upsert(const TableView& t, uint64_t n, const InsertCall& c, ui
 }
 
 // Key-side probes need no row copy, so the group size does not follow dim:
-// 8 lanes (one 16-byte digest load each) unless overridden.
+// 8 lanes (one 16-byte digest load per line each) unless overridden.
 hipError_t launch_locate(const TableView& t, uint64_t n, const uint64_t* keys, uint64_t* ptrs_out,
                          uint8_t* found_out, uint64_t* scores_out, hipStream_t s, KernelTimer* tm) {
   const int g = (t.lanes == 4 || t.lanes == 16) ? static_cast<int>(t.lanes) : 8;
-  if (t.dual) return locate_g<kInsG, true>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+  if (t.dual) {
+    return g == 16 ? locate_g<16, true>(t, n, keys, ptrs_out, found_out, scores_out, s, tm)
+                   : locate_g<8, true>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
+  }
   switch (g) {
     case 4: return locate_g<4, false>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
     case 16: return locate_g<16, false>(t, n, keys, ptrs_out, found_out, scores_out, s, tm);
