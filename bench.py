@@ -950,7 +950,9 @@ def run_gpu(args):
 def run_extra_ops(args, tables, batch, dim, hit):
     """The other calls of the paper's §4.1 on the same tables, after the timed
     region (reported in detail only): find* and contains on the step's find
-    batches; insert_and_evict, then find_or_insert, on fresh batches of the
+    batches, and find with the stored scores returned (kernel time; 16 more
+    bytes per hit: score read and written); insert_and_evict, then
+    find_or_insert, on fresh batches of the
     upsert mix (90 % resident, 10 % new keys). Per call: median of HIP-event
     times around the call; per kernel: the library's event times."""
     import torch
@@ -988,6 +990,17 @@ def run_extra_ops(args, tables, batch, dim, hit):
             r[name] = dict(call_ms_median=round(t, 5), bkvs=round(batch / t / 1e6, 3), kernel_avg_ms=round(kavg, 5),
                            achieved_GBps=round(byts / (kavg * 1e-3) / 1e9, 1),
                            frac=round(byts / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        # find with the stored scores returned (the metric's one extra run)
+        scs = torch.empty(batch, dtype=torch.int64, device=dev)
+        tab.profile_start()
+        for s in range(reps + 2):
+            tab.find(T["finds"][s % len(T["finds"])], values_out=T["out"], found_out=found, scores_out=scs)
+        ks = tab.profile_stop()
+        kavg = ks["find"][1] / ks["find"][0]
+        byts = batch * (find_bytes_per_key(dim, hit[lam]) + 16 * hit[lam])
+        r["find_with_scores"] = dict(kernel_avg_ms=round(kavg, 5), bkvs=round(batch / kavg / 1e6, 3),
+                                     achieved_GBps=round(byts / (kavg * 1e-3) / 1e9, 1),
+                                     frac=round(byts / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
         # write calls on fresh batches of the upsert mix
         n_new = int(round(batch * args.new_frac))
         k_all, _, _, _ = tab.export_batch(with_values=False)

@@ -359,6 +359,10 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
     if (lane == 0) found[i] = 0;
     return;
   }
+  // The stored score is requested before the row, so both arrive in the
+  // same round trip.
+  uint64_t sc = 0;
+  if (scores_out && lane == 0) sc = t.scores[p];
   // Host-resident rows are read with cacheable loads: repeated (hot) keys of
   // a batch then find their rows in L2 instead of crossing the host link again.
   if (static_cast<uint64_t>(p) >= t.split) {
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
   }
   if (lane == 0) {
     found[i] = 1;
-    if (scores_out) scores_out[i] = t.scores[p];
+    if (scores_out) scores_out[i] = sc;
   }
 }
 
