@@ -1054,7 +1054,7 @@ def run_cpu_baseline(args):
 
     cap = 1 << 22
     batch = 1 << 18
-    rounds = 4
+    rounds = 16
     dim = args.dim
     lams = [float(x) for x in args.lambdas.split(",")]
     zeros = np.zeros((batch, dim), np.float32)
@@ -1086,7 +1086,8 @@ def run_cpu_baseline(args):
             secs += time.perf_counter() - t0
             ops += 2 * batch
         o.close()
-    return dict(value=ops / secs / 1e9, secs=secs, total=time.perf_counter() - t_all, cap=cap, batch=batch)
+    return dict(value=ops / secs / 1e9, secs=secs, total=time.perf_counter() - t_all, cap=cap, batch=batch,
+                rounds=rounds)
 
 
 def main():
@@ -1176,7 +1177,7 @@ def main():
             "cores": 1,
             "kind": "oracle",
             "sample": (f"single-threaded oracle, capacity 2^22 dim {args.dim} tables at lambda {args.lambdas}, "
-                       f"4 rounds of one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign "
+                       f"{cpu['rounds']} rounds of one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign "
                        f"(same resident/new mix) per lambda; {cpu['secs']:.1f}s timed of {cpu['total']:.1f}s"),
         },
         "detail": {
