@@ -845,27 +845,72 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
 // occupancy (group-uniform), this lane's 8 digest bytes and, once loaded, the
 // scores and keys of this lane's 8 slots (slots 8*lane .. 8*lane+7). Only the
 // lane owning a slot reads or writes that slot's key, score and digest.
+// The score column is loaded for a full bucket; the whole key column only
+// when a second chain key needs the hit check: a victim is chosen from the
+// scores and the keys of the slots at the lowest score alone.
 struct Bucket {
   uint32_t b;
   uint32_t occ;
   uint32_t dig0, dig1;
-  bool cols;  // sc/kc valid (group-uniform)
+  bool scols;  // sc valid (group-uniform)
+  bool kcols;  // kc valid for every slot (group-uniform)
   uint64_t sc[8];
   uint64_t kc[8];
 };
 
-__device__ __forceinline__ void bucket_load_cols(Bucket& o, const TableView& t, int lane) {
+__device__ __forceinline__ void bucket_load_scores(Bucket& o, const TableView& t, int lane) {
   const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
 #pragma unroll
   for (int u = 0; u < 8; u += 2) {
     const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(t.scores + base + u);
-    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
     o.sc[u] = a.x;
     o.sc[u + 1] = a.y;
+  }
+  o.scols = true;
+}
+
+__device__ __forceinline__ void bucket_load_keys(Bucket& o, const TableView& t, int lane) {
+  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
     o.kc[u] = c.x;
     o.kc[u + 1] = c.y;
   }
-  o.cols = true;
+  o.kcols = true;
+}
+
+// Lowest (score, key) entry of the owned full bucket (group-uniform score and
+// key, and its slot). Without the key column, the keys of the slots at the
+// lowest score are loaded (one round trip); their register copies are then
+// valid for those slots only.
+__device__ __forceinline__ int bucket_lowest(Bucket& o, const TableView& t, int lane, uint64_t* min_score,
+                                             uint64_t* min_key) {
+  if (!o.scols) bucket_load_scores(o, t, lane);
+  uint64_t ls = o.sc[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
+  const uint64_t gs = group_min<kInsG>(ls);
+  if (!o.kcols) {
+    const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (o.sc[u] == gs) o.kc[u] = t.keys[base + u];
+  }
+  uint64_t lk = ~0ull;
+  int lslot = -1;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (o.sc[u] == gs && (lslot < 0 || o.kc[u] < lk)) {
+      lk = o.kc[u];
+      lslot = lane * 8 + u;
+    }
+  }
+  const uint64_t gk = group_min<kInsG>(lslot >= 0 ? lk : ~0ull);
+  const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
+  *min_score = gs;
+  *min_key = gk;
+  return __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
 }
 
 // Writes slot s (key only when `is_new`, then digest, score) through its owner
@@ -885,13 +930,11 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
       o.dig0 = (o.dig0 & ~(0xFFu << sh)) | (d << sh);
     }
   }
-  if (o.cols) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool here = u == (s & 7);
-      o.sc[u] = here ? score : o.sc[u];
-      o.kc[u] = here ? k : o.kc[u];
-    }
+  for (int u = 0; u < 8; ++u) {
+    const bool here = u == (s & 7);
+    if (o.scols) o.sc[u] = here ? score : o.sc[u];
+    if (o.kcols) o.kc[u] = here ? k : o.kc[u];
   }
 }
 
@@ -913,7 +956,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
   };
   int hit = -1;
   if (!fresh) {
-    if (o.cols) {
+    if (o.kcols) {
       int lh = -1;
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -939,24 +982,9 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
     if (EVICT && lane == 0) st.kind[idx] = 0;
     return;
   }
-  if (!o.cols) bucket_load_cols(o, t, lane);
-  uint64_t ls = o.sc[0];
-#pragma unroll
-  for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
-  const uint64_t gs = group_min<kInsG>(ls);
-  uint64_t lk = ~0ull;
-  int lslot = -1;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (o.sc[u] == gs && (lslot < 0 || o.kc[u] < lk)) {
-      lk = o.kc[u];
-      lslot = lane * 8 + u;
-    }
-  }
-  const uint64_t gk = group_min<kInsG>(lslot >= 0 ? lk : ~0ull);
+  uint64_t gs, gk;
+  const int vs = bucket_lowest(o, t, lane, &gs, &gk);
   if (score > gs || (score == gs && k > gk)) {
-    const uint64_t vb = group_bits<kInsG>(__ballot(lslot >= 0 && lk == gk));
-    const int vs = __shfl(lslot, __ffsll(static_cast<unsigned long long>(vb)) - 1, kInsG);
     if constexpr (EVICT) {
       // the victim's row is staged (read by the lanes that wrote it, if this
       // kernel did) before the new row overwrites it
@@ -1026,14 +1054,20 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     const uint64_t score = s_score[e];
     Bucket o;
     o.b = tgt & ~kFullBit;
-    o.cols = false;
+    o.scols = false;
+    o.kcols = false;
     uint32_t head = 0;
     if (lane == 0) head = __hip_atomic_load(t.head + o.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
     RowRegs rr;
     const float* row = values + static_cast<uint64_t>(i) * t.dim;
     if (in_regs) row_regs_load(rr, row, t.dim, lane);
-    if (tgt & kFullBit) bucket_load_cols(o, t, lane);
+    if (tgt & kFullBit) {
+      bucket_load_scores(o, t, lane);
+      // dual mode records the bucket's lowest entry at the end, which needs
+      // every key once the lowest slot has been replaced
+      if (DUAL) bucket_load_keys(o, t, lane);
+    }
     o.dig0 = dv.x;
     o.dig1 = dv.y;
     uint32_t c = 8 - __builtin_popcount(zero_byte_bits(o.dig0)) - __builtin_popcount(zero_byte_bits(o.dig1));
@@ -1048,6 +1082,9 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
     for (uint64_t step = 0; cur != i && cur < n && step < n; ++step) {
+      // a full bucket's key column, for the hit checks of the chain's keys,
+      // arrives with the first chain key's inputs
+      if (o.scols && !o.kcols) bucket_load_keys(o, t, lane);
       const uint32_t after = next[cur];
       const uint64_t kc = keys[cur];
       const uint64_t scc = scores[cur];
@@ -1058,15 +1095,8 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     }
     if (DUAL && o.occ >= kSlots) {
       // record the bucket's lowest (score, key) for later dual-bucket choices
-      if (!o.cols) bucket_load_cols(o, t, lane);
-      uint64_t ls = o.sc[0];
-#pragma unroll
-      for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
-      const uint64_t gs = group_min<kInsG>(ls);
-      uint64_t lk = ~0ull;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lk = (o.sc[u] == gs && o.kc[u] < lk) ? o.kc[u] : lk;
-      const uint64_t gk = group_min<kInsG>(lk);
+      uint64_t gs, gk;
+      (void)bucket_lowest(o, t, lane, &gs, &gk);
       if (lane == 0) {
         ulonglong2 rec;
         rec.x = gs;
