@@ -157,6 +157,67 @@ def test_lambda_sweep_reduced_exact(lam):
     check_find(tab, o, q)
 
 
+def one_new_key_per_bucket(o, seed, stream, start, buckets):
+    """One never-inserted key routed to each of `buckets` distinct buckets
+    (drawn from a unique-key stream; returns the keys and the next cursor)."""
+    picked = {}
+    cur = start
+    while len(picked) < buckets:
+        cand = np_u64(gen.unique_keys(seed, stream, cur, 4 * buckets))
+        cur += 4 * buckets
+        b1, _, _ = o.route(cand)
+        for k, b in zip(cand.tolist(), b1.tolist()):
+            if b not in picked:
+                picked[b] = k
+    keys = np.array([picked[b] for b in sorted(picked)], dtype=np.uint64)
+    return torch.from_numpy(keys.view(np.int64)).to(dev()), cur
+
+
+@pytest.mark.parametrize("resident_scores", ["all_equal", "spread"])
+def test_single_new_key_per_full_bucket_exact(resident_scores):
+    """Every batch sends exactly one new key to each bucket of a full table,
+    so each bucket's chain is that one key and its owner decides eviction
+    from the score column and the keys tied at the lowest score. Residents
+    all share one score ("all_equal": every slot is tied) or carry spread
+    scores with a few ties ("spread"); the new keys' scores equal the lowest
+    resident score in half of the batches (admitted iff the key outranks the
+    lowest key) and exceed it in the others. Contents match the oracle after
+    every batch."""
+    H = hkv()
+    C, D = 1 << 14, 16
+    nbk = C // SLOTS
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    seed = 0x484B56000000F11E
+    cur = 0
+    step = 0
+    while o.size() < C:
+        step += 1
+        n = C
+        keys = gen.unique_keys(seed, 1, cur, n, device=dev())
+        cur += n
+        if resident_scores == "all_equal":
+            sc = torch.full((n,), 100, dtype=torch.int64, device=dev())
+        else:
+            sc = 100 + (gen.counter_words(seed, 2, cur, n, dev()) & 7)  # 8 score levels, many ties
+        vals = gen.values(keys, step, D)
+        tab.insert_or_assign(keys, vals, sc)
+        o.insert_or_assign(np_u64(keys), np_u64(sc), values=vals.cpu().numpy())
+    assert_same_contents(tab, o)
+    ncur = 0
+    for j in range(6):
+        step += 1
+        keys, ncur = one_new_key_per_bucket(o, seed, 3, ncur, nbk)
+        lowest = int(o.export()["scores"].min())
+        base = lowest if j % 2 == 0 else lowest + 1
+        sc = torch.full((keys.numel(),), base, dtype=torch.int64, device=dev())
+        vals = gen.values(keys, step, D)
+        tab.insert_or_assign(keys, vals, sc)
+        o.insert_or_assign(np_u64(keys), np_u64(sc), values=vals.cpu().numpy())
+        assert_same_contents(tab, o)
+    check_find(tab, o, mixed_queries(o, 4096, 0.5, seed, 9))
+
+
 def test_mixed_find_assign_upsert_reduced_exact():
     """Reader / updater / inserter steps at lambda = 1 (2^17 slots, dim 64):
     per step a find, an assign of resident keys, an upsert of half fresh and
