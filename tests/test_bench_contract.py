@@ -1,0 +1,57 @@
+"""CPU checks of bench.py's contract: the one-GPU exit, the algorithmic byte
+counts behind its roofline figures, and the code hash that ties a committed
+rocprofv3 summary to the kernel source it measured."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("dim,expected", [(64, 609.0), (32, 378.6)])
+def test_find_bytes_match_the_derived_roofline(dim, expected):
+    # one 128-byte digest line, 8-byte key in, half a false-positive key
+    # compare, and for each hit (90 %) the 8-byte key plus the row read and
+    # written: 141 + 8h + 8Dh bytes per key
+    assert bench.find_bytes_per_key(dim, 0.9) == pytest.approx(expected)
+
+
+def test_write_bytes_count_each_access_once():
+    d = 64
+    # resident key: key, line, false positives, candidate key, row in, score
+    # in, row write, score write
+    assert bench.probe_bytes_per_key(d, 1.0) == 8 + 128 + 4 + 8 + 4 * d + 8 + 4 * d + 8
+    # missing key: key, line, false positives, chain link
+    assert bench.probe_bytes_per_key(d, 0.0) == 8 + 128 + 4 + 8
+    assert bench.assign_bytes_per_key(d) == 164 + 8 * d
+    # owner kernel: the chain word of every key, nothing more without new keys
+    assert bench.owner_bytes_per_key(d, 1.0, 1.0) == 4
+    # an evicting new key adds the score column and one tied key
+    assert (bench.owner_bytes_per_key(d, 0.0, 1.0) - bench.owner_bytes_per_key(d, 0.0, 0.0)) == 1024 + 8
+
+
+def test_code_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
+    src = open(bench.KERNEL_SOURCE, encoding="utf-8").read()
+    h0 = bench.kernel_code_sha256()
+    commented = tmp_path / "k.hip"
+    commented.write_text("// a comment\n/* block\n comment */\n" + src.replace(";", ";  ") + "\n\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(commented))
+    assert bench.kernel_code_sha256() == h0
+    changed = tmp_path / "k2.hip"
+    changed.write_text(src.replace("kBlock = 256", "kBlock = 512", 1))
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(changed))
+    assert bench.kernel_code_sha256() != h0
