@@ -344,16 +344,12 @@ __device__ __forceinline__ void probe_many(const TableView& t, const uint64_t (&
 
 // ---------------------------------------------------------------- readers --
 
+// find for key i by the G lanes of a group (Algorithm 1): probe, then the
+// row, found flag and (optionally) score of a hit; a miss writes found = 0.
 template <int G, bool V4, bool DUAL, bool NT>
-__global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
-                                                      const uint64_t* __restrict__ keys,
-                                                      float* __restrict__ out,
-                                                      uint8_t* __restrict__ found,
-                                                      uint64_t* __restrict__ scores_out) {
-  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
-  const int lane = static_cast<int>(threadIdx.x & (G - 1));
-  if (i >= n) return;  // groups are lane-aligned, so a whole group leaves together
-  const uint64_t k = keys[i];
+__device__ __forceinline__ void find_one(const TableView& t, uint64_t i, uint64_t k, float* __restrict__ out,
+                                         uint8_t* __restrict__ found, uint64_t* __restrict__ scores_out,
+                                         int lane) {
   const int64_t p = probe<G, DUAL, NT>(t, k, lane);
   if (p < 0) {
     if (lane == 0) found[i] = 0;
@@ -373,6 +369,58 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
   if (lane == 0) {
     found[i] = 1;
     if (scores_out) scores_out[i] = sc;
+  }
+}
+
+template <int G, bool V4, bool DUAL, bool NT>
+__global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
+                                                      const uint64_t* __restrict__ keys,
+                                                      float* __restrict__ out,
+                                                      uint8_t* __restrict__ found,
+                                                      uint64_t* __restrict__ scores_out) {
+  const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
+  if (i >= n) return;  // groups are lane-aligned, so a whole group leaves together
+  find_one<G, V4, DUAL, NT>(t, i, keys[i], out, found, scores_out, lane);
+}
+
+// find when value rows live in host memory. The XCDs of the GPU have an L2
+// each, and workgroups are handed to the XCDs in turn (workgroup w to XCD
+// w mod 8), so a hot key whose draws land in workgroups of several XCDs has
+// its row fetched over the host link once per XCD. Here every chunk of
+// kXcdChunk keys is served by kXcds consecutive workgroups, and workgroup x of
+// a chunk serves only the chunk's keys whose hash bits 56..58 equal x: all
+// draws of a key meet in one XCD's L2 and its row crosses the link once.
+// Correctness does not depend on the placement (every key is served by
+// exactly one workgroup); only the hit rate of the L2s does. Each workgroup
+// reads the whole chunk's keys (8 bytes per key per workgroup, from L2).
+constexpr int kXcds = 8;
+
+template <int G, bool V4, bool DUAL, bool NT>
+__global__ __launch_bounds__(kBlock) void find_xcd_kernel(TableView t, uint64_t n,
+                                                          const uint64_t* __restrict__ keys,
+                                                          float* __restrict__ out,
+                                                          uint8_t* __restrict__ found,
+                                                          uint64_t* __restrict__ scores_out) {
+  constexpr int kGroups = kBlock / G;
+  constexpr int kXcdChunk = kGroups * kXcds;  // on average one key per group
+  __shared__ uint32_t s_idx[kXcdChunk];
+  __shared__ uint32_t s_count;
+  const uint32_t x = blockIdx.x % kXcds;
+  const uint64_t c0 = static_cast<uint64_t>(blockIdx.x / kXcds) * kXcdChunk;
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < static_cast<uint32_t>(kXcdChunk); j += kBlock) {
+    const uint64_t i = c0 + j;
+    if (i < n && static_cast<uint32_t>(fmix64(keys[i]) >> 56 & (kXcds - 1)) == x)
+      s_idx[atomicAdd(&s_count, 1u)] = j;
+  }
+  __syncthreads();
+  const uint32_t mine = s_count;
+  const int lane = static_cast<int>(threadIdx.x & (G - 1));
+  for (uint32_t e = threadIdx.x / G; e < mine; e += kGroups) {
+    const uint64_t i = c0 + s_idx[e];
+    find_one<G, V4, DUAL, NT>(t, i, keys[i], out, found, scores_out, lane);
   }
 }
 
@@ -1335,6 +1383,14 @@ int lanes_for(const TableView& t) {
 template <int G, bool V4, bool DUAL>
 hipError_t find_g(const TableView& t, uint64_t n, const uint64_t* keys, float* out, uint8_t* found,
                   uint64_t* sc, hipStream_t s, KernelTimer* tm) {
+  if (t.split < t.nb * kSlots) {
+    // some rows in host memory: keys partitioned over the XCDs
+    const uint64_t chunk = static_cast<uint64_t>(kBlock / G) * kXcds;
+    const uint64_t blocks = (n + chunk - 1) / chunk * kXcds;
+    HKV_LAUNCH(tm, "find", (find_xcd_kernel<G, V4, DUAL, true>), dim3(static_cast<uint32_t>(blocks)),
+               dim3(kBlock), s, t, n, keys, out, found, sc);
+    return hipGetLastError();
+  }
   HKV_LAUNCH(tm, "find", (find_kernel<G, V4, DUAL, true>), dim3(grid_for(n * G)), dim3(kBlock), s, t, n,
              keys, out, found, sc);
   return hipGetLastError();

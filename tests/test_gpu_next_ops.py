@@ -506,6 +506,26 @@ def test_host_rows_read_again_after_updates(budget_buckets):
     assert_same_contents(tab, o)
 
 
+@pytest.mark.parametrize("D,dual", [(5, False), (33, False), (64, True)])
+def test_host_rows_find_partitioned_over_xcds(D, dual):
+    """With rows in host memory, find serves each chunk of keys with one
+    workgroup per XCD, each taking the keys of its hash class. Ragged batch
+    sizes, repeated keys, odd dims (scalar row copies) and dual mode must give
+    the oracle's flags, rows and scores exactly."""
+    H = hkv()
+    C = 24 * SLOTS
+    tab = H.HashTable(C, D, dual_bucket=dual, values_on_host=True, serial_insert=dual)
+    o = oracle.OracleTable(C, D, dual=dual)
+    fill(tab, o, C, D, 41, 1, batch=1100)
+    from test_gpu_parity import check_find
+
+    for n, seed in ((1, 3), (257, 4), (3001, 5)):
+        q = mixed_queries(o, n, 0.7, seed, 60 + seed)
+        check_find(tab, o, q)
+    hot = sample_present(o, 16, 8)
+    check_find(tab, o, to_dev(np.repeat(hot, 40)))
+
+
 @pytest.mark.parametrize("D", [1, 5, 33])
 def test_insert_and_evict_and_find_or_insert_odd_dims(D):
     """Rows that are not a whole number of 16-byte pieces take the scalar copy
