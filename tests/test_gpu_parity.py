@@ -452,6 +452,39 @@ def test_values_on_host_tiered_mode():
     assert_same_contents(tab, o)
 
 
+def test_export_then_reinsert_restores_the_table():
+    """Checkpoint and resume through the public calls: export a full table
+    (after evictions) in slot ranges, destroy it, insert the exported keys,
+    rows and scores into a new table in shuffled order. Every bucket held at
+    most 128 entries, all routed to it, so the new table has the same
+    per-bucket sets, rows and scores as the oracle that followed the first."""
+    H = hkv()
+    C, D = 48 * SLOTS, 16
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    seed = 0x484B5600000C4EC7
+    for step in range(1, 5):
+        keys = gen.unique_keys(seed, 1, (step - 1) * 3000, 3000, device=dev())
+        sc = 10 * step + (gen.counter_words(seed, 2, step * 3000, 3000, dev()) & 7)
+        vals = gen.values(keys, step, D)
+        tab.insert_or_assign(keys, vals, sc)
+        o.insert_or_assign(np_u64(keys), np_u64(sc), values=vals.cpu().numpy())
+    assert tab.size() == C
+    parts = [tab.export_batch(off, 1000) for off in range(0, C, 1000)]
+    k = torch.cat([q[0] for q in parts])
+    v = torch.cat([q[1] for q in parts])
+    s_ = torch.cat([q[2] for q in parts])
+    tab.close()
+    assert k.numel() == C
+    order = torch.from_numpy(np.random.default_rng(5).permutation(C)).to(dev())
+    k, v, s_ = k[order].contiguous(), v[order].contiguous(), s_[order].contiguous()
+    fresh = H.HashTable(C, D)
+    fresh.insert_or_assign(k, v, s_)
+    assert_same_contents(fresh, o)
+    check_find(fresh, o, mixed_queries(o, 5000, 0.8, seed, 3))
+    fresh.close()
+
+
 def test_export_ranges_partition_the_table():
     H = hkv()
     C, D = 16 * SLOTS, 2
