@@ -501,6 +501,24 @@ def test_export_ranges_partition_the_table():
     assert parts == whole and len(whole) == tab.size()
 
 
+def test_allocation_failure_is_reported_and_leaves_the_device_usable():
+    """A table whose rows cannot fit in HBM (2^20 slots of 2^20 floats: 4 TiB)
+    fails with HKV_ENOMEM and frees what it had allocated; a normal table
+    created right after works."""
+    H = hkv()
+    with pytest.raises(H.HkvError) as ei:
+        H.HashTable(1 << 20, 1 << 20)
+    assert ei.value.status == -2
+    assert "capacity" in str(ei.value)
+    tab = H.HashTable(4 * SLOTS, 8)
+    k = torch.arange(1, 301, dtype=torch.int64, device=dev())
+    tab.insert_or_assign(k, gen.values(k, 1, 8), torch.ones(300, dtype=torch.int64, device=dev()))
+    _, found, _ = tab.find(k)
+    torch.cuda.synchronize()
+    assert int(found.sum()) == min(300, tab.size()) and tab.size() > 0
+    tab.close()
+
+
 def test_invalid_pointers_are_rejected():
     H = hkv()
     tab = H.HashTable(SLOTS, 4)
