@@ -900,8 +900,9 @@ struct Bucket {
   uint32_t b;
   uint32_t occ;
   uint32_t dig0, dig1;
-  bool scols;  // sc valid (group-uniform)
-  bool kcols;  // kc valid for every slot (group-uniform)
+  bool scols;     // sc valid (group-uniform)
+  bool kcols;     // kc valid for every slot (group-uniform)
+  uint32_t kval;  // this lane's slots whose kc is valid (bit u: slot 8*lane+u)
   uint64_t sc[8];
   uint64_t kc[8];
 };
@@ -926,12 +927,12 @@ __device__ __forceinline__ void bucket_load_keys(Bucket& o, const TableView& t, 
     o.kc[u + 1] = c.y;
   }
   o.kcols = true;
+  o.kval = 0xFFu;
 }
 
 // Lowest (score, key) entry of the owned full bucket (group-uniform score and
-// key, and its slot). Without the key column, the keys of the slots at the
-// lowest score are loaded (one round trip); their register copies are then
-// valid for those slots only.
+// key, and its slot). Keys of the slots at the lowest score that are not in
+// registers yet are loaded (one round trip, none when all are known).
 __device__ __forceinline__ int bucket_lowest(Bucket& o, const TableView& t, int lane, uint64_t* min_score,
                                              uint64_t* min_key) {
   if (!o.scols) bucket_load_scores(o, t, lane);
@@ -940,10 +941,21 @@ __device__ __forceinline__ int bucket_lowest(Bucket& o, const TableView& t, int 
   for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
   const uint64_t gs = group_min<kInsG>(ls);
   if (!o.kcols) {
-    const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+    // a lane with an unknown key at the lowest score reads all 8 of its keys:
+    // the same 64-byte burst as one key, in four 16-byte loads
+    bool need = false;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (o.sc[u] == gs) o.kc[u] = t.keys[base + u];
+    for (int u = 0; u < 8; ++u) need |= o.sc[u] == gs && !((o.kval >> u) & 1u);
+    if (need) {
+      const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
+        o.kc[u] = c.x;
+        o.kc[u + 1] = c.y;
+      }
+      o.kval = 0xFFu;
+    }
   }
   uint64_t lk = ~0ull;
   int lslot = -1;
@@ -982,8 +994,9 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
   for (int u = 0; u < 8; ++u) {
     const bool here = u == (s & 7);
     if (o.scols) o.sc[u] = here ? score : o.sc[u];
-    if (o.kcols) o.kc[u] = here ? k : o.kc[u];
+    o.kc[u] = here ? k : o.kc[u];
   }
+  o.kval |= 1u << (s & 7);
 }
 
 // Algorithm 2 for one key against the owned bucket, with the input row already
@@ -1104,18 +1117,14 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     o.b = tgt & ~kFullBit;
     o.scols = false;
     o.kcols = false;
+    o.kval = 0;
     uint32_t head = 0;
     if (lane == 0) head = __hip_atomic_load(t.head + o.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
     RowRegs rr;
     const float* row = values + static_cast<uint64_t>(i) * t.dim;
     if (in_regs) row_regs_load(rr, row, t.dim, lane);
-    if (tgt & kFullBit) {
-      bucket_load_scores(o, t, lane);
-      // dual mode records the bucket's lowest entry at the end, which needs
-      // every key once the lowest slot has been replaced
-      if (DUAL) bucket_load_keys(o, t, lane);
-    }
+    if (tgt & kFullBit) bucket_load_scores(o, t, lane);
     o.dig0 = dv.x;
     o.dig1 = dv.y;
     uint32_t c = 8 - __builtin_popcount(zero_byte_bits(o.dig0)) - __builtin_popcount(zero_byte_bits(o.dig1));
