@@ -508,7 +508,9 @@ def online_run(args) -> None:
     (key = id), 2^20 draws per batch deduplicated, score = the key's
     cumulative frequency (LFU), until it is full, then 200 more batches.
     Before each batch's insert_or_assign, contains() looks up the batch's raw
-    draws: the cache hit ratio. Reported per mode: batches to fill,
+    draws: the cache hit ratio. find (rows copied out) is timed on a batch of
+    raw draws once the table is half full and again at the end. Reported per
+    mode: batches to fill,
     load factor at the first eviction (first batch that adds fewer keys than
     it has new ones), hit ratio and kernel-timed rates over the 200 batches,
     and top-N retention after them (N = capacity; ideal = the N highest
@@ -527,7 +529,19 @@ def online_run(args) -> None:
         t0 = time.perf_counter()
         tab = H.HashTable(cap, dim, dual_bucket=mode == "dual")
         freq = torch.zeros(n_ids + 1, dtype=torch.int64, device=dev)
-        b, size, first_evict = 0, 0, None
+        rows_out = torch.empty((draws, dim), dtype=torch.float32, device=dev)
+        found_out = torch.empty(draws, dtype=torch.uint8, device=dev)
+
+        def find_ms(q):
+            # find (rows copied out) on a batch of raw draws: kernel time
+            tab.find(q, values_out=rows_out, found_out=found_out)
+            tab.profile_start()
+            for _ in range(3):
+                tab.find(q, values_out=rows_out, found_out=found_out)
+            ks = tab.profile_stop()
+            return ks["find"][1] / ks["find"][0]
+
+        b, size, first_evict, find_half = 0, 0, None, None
         while size < cap:
             r = zipf.draw(seed, 1, b * draws, draws, device=dev)
             uniq, cnt = torch.unique(r, return_counts=True)
@@ -540,6 +554,8 @@ def online_run(args) -> None:
                 first_evict = size / cap
             size = new_size
             b += 1
+            if find_half is None and size >= cap // 2:
+                find_half = (size / cap, find_ms(zipf.draw(seed, 1, b * draws, draws, device=dev)))
             if b > 4000:
                 raise RuntimeError("table never reached full capacity")
         fill_batches = b
@@ -569,6 +585,7 @@ def online_run(args) -> None:
         ks = tab.profile_stop()
         up_ms = sum(ks[n][1] for n in ("upsert_probe", "upsert_owner")) / steady_batches
         look_ms = ks["contains"][1] / ks["contains"][0] if "contains" in ks else None
+        find_full = find_ms(batches[-1][0])
         # top-N retention
         k, _, _, _ = tab.export_batch(with_values=False)
         seen = torch.nonzero(freq > 0).flatten()
@@ -583,13 +600,15 @@ def online_run(args) -> None:
                    top_n_retention=round(retention, 5), distinct_keys_per_batch=int(keys / steady_batches),
                    upsert_bkvs=round(keys / steady_batches / up_ms / 1e6, 3),
                    lookup_bkvs=round(draws / look_ms / 1e6, 3) if look_ms else None,
+                   find_bkvs_at_half=round(draws / find_half[1] / 1e6, 3), half_lambda=round(find_half[0], 4),
+                   find_bkvs_full=round(draws / find_full / 1e6, 3),
                    upsert_kernels_ms={n: round(ks[n][1] / ks[n][0], 4) for n in ("upsert_probe", "upsert_owner")},
                    combined_wall_bkvs=round((keys + steady_batches * draws) / wall / 1e9, 3),
                    size=int(k.numel()))
         log(f"online {mode}: {res}")
         out[mode] = res
         tab.close()
-        del batches, freq, mark, seen, fs, o, k
+        del batches, freq, mark, seen, fs, o, k, rows_out, found_out
         torch.cuda.empty_cache()
     if "dual" in out and "single" in out:
         out["dual_over_single_upsert"] = round(out["dual"]["upsert_bkvs"] / out["single"]["upsert_bkvs"], 3)
