@@ -961,9 +961,12 @@ def run_gpu(args):
     for T in tables:
         T["tab"].close()
     busy = sum(v[1] for v in kstats.values())
+    # algorithmic bytes of one whole step (every kernel on every table)
+    step_bytes = sum(bytes_per_launch[name] for name in kstats if name in bytes_per_launch) * len(tables)
     return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
                 dominant=dominant, h=h_avg, gpu_busy_frac=busy / (wall_timed_kernels * 1e3),
-                wall_timed_kernels=wall_timed_kernels, insert_new=insert_new, extra_ops=extra_ops)
+                wall_timed_kernels=wall_timed_kernels, insert_new=insert_new, extra_ops=extra_ops,
+                step_bytes=step_bytes)
 
 
 def run_extra_ops(args, tables, batch, dim, hit):
@@ -1217,6 +1220,11 @@ def main():
                       / (1 << 20) / g["kernels"]["upsert_probe"]["avg_ms"], 4)
                 if g["pattern"] and "upsert_probe" in g["kernels"] else None),
             "dominant_frac_of_copy": round(g["kernels"][g["dominant"]]["achieved_GBps"] / g["copy_GBps"], 4),
+            # the whole workload against the HBM peak: algorithmic bytes of all
+            # kernels of a step over the plain (untimed-kernel) step time
+            "step_algorithmic_bytes": round(g["step_bytes"]),
+            "step_algorithmic_GBps": round(g["step_bytes"] / (g["wall"] / args.steps) / 1e9, 1),
+            "step_frac_of_hbm_peak": round(g["step_bytes"] / (g["wall"] / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
             "hit_rate": round(g["h"], 4),
         },
     }
