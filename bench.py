@@ -624,8 +624,10 @@ def api_sweep(args) -> None:
     configurations (A: dim 8, 2^27 slots; B: dim 32, 2^27; C: dim 64, 2^26)
     at each load factor of --api-lambdas, 2^batch_log2-key batches: find (90 % resident), find*,
     contains, assign (resident keys), insert_or_assign, insert_and_evict and
-    find_or_insert (90 % resident, 10 % new keys). 2 warm-up and 10 timed
-    batches per call; rate = keys / kernel time per call (library events).
+    find_or_insert (90 % resident, 10 % new keys); 2 warm-up and 10 timed
+    batches per call. Last, insert_or_assign of all-new keys, 2 warm-up and 3
+    timed batches (lambda_end shows the drift). Rate = keys / kernel time per
+    call (library events).
     Prints one JSON line."""
     import torch
 
@@ -654,6 +656,12 @@ def api_sweep(args) -> None:
             u = gen.shuffle(u, SEED, 700 + j)
             writes.append((u, gen.values(u, 2000 + j, dim, SEED),
                            torch.full((batch,), step + j, dtype=torch.int64, device=dev)))
+        # all-new keys (the paper's insert_or_assign measurement: at lambda = 1
+        # every insert evicts); few batches, so the load factor drifts little
+        new_reps = 5
+        fresh = [gen.unique_keys(SEED, 614, j * batch, batch, device=dev) for j in range(new_reps)]
+        fresh = [(u, gen.values(u, 3000 + j, dim, SEED), torch.full((batch,), step + 4 * reps + j, dtype=torch.int64,
+                                                                     device=dev)) for j, u in enumerate(fresh)]
         vals = torch.empty((batch, dim), dtype=torch.float32, device=dev)
         found = torch.empty(batch, dtype=torch.uint8, device=dev)
         ptrs = torch.empty(batch, dtype=torch.int64, device=dev)
@@ -668,24 +676,26 @@ def api_sweep(args) -> None:
             "insert_and_evict": lambda j: tab.insert_and_evict(*writes[reps + j], out=ev),
             "find_or_insert": lambda j: tab.find_or_insert(writes[2 * reps + j][0], writes[2 * reps + j][1],
                                                            writes[2 * reps + j][2], found_out=found),
+            "insert_or_assign_new_keys": lambda j: tab.insert_or_assign(*fresh[j]),
         }
         res = {}
         for api, call in calls.items():
+            n_calls = new_reps if api == "insert_or_assign_new_keys" else reps
             for j in range(2):
                 call(j)
             torch.cuda.synchronize()
             tab.profile_start()
-            for j in range(2, reps):
+            for j in range(2, n_calls):
                 call(j)
             ks = tab.profile_stop()
-            per_call = sum(v[1] for v in ks.values()) / (reps - 2)
+            per_call = sum(v[1] for v in ks.values()) / (n_calls - 2)
             keys = n_hit if api == "assign" else batch
             res[api] = round(keys / per_call / 1e6, 3)
         res["lambda_end"] = round(tab.size() / cap, 4)
         out[f"{name}: dim {dim}, 2^{lg} slots, lambda {lam}"] = res
         log(f"config {name} lambda {lam}: {res}")
         tab.close()
-        del finds, writes
+        del finds, writes, fresh
         torch.cuda.empty_cache()
     print(json.dumps({"api_sweep_bkvs": out, "batch": batch}), flush=True)
 
