@@ -1033,6 +1033,19 @@ def run_extra_ops(args, tables, batch, dim, hit):
         r["find_with_scores"] = dict(kernel_avg_ms=round(kavg, 5), bkvs=round(batch / kavg / 1e6, 3),
                                      achieved_GBps=round(byts / (kavg * 1e-3) / 1e9, 1),
                                      frac=round(byts / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        # export of the whole table with rows (checkpointing, §4.1): kernel time
+        tab.export_batch(with_values=True)
+        torch.cuda.empty_cache()
+        tab.profile_start()
+        ek, ev_, es_, ep_ = tab.export_batch(with_values=True)
+        ks = tab.profile_stop()
+        ex_ms = ks["export"][1] / ks["export"][0]
+        ex_bytes = ek.numel() * (8 + 8 + 4 * dim) * 2 + tab.capacity // 128 * 4  # read + write, occupancy words
+        r["export_with_rows"] = dict(entries=int(ek.numel()), kernel_ms=round(ex_ms, 4),
+                                     bkvs=round(ek.numel() / ex_ms / 1e6, 3),
+                                     GBps=round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1))
+        del ek, ev_, es_, ep_
+        torch.cuda.empty_cache()
         # write calls on fresh batches of the upsert mix
         n_new = int(round(batch * args.new_frac))
         k_all, _, _, _ = tab.export_batch(with_values=False)

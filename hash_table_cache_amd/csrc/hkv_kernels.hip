@@ -478,6 +478,17 @@ __global__ __launch_bounds__(kBlock) void size_kernel(const uint32_t* __restrict
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0; }
 
+// export (§4.1): the occupied slots of positions [begin, end), compacted in
+// unspecified order. Slots fill in order and nothing is erased, so the
+// occupied slots of a bucket are [0, occ): the part of a bucket inside the
+// range is one run of consecutive slots whose rows are one run of memory. A
+// block takes kExportBuckets consecutive buckets, reserves room for all their
+// occupied slots with one atomic add (one per wave serialized on the single
+// counter: 12 ms for 2^26 slots), and its waves copy one bucket's run at a
+// time: keys, scores and positions one slot per lane, the rows as one
+// contiguous copy shared by the 64 lanes.
+constexpr int kExportBuckets = 128;
+
 template <bool V4>
 __global__ __launch_bounds__(kBlock) void export_kernel(TableView t, uint64_t begin, uint64_t end,
                                                         uint64_t* __restrict__ keys_out,
@@ -485,20 +496,80 @@ __global__ __launch_bounds__(kBlock) void export_kernel(TableView t, uint64_t be
                                                         uint64_t* __restrict__ scores_out,
                                                         uint64_t* __restrict__ pos_out,
                                                         unsigned long long* count) {
-  const uint64_t p = begin + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  bool live = false;
-  if (p < end) live = (p & (kSlots - 1)) < t.occ[p / kSlots];
-  const uint64_t bal = __ballot(live);
-  const int lane = wave_lane();
-  unsigned long long base = 0;
-  if (lane == 0 && bal) base = atomicAdd(count, static_cast<unsigned long long>(__popcll(bal)));
-  base = __shfl(base, 0, 64);
-  if (!live) return;
-  const uint64_t j = base + __popcll(bal & ((1ull << lane) - 1));
-  keys_out[j] = t.keys[p];
-  if (scores_out) scores_out[j] = t.scores[p];
-  if (pos_out) pos_out[j] = p;
-  if (values_out) copy_row<1, V4, false>(values_out + j * t.dim, row_of(t, p), t.dim, 0);
+  __shared__ uint32_t s_lo[kExportBuckets];   // first slot of the bucket's run
+  __shared__ uint32_t s_n[kExportBuckets];    // its length
+  __shared__ uint32_t s_off[kExportBuckets];  // its offset among the block's entries
+  __shared__ unsigned long long s_base;
+  const uint64_t b_first = begin / kSlots;
+  const uint64_t b_end = (end + kSlots - 1) / kSlots;
+  const uint64_t b0 = b_first + static_cast<uint64_t>(blockIdx.x) * kExportBuckets;
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  if (threadIdx.x < 64) {
+    // the first wave: runs of buckets 2*lane and 2*lane+1, then their offsets
+    uint32_t lo[2], n[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t b = b0 + 2 * lane + h;
+      lo[h] = 0;
+      n[h] = 0;
+      if (b < b_end) {
+        const uint64_t first = b * kSlots;
+        lo[h] = begin > first ? static_cast<uint32_t>(begin - first) : 0u;
+        const uint32_t hi = end < first + kSlots ? static_cast<uint32_t>(end - first) : static_cast<uint32_t>(kSlots);
+        const uint32_t occ = t.occ[b];
+        const uint32_t top = occ < hi ? occ : hi;
+        n[h] = top > lo[h] ? top - lo[h] : 0u;
+      }
+    }
+    uint32_t sum = n[0] + n[1];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(sum, o, 64);
+      if (lane >= o) sum += y;
+    }
+    const uint32_t excl = sum - n[0] - n[1];
+    s_lo[2 * lane] = lo[0];
+    s_lo[2 * lane + 1] = lo[1];
+    s_n[2 * lane] = n[0];
+    s_n[2 * lane + 1] = n[1];
+    s_off[2 * lane] = excl;
+    s_off[2 * lane + 1] = excl + n[0];
+    if (lane == 63) s_base = sum ? atomicAdd(count, static_cast<unsigned long long>(sum)) : 0ull;
+  }
+  __syncthreads();
+  const unsigned long long base = s_base;
+  for (int q = static_cast<int>(threadIdx.x >> 6); q < kExportBuckets; q += kBlock / 64) {
+    const uint32_t n = s_n[q];
+    if (n == 0) continue;
+    const uint64_t p0 = (b0 + q) * kSlots + s_lo[q];
+    const uint64_t j0 = base + s_off[q];
+    for (uint32_t e = lane; e < n; e += 64) {
+      keys_out[j0 + e] = t.keys[p0 + e];
+      if (scores_out) scores_out[j0 + e] = t.scores[p0 + e];
+      if (pos_out) pos_out[j0 + e] = p0 + e;
+    }
+    if (!values_out) continue;
+    // the run's rows: n * dim consecutive floats (one bucket's rows share a region)
+    const float* src = row_of(t, p0);
+    float* dst = values_out + j0 * t.dim;
+    const uint64_t total = static_cast<uint64_t>(n) * t.dim;
+    if constexpr (V4) {
+      const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+      f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+      const uint64_t n4 = total >> 2;
+      for (uint64_t c = lane; c < n4; c += 4 * 64) {
+        f32x4 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (c + r * 64 < n4) v[r] = s4[c + r * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (c + r * 64 < n4) d4[c + r * 64] = v[r];
+      }
+    } else {
+      for (uint64_t c = lane; c < total; c += 64) dst[c] = src[c];
+    }
+  }
 }
 
 // --------------------------------------------------------------- updaters --
@@ -1593,12 +1664,14 @@ hipError_t launch_export(const TableView& t, uint64_t begin, uint64_t end, uint6
                          unsigned long long* count_out, bool vec4, hipStream_t s, KernelTimer* tm) {
   HKV_LAUNCH(tm, "zero", zero_u64_kernel, dim3(1), dim3(1), s, count_out);
   if (end > begin) {
+    const uint64_t buckets = (end + kSlots - 1) / kSlots - begin / kSlots;
+    const dim3 grid(static_cast<uint32_t>((buckets + kExportBuckets - 1) / kExportBuckets));
     if (vec4)
-      HKV_LAUNCH(tm, "export", export_kernel<true>, dim3(grid_for(end - begin)), dim3(kBlock), s, t, begin,
-                 end, keys_out, values_out, scores_out, pos_out, count_out);
+      HKV_LAUNCH(tm, "export", export_kernel<true>, grid, dim3(kBlock), s, t, begin, end, keys_out, values_out,
+                 scores_out, pos_out, count_out);
     else
-      HKV_LAUNCH(tm, "export", export_kernel<false>, dim3(grid_for(end - begin)), dim3(kBlock), s, t, begin,
-                 end, keys_out, values_out, scores_out, pos_out, count_out);
+      HKV_LAUNCH(tm, "export", export_kernel<false>, grid, dim3(kBlock), s, t, begin, end, keys_out, values_out,
+                 scores_out, pos_out, count_out);
   }
   return hipGetLastError();
 }
