@@ -87,15 +87,16 @@ def check_find_exact(tab, q, resident_sorted, version_of):
     return int(f.sum())
 
 
-@pytest.mark.parametrize("lam", [0.5, 1.0])
-def test_lambda_sweep_table_at_full_size(lam):
-    """2^26 slots, dim 64, single bucket: fill with distinct uniform keys in
-    2^20 batches (score = batch index), then exact contents of 2000 sampled
-    buckets, an exact 2^20-key find (90 % resident), one upsert step
+@pytest.mark.parametrize("lam,cap_log2", [(0.5, 26), (1.0, 26), (1.0, 28)])
+def test_lambda_sweep_table_at_full_size(lam, cap_log2):
+    """2^26 slots (and 2^28, the largest capacity of the workloads, with its
+    64 GiB of rows in HBM), dim 64, single bucket: fill with distinct uniform
+    keys in 2^20 batches (score = batch index), then exact contents of 2000
+    sampled buckets, an exact 2^20-key find (90 % resident), one upsert step
     (90 % resident, 10 % new), and the checks again."""
     H = hkv()
-    cap, D, batch = 1 << 26, 64, 1 << 20
-    seed = 0x484B56000000AA00 + int(lam * 100)
+    cap, D, batch = 1 << cap_log2, 64, 1 << 20
+    seed = 0x484B56000000AA00 + int(lam * 100) + cap_log2
     tab = H.HashTable(cap, D)
     t0 = time.time()
     target = int(lam * cap)
@@ -108,7 +109,8 @@ def test_lambda_sweep_table_at_full_size(lam):
         tab.insert_or_assign(k, gen.values(k, step, D), torch.full((n,), step, dtype=torch.int64, device=dev()))
         score_parts.append((cursor, n, step))
         cursor += n
-    log(f"lambda {lam}: {cursor} keys in {step} batches, size {tab.size()}, {time.time() - t0:.1f}s")
+    log(f"lambda {lam}, 2^{cap_log2} slots: {cursor} keys in {step} batches, size {tab.size()}, "
+        f"{time.time() - t0:.1f}s")
     allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
     alls = torch.cat([torch.full((n,), st, dtype=torch.int64, device=dev()) for _, n, st in score_parts])
 
