@@ -148,6 +148,15 @@ def owner_bytes_per_key(dim: int, f: float, e: float) -> float:
     return 4 + (1 - f) * (8 + 8 + 4 * dim + 4 + 4 + 128 + 4 + 8 + 1 + 8 + 4 * dim + e * (1024 + 8))
 
 
+def launch_cv(stat) -> float:
+    """Coefficient of variation of a kernel's launch times from the library's
+    (launches, total, max, min, sum of squares) record."""
+    n, tot, _, _, sq = stat
+    mean = tot / n
+    var = max(0.0, sq / n - mean * mean)
+    return round(var ** 0.5 / mean, 4) if mean > 0 else 0.0
+
+
 def batch_size(args) -> int:
     return 1 << args.batch_log2
 
@@ -896,7 +905,7 @@ def run_gpu(args):
     kstats = {}
     for T in tables:
         T["kernels"] = T["tab"].profile_stop()
-        for name, (cnt, tot, mx) in T["kernels"].items():
+        for name, (cnt, tot, *_) in T["kernels"].items():
             a = kstats.setdefault(name, [0, 0.0])
             a[0] += cnt
             a[1] += tot
@@ -913,10 +922,12 @@ def run_gpu(args):
     for T in tables:
         ks = T["kernels"]
         fm = ks["find"][1] / ks["find"][0]
-        e = dict(find_ms=round(fm, 5), find_bkvs=round(batch / fm / 1e6, 3), hit_rate=round(hit[T["lam"]], 4))
+        e = dict(find_ms=round(fm, 5), find_bkvs=round(batch / fm / 1e6, 3), hit_rate=round(hit[T["lam"]], 4),
+                 find_cv=launch_cv(ks["find"]))
         if not args.find_only:
             um = sum(ks[k][1] / ks[k][0] for k in ("upsert_probe", "upsert_owner"))
-            e.update(upsert_ms=round(um, 5), upsert_bkvs=round(batch / um / 1e6, 3))
+            e.update(upsert_ms=round(um, 5), upsert_bkvs=round(batch / um / 1e6, 3),
+                     upsert_probe_cv=launch_cv(ks["upsert_probe"]), upsert_owner_cv=launch_cv(ks["upsert_owner"]))
         e.update(lambda_start=round(T["lam_start"], 4), lambda_end=round(T["lam_end"], 4))
         detail[str(T["lam"])] = e
     fb = [v["find_bkvs"] for v in detail.values()]

@@ -68,6 +68,8 @@ class HkvKernelStat(ctypes.Structure):
         ("launches", ctypes.c_uint64),
         ("total_ms", ctypes.c_double),
         ("max_ms", ctypes.c_double),
+        ("min_ms", ctypes.c_double),
+        ("sumsq_ms2", ctypes.c_double),
     ]
 
 
@@ -272,10 +274,11 @@ def hkv_profile_start(table) -> None:
 
 
 def hkv_profile_stop(table) -> dict:
-    """Returns {kernel name: (launches, total_ms, max_ms)}."""
+    """Returns {kernel name: (launches, total_ms, max_ms, min_ms, sumsq_ms2)}."""
     cap = 16
     out = (HkvKernelStat * cap)()
     count = ctypes.c_uint32(0)
     _check(lib.hkv_profile_stop(table, out, cap, ctypes.byref(count)))
-    return {out[j].name.decode(): (int(out[j].launches), float(out[j].total_ms), float(out[j].max_ms))
+    return {out[j].name.decode(): (int(out[j].launches), float(out[j].total_ms), float(out[j].max_ms),
+                                   float(out[j].min_ms), float(out[j].sumsq_ms2))
             for j in range(min(cap, count.value))}

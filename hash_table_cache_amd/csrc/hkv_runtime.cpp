@@ -717,10 +717,13 @@ HKV_API hkv_status hkv_profile_stop(hkv_table* t, hkv_kernel_stat* out, uint32_t
       agg.push_back(hkv_kernel_stat{});
       a = &agg.back();
       std::snprintf(a->name, sizeof(a->name), "%s", r.name);
+      a->min_ms = ms;
     }
     a->launches += 1;
     a->total_ms += ms;
+    a->sumsq_ms2 += static_cast<double>(ms) * ms;
     if (ms > a->max_ms) a->max_ms = ms;
+    if (ms < a->min_ms) a->min_ms = ms;
     t->prof.give_back(r.start);
     t->prof.give_back(r.stop);
   }

@@ -269,6 +269,8 @@ typedef struct hkv_kernel_stat {
   uint64_t launches;  /* timed launches of that kernel */
   double total_ms;    /* sum of their times */
   double max_ms;      /* longest one */
+  double min_ms;      /* shortest one */
+  double sumsq_ms2;   /* sum of their squared times (spread across launches) */
 } hkv_kernel_stat;
 
 /* hkv_profile_start - discards earlier records and turns timing on. */
