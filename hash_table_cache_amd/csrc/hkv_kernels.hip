@@ -962,18 +962,19 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
 
 // State of a bucket owned by a 16-lane group in the owner kernel: its
 // occupancy (group-uniform), this lane's 8 digest bytes and, once loaded, the
-// scores and keys of this lane's 8 slots (slots 8*lane .. 8*lane+7). Only the
-// lane owning a slot reads or writes that slot's key, score and digest.
-// The score column is loaded for a full bucket; the whole key column only
-// when a second chain key needs the hit check: a victim is chosen from the
-// scores and the keys of the slots at the lowest score alone.
+// scores of this lane's 8 slots (slots 8*lane .. 8*lane+7) and the keys it
+// knows. Only the lane owning a slot reads or writes that slot's key, score
+// and digest. The score column is loaded for a full bucket; keys are read
+// only where a victim must be chosen among slots at the lowest score, a
+// lane's 8 at a time (one 64-byte burst, the price of reading one), and every
+// key the group writes stays known.
 struct Bucket {
   uint32_t b;
   uint32_t occ;
   uint32_t dig0, dig1;
-  bool scols;     // sc valid (group-uniform)
-  bool kcols;     // kc valid for every slot (group-uniform)
-  uint32_t kval;  // this lane's slots whose kc is valid (bit u: slot 8*lane+u)
+  bool scols;      // sc valid (group-uniform)
+  uint32_t kval;   // this lane's slots whose kc is valid (bit u: slot 8*lane+u)
+  uint32_t wmask;  // this lane's slots written by this kernel (their kc is valid)
   uint64_t sc[8];
   uint64_t kc[8];
 };
@@ -989,18 +990,6 @@ __device__ __forceinline__ void bucket_load_scores(Bucket& o, const TableView& t
   o.scols = true;
 }
 
-__device__ __forceinline__ void bucket_load_keys(Bucket& o, const TableView& t, int lane) {
-  const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
-#pragma unroll
-  for (int u = 0; u < 8; u += 2) {
-    const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
-    o.kc[u] = c.x;
-    o.kc[u + 1] = c.y;
-  }
-  o.kcols = true;
-  o.kval = 0xFFu;
-}
-
 // Lowest (score, key) entry of the owned full bucket (group-uniform score and
 // key, and its slot). Keys of the slots at the lowest score that are not in
 // registers yet are loaded (one round trip, none when all are known).
@@ -1011,22 +1000,20 @@ __device__ __forceinline__ int bucket_lowest(Bucket& o, const TableView& t, int 
 #pragma unroll
   for (int u = 1; u < 8; ++u) ls = o.sc[u] < ls ? o.sc[u] : ls;
   const uint64_t gs = group_min<kInsG>(ls);
-  if (!o.kcols) {
-    // a lane with an unknown key at the lowest score reads all 8 of its keys:
-    // the same 64-byte burst as one key, in four 16-byte loads
-    bool need = false;
+  // a lane with an unknown key at the lowest score reads all 8 of its keys:
+  // the same 64-byte burst as one key, in four 16-byte loads
+  bool need = false;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) need |= o.sc[u] == gs && !((o.kval >> u) & 1u);
-    if (need) {
-      const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
+  for (int u = 0; u < 8; ++u) need |= o.sc[u] == gs && !((o.kval >> u) & 1u);
+  if (need) {
+    const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + lane * 8;
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
-        o.kc[u] = c.x;
-        o.kc[u + 1] = c.y;
-      }
-      o.kval = 0xFFu;
+    for (int u = 0; u < 8; u += 2) {
+      const ulonglong2 c = *reinterpret_cast<const ulonglong2*>(t.keys + base + u);
+      o.kc[u] = c.x;
+      o.kc[u + 1] = c.y;
     }
+    o.kval = 0xFFu;
   }
   uint64_t lk = ~0ull;
   int lslot = -1;
@@ -1068,6 +1055,7 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
     o.kc[u] = here ? k : o.kc[u];
   }
   o.kval |= 1u << (s & 7);
+  o.wmask |= 1u << (s & 7);
 }
 
 // Algorithm 2 for one key against the owned bucket, with the input row already
@@ -1086,19 +1074,18 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
       copy_row<kInsG, V4, true>(rows + static_cast<uint64_t>(s) * t.dim, row, t.dim, lane);
     }
   };
+  // A chain key was absent when the probe kernel ran and only this group has
+  // written the bucket since, so it can only be a key this group wrote (a
+  // duplicate earlier in the chain): the hit check compares the written
+  // slots, whose keys are in registers, and loads nothing.
   int hit = -1;
   if (!fresh) {
-    if (o.kcols) {
-      int lh = -1;
+    int lh = -1;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (o.kc[u] == k) lh = lane * 8 + u;
-      const uint64_t hb = group_bits<kInsG>(__ballot(lh >= 0));
-      if (hb) hit = __shfl(lh, __ffsll(static_cast<unsigned long long>(hb)) - 1, kInsG);
-    } else {
-      Owned tmp{o.b, o.occ, o.dig0, o.dig1};
-      hit = own_find(tmp, t, k, d * 0x01010101u, lane);
-    }
+    for (int u = 0; u < 8; ++u)
+      if (((o.wmask >> u) & 1u) && o.kc[u] == k) lh = lane * 8 + u;
+    const uint64_t hb = group_bits<kInsG>(__ballot(lh >= 0));
+    if (hb) hit = __shfl(lh, __ffsll(static_cast<unsigned long long>(hb)) - 1, kInsG);
   }
   if (hit >= 0) {
     bucket_write(o, t, hit, false, k, d, score, lane);
@@ -1144,11 +1131,10 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
 // among its 256 keys in LDS and deals them out to its 16-lane groups in turn.
 // An owner loads, in one round trip, the bucket's
 // digest line, the chain head, its key's row and - when the probe kernel saw
-// the bucket full - the scores and keys of all slots; it applies its own key,
-// then the chain from its head down to itself (Algorithm 2, each chain key
-// costing one round trip for its inputs), writes the occupancy and resets the
-// chain head. With distinct keys any order within a chain gives the same
-// bucket contents.
+// the bucket full - the scores of all slots; it applies its own key, then the
+// chain from its head down to itself (Algorithm 2, each chain key costing one
+// round trip for its inputs), writes the occupancy and resets the chain head.
+// With distinct keys any order within a chain gives the same bucket contents.
 template <bool V4, bool DUAL, bool EVICT>
 __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
@@ -1187,8 +1173,8 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     Bucket o;
     o.b = tgt & ~kFullBit;
     o.scols = false;
-    o.kcols = false;
     o.kval = 0;
+    o.wmask = 0;
     uint32_t head = 0;
     if (lane == 0) head = __hip_atomic_load(t.head + o.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
@@ -1210,9 +1196,6 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
     for (uint64_t step = 0; cur != i && cur < n && step < n; ++step) {
-      // a full bucket's key column, for the hit checks of the chain's keys,
-      // arrives with the first chain key's inputs
-      if (o.scols && !o.kcols) bucket_load_keys(o, t, lane);
       const uint32_t after = next[cur];
       const uint64_t kc = keys[cur];
       const uint64_t scc = scores[cur];
