@@ -86,6 +86,8 @@ def parse_args():
     p.add_argument("--online", action="store_true",
                    help="single- vs dual-bucket continuous Zipf upsert at full capacity (use --capacity-log2 27)")
     p.add_argument("--online-modes", default="single,dual", help="bucket modes of --online")
+    p.add_argument("--graph", action="store_true",
+                   help="small launch-bound batches issued eagerly and replayed from a HIP graph")
     p.add_argument("--triple", action="store_true",
                    help="the mixed find/assign/insert_or_assign workload (use with --capacity-log2 27)")
     p.add_argument("--tiered", action="store_true",
@@ -623,6 +625,70 @@ def online_run(args) -> None:
         out["dual_over_single_upsert"] = round(out["dual"]["upsert_bkvs"] / out["single"]["upsert_bkvs"], 3)
     print(json.dumps({"online": out, "capacity": cap, "dim": dim, "zipf_alpha": 1.05, "ids": n_ids,
                       "draws_per_batch": draws, "steady_batches": steady_batches}), flush=True)
+
+
+def graph_run(args) -> None:
+    """Small, launch-bound batches (the tiny workload's shape: 2^16 slots, dim
+    16, full, 16384-key batches): per step a find and an insert_or_assign of
+    16384 keys, issued eagerly, then the same step captured once into a HIP
+    graph and replayed. All calls on one stream (the table records no events)
+    and the inserter workspace sized by the eager steps before capture. Rate =
+    keys of the timed steps / wall time. Prints one JSON line."""
+    import torch
+
+    import hash_table_cache_amd as H
+    import hkv_inputs as gen
+
+    dev = torch.device("cuda", 0)
+    cap, dim, n = 1 << 16, 16, 16384
+    s = torch.cuda.Stream()
+    tab = H.HashTable(cap, dim)
+    res = {}
+    with torch.cuda.stream(s):
+        for step in range(1, 9):
+            k = gen.keys_in_range(SEED, step, n, 1, 1 << 40, device=dev)
+            tab.insert_or_assign(k, gen.values(k, step, dim, SEED), torch.full((n,), step, dtype=torch.int64,
+                                                                                 device=dev), stream=s)
+        ek, _, _, _ = tab.export_batch(with_values=False, stream=s)
+        half = ek[torch.randperm(ek.numel(), device=dev)[: n // 2]]
+        qk = gen.shuffle(torch.cat([half, gen.unique_keys(SEED, 90, 0, n - half.numel(), device=dev)]), SEED, 91)
+        uk = ek[torch.randperm(ek.numel(), device=dev)[:n]].contiguous()
+        uv = gen.values(uk, 100, dim, SEED)
+        us = torch.full((n,), 100, dtype=torch.int64, device=dev)
+        out = torch.empty((n, dim), dtype=torch.float32, device=dev)
+        found = torch.empty(n, dtype=torch.uint8, device=dev)
+
+        def step_calls():
+            tab.find(qk, values_out=out, found_out=found, stream=s)
+            tab.insert_or_assign(uk, uv, us, stream=s)
+
+        reps = max(args.steps, 20) * 10
+        for _ in range(10):
+            step_calls()
+        s.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step_calls()
+        s.synchronize()
+        eager = time.perf_counter() - t0
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step_calls()
+        for _ in range(10):
+            g.replay()
+        s.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        s.synchronize()
+        graph = time.perf_counter() - t0
+    res = dict(workload="2^16 slots, dim 16, full; per step find 16384 keys (half resident) + insert_or_assign of "
+                        "16384 resident keys", steps=reps,
+               eager_us_per_step=round(eager / reps * 1e6, 2), graph_us_per_step=round(graph / reps * 1e6, 2),
+               eager_bkvs=round(2 * n * reps / eager / 1e9, 3), graph_bkvs=round(2 * n * reps / graph / 1e9, 3))
+    log(f"graph: {res}")
+    tab.close()
+    print(json.dumps({"graph": res}), flush=True)
 
 
 API_CONFIGS = (("A", 8, 27), ("B", 32, 27), ("C", 64, 26))  # (name, dim, log2 capacity), pure HBM
@@ -1175,6 +1241,9 @@ def main():
         return
     if args.online:
         online_run(args)
+        return
+    if args.graph:
+        graph_run(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()
