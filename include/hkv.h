@@ -40,9 +40,10 @@
  *     the first call from a second stream waits once for the device
  *     (hipDeviceSynchronize). Several host threads may call concurrently.
  *   - The calls may be captured into a HIP graph when every call on the table
- *     is issued on the capturing stream and an inserter call of at least as
- *     many keys ran before the capture (inserters grow a workspace on demand,
- *     which a capture cannot do).
+ *     is issued on the capturing stream and, for each inserter call captured,
+ *     a call of the same kind with at least as many keys ran before the
+ *     capture (inserters grow their workspaces on demand, which a capture
+ *     cannot do).
  *   - Arguments are validated synchronously; on any error nothing is enqueued,
  *     the call returns a negative status and hkv_last_error() describes it.
  *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 3 keys.
