@@ -27,6 +27,8 @@ Embedding Storage", arXiv 2603.17168):
 import math
 import pathlib
 
+import hypothesis
+import hypothesis.strategies as st
 import numpy as np
 import pytest
 import torch
@@ -141,6 +143,75 @@ def random_workload(seed, B, dim, batches, batch, key_pool, tie_heavy):
 @pytest.mark.parametrize("tie_heavy", [False, True])
 def test_single_bucket_topk_tiny_tables(B, tie_heavy):
     random_workload(10 + B, B, 3, batches=12, batch=150 * B, key_pool=600 * B, tie_heavy=tie_heavy)
+
+
+# Score schemes for the property test below. Each keeps every key's score
+# non-decreasing over time, the condition under which the table's contents
+# equal the top 128 by (score, key) of everything ever offered to a bucket:
+# a key that was evicted or rejected sits below a bucket minimum that never
+# falls again.
+def _scores(scheme, rng, step, n):
+    if scheme == "constant":        # every key the same score forever
+        return u64(np.full(n, 7))
+    if scheme == "step":            # one score per batch: ties inside it
+        return u64(np.full(n, step))
+    if scheme == "coarse":          # four levels per batch: many ties
+        return u64(step * 4 + rng.integers(0, 4, size=n))
+    return u64(step * 1000 + rng.integers(0, 1000, size=n))  # "jitter"
+
+
+_ASSIGN_TOP = {"constant": lambda s: 7, "step": lambda s: s,
+               "coarse": lambda s: s * 4 + 3, "jitter": lambda s: s * 1000 + 999}
+
+
+@hypothesis.settings(max_examples=60, deadline=None, derandomize=True,
+                     suppress_health_check=[hypothesis.HealthCheck.too_slow])
+@hypothesis.given(
+    seed=st.integers(0, 2**32 - 1),
+    B=st.integers(1, 5),
+    dim=st.sampled_from([1, 3]),
+    batches=st.integers(1, 7),
+    batch=st.integers(1, 420),
+    pool_factor=st.sampled_from([1, 2, 4]),
+    scheme=st.sampled_from(["constant", "step", "coarse", "jitter"]),
+    with_assign=st.booleans(),
+)
+def test_single_bucket_topk_property(seed, B, dim, batches, batch, pool_factor, scheme, with_assign):
+    """Random tiny tables (including bucket counts that are not powers of two,
+    where routing is hash mod B), batch sizes from one key to more than three
+    buckets' worth, and score streams from all-equal to jittered: after every
+    insert_or_assign, and after every assign of raised scores, each bucket holds
+    exactly the top 128 of its offered keys by (score, key) with the
+    last-written row and score (the paper's cache semantics, §3.1 and §4.1),
+    and find agrees with that set."""
+    rng = np.random.default_rng(seed)
+    t = oracle.OracleTable(capacity=B * SLOTS, dim=dim)
+    model = TopKModel(lambda k: t.route(k)[0], dim)
+    pool = np.unique(rand_keys(rng, max(1, batch * pool_factor)))
+    for step in range(1, batches + 1):
+        keys = rng.choice(pool, size=min(batch, pool.size), replace=False)
+        sc = _scores(scheme, rng, step, keys.size)
+        vals = rng.standard_normal((keys.size, dim)).astype(np.float32)
+        t.insert_or_assign(keys, sc, values=vals)
+        model.insert_or_assign(keys, sc, vals)
+        check_against_model(t, model, dim)
+        if with_assign:
+            # raise some scores to the top of this batch's range: residents
+            # stay resident, absent keys are ignored
+            ak = rng.choice(pool, size=min(pool.size, 1 + batch // 3), replace=False)
+            asc = u64(np.full(ak.size, _ASSIGN_TOP[scheme](step)))
+            av = rng.standard_normal((ak.size, dim)).astype(np.float32)
+            t.assign(ak, values=av, scores=asc)
+            model.assign(ak, asc, av)
+            check_against_model(t, model, dim)
+        probe = rng.choice(pool, size=min(pool.size, 64), replace=False)
+        got, found, fsc, _ = t.find(probe)
+        res = model.resident_keys()
+        for i, k in enumerate(probe.tolist()):
+            assert bool(found[i]) == (k in res)
+            if found[i]:
+                assert int(fsc[i]) == model.score[k]
+                np.testing.assert_array_equal(got[i], model.payload[k])
 
 
 def test_single_bucket_adversarial_one_bucket():

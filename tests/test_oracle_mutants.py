@@ -53,6 +53,15 @@ MUTANTS = {
                              "  for (uint64_t i = 0; i < n; ++i) {\n    if (res[i] || is_reserved(keys[i])) continue;",
                              "    continue;\n  }\n  uint64_t m = 0;\n"
                              "  for (uint64_t i = 0; i < n; ++i) {\n    if (is_reserved(keys[i])) continue;"),
+    # victim picked by score alone: the first minimum-score slot, whatever its key
+    "victim_by_score_only": ("if (rank_below(t.score[p], t.key[p], t.score[q], t.key[q])) m = s;",
+                             "if (t.score[p] < t.score[q]) m = s;"),
+    # bucket index by mask: equal to the modulo only when B is a power of two
+    "bucket_by_mask": ("r.b1 = h1 % t.buckets;", "r.b1 = h1 & (t.buckets - 1);"),
+    "assign_drops_rows": ("    } else if (values) {\n      for (uint32_t c = 0; c < t.dim; ++c) t.value[p * t.dim + c] = values[i * t.dim + c];",
+                          "    } else if (false) {\n      for (uint32_t c = 0; c < t.dim; ++c) t.value[p * t.dim + c] = values[i * t.dim + c];"),
+    "first_empty_skips_slot0": ("for (int s = 0; s < kSlots; ++s)\n    if (t.key[pos_of(b, s)] == kEmptyKey) return s;",
+                                "for (int s = 1; s < kSlots; ++s)\n    if (t.key[pos_of(b, s)] == kEmptyKey) return s;"),
     "find_or_insert_keeps_score": ("    t.score[p] = scores[i];\n    if (t.tag_mode) {\n      tags_inout[i] = t.tag[p];",
                                    "    if (t.tag_mode) {\n      tags_inout[i] = t.tag[p];"),
 }
@@ -85,6 +94,7 @@ def test_pin_suite_catches_every_planted_mistake(tmp_path):
     assert control.returncode == 0, "unmutated copy fails its pins:\n" + control.stdout[-3000:]
     survivors = [name for name, r in results.items() if r.returncode == 0]
     caught_by = {name: next((l.split("::")[1].split(" ")[0] for l in r.stdout.splitlines()
-                             if l.startswith("FAILED")), "?") for name, r in results.items()}
+                             if l.startswith("FAILED")), f"the suite ending with status {r.returncode}")
+                 for name, r in results.items()}
     print("\n".join(f"{name:34s} caught by {caught_by[name]}" for name in sorted(results)))
     assert not survivors, f"mistakes no pin catches: {survivors}"
