@@ -18,8 +18,8 @@ import hkv_inputs as gen
 import oracle
 from conftest import gpu_available
 from helpers import SLOTS
-from test_gpu_parity import (NAN_BITS, SENTINEL_SCORE, assert_same_contents, dev, hkv, mixed_queries, np_u64,
-                             sample_present, to_dev)
+from test_gpu_parity import (NAN_BITS, SENTINEL_SCORE, assert_same_contents, check_find, dev, hkv, mixed_queries,
+                             np_u64, sample_present, to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -555,6 +555,53 @@ def test_insert_and_evict_and_find_or_insert_odd_dims(D):
             assert np.array_equal(found.cpu().numpy(), ofound)
             assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
         assert_same_contents(tab, o)
+
+
+@pytest.mark.parametrize("D", [129, 132, 256, 260])
+def test_wide_rows_every_call_exact(D):
+    """Rows wider than 128 floats: the row copies loop over several 512-byte
+    pieces per 16 lanes, and the inserter's owner copies rows from the input
+    instead of holding them in registers, on every path (update, empty slot,
+    eviction, rejection, staging of evicted rows). 129 takes the scalar copy."""
+    H = hkv()
+    C = 16 * SLOTS
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    step, _ = fill(tab, o, C, D, 41, 1, batch=1000)
+    assert_same_contents(tab, o)
+    check_find(tab, o, mixed_queries(o, 700, 0.7, 5, 11))
+    step += 1
+    absent = gen.unique_keys(41, 9, 0, 100).numpy().view(np.uint64)
+    ak = np.random.default_rng(1).permutation(np.concatenate([sample_present(o, 400, 3), absent]))
+    akt = to_dev(ak)
+    av = gen.values(akt, 500 + step, D)
+    asc = torch.full((ak.size,), step, dtype=torch.int64, device=dev())
+    tab.assign(akt, av, asc)
+    o.assign(ak, values=av.cpu().numpy(), scores=np_u64(asc))
+    assert_same_contents(tab, o)
+    for t in range(4):
+        step += 1
+        fresh = gen.unique_keys(41, 20 + t, 0, 600).numpy().view(np.uint64)
+        k = np.random.default_rng(10 + t).permutation(np.concatenate([fresh, sample_present(o, 600, 80 + t)]))
+        kt = to_dev(k)
+        v = gen.values(kt, 600 + step, D)
+        # odd calls offer scores below every resident's, so admission turns
+        # the new keys away
+        sc = torch.full((k.size,), step if t % 2 == 0 else 0, dtype=torch.int64, device=dev())
+        if t < 2:
+            got = evict_sets(*tab.insert_and_evict(kt, v, sc))
+            want = oracle_evict_sets(o.insert_and_evict(k, np_u64(sc), values=v.cpu().numpy()))
+            assert got[0].size > 0 and np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+            assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        else:
+            v0 = v.cpu().numpy()
+            rows, found = tab.find_or_insert(kt, v, sc)
+            orows, ofound = o.find_or_insert(k, np_u64(sc), values=v0)
+            torch.cuda.synchronize()
+            assert np.array_equal(found.cpu().numpy(), ofound)
+            assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        assert_same_contents(tab, o)
+    check_find(tab, o, mixed_queries(o, 700, 0.7, 6, 12))
 
 
 def test_find_or_insert_dual_parallel_invariants():
