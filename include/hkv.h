@@ -50,6 +50,12 @@
  *   - The reserved keys HKV_EMPTY_KEY and HKV_LOCKED_KEY always miss in the
  *     readers and are skipped by the updaters and inserters.
  *   - No C++ exception crosses this boundary.
+ *   - Two environment variables, read by hkv_create, override launch shapes
+ *     for tuning; results do not depend on them. HKV_GROUP_LANES: lanes that
+ *     serve one key in the probing kernels (4, 8 or 16; any other value keeps
+ *     the default chosen from dim). HKV_KEYS_PER_GROUP: keys each group serves
+ *     in the key-side probes of hkv_find_ptr and hkv_contains (1, 2 or 4;
+ *     default 2).
  */
 #ifndef HKV_H_
 #define HKV_H_
