@@ -1,0 +1,84 @@
+"""Seeded random small configurations: the HIP table against the CPU oracle,
+exact, through the C ABI.
+
+Each case draws a bucket count (powers of two and not, down to one bucket), a
+row width (scalar and 16-byte copy paths, rows above 128 floats), a score
+scheme (all equal, one score per call, jittered) and a sequence of calls of
+every kind with batch sizes from one key to three times the capacity. Scores
+never decrease for a key, so every call's result is the same in any order of
+its keys and single-bucket mode is compared exactly after every call:
+per-bucket contents, rows and scores, find outputs (misses untouched),
+insert_and_evict's hand-back as a set, find_or_insert's flags and rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import hkv_inputs as gen
+import oracle
+from conftest import gpu_available
+from helpers import SLOTS
+from test_gpu_next_ops import evict_sets, oracle_evict_sets
+from test_gpu_parity import assert_same_contents, check_find, dev, hkv, np_u64, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+CALLS = ["insert_or_assign", "assign", "insert_and_evict", "find_or_insert", "find"]
+
+
+def scheme_scores(scheme, rng, step, n):
+    if scheme == "constant":
+        return np.full(n, 7, np.uint64)
+    if scheme == "step":
+        return np.full(n, step, np.uint64)
+    return (step * 1000 + rng.integers(0, 1000, size=n)).astype(np.uint64)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_small_configuration_exact(case):
+    H = hkv()
+    rng = np.random.default_rng(5000 + case)
+    B = int(rng.choice([1, 2, 3, 5, 8, 13]))
+    D = int(rng.choice([1, 2, 4, 7, 16, 64, 132]))
+    scheme = str(rng.choice(["constant", "step", "jitter"]))
+    C = B * SLOTS
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    pool = gen.unique_keys(case, 7, 0, int(C * rng.uniform(0.5, 4.0)) + 1).numpy().view(np.uint64)
+    absent = gen.unique_keys(case, 8, 0, 64).numpy().view(np.uint64)
+    calls = int(rng.integers(4, 10))
+    for step in range(1, calls + 1):
+        # the first call always inserts, so that later calls meet residents
+        call = "insert_or_assign" if step == 1 else str(rng.choice(CALLS))
+        n = int(rng.integers(1, min(pool.size, 3 * C) + 1))
+        k = rng.choice(pool, size=n, replace=False)
+        kt = to_dev(k)
+        sc = scheme_scores(scheme, rng, step, n)
+        sct = to_dev(sc)
+        v = gen.values(kt, 100 * case + step, D)
+        print(f"case {case}: B={B} D={D} scheme={scheme} step={step} call={call} n={n}", flush=True)
+        if call == "insert_or_assign":
+            tab.insert_or_assign(kt, v, sct)
+            o.insert_or_assign(k, sc, values=v.cpu().numpy())
+        elif call == "assign":
+            # rows only, scores only, or both
+            what = int(rng.integers(0, 3))
+            tab.assign(kt, v if what != 1 else None, sct if what != 0 else None)
+            o.assign(k, values=v.cpu().numpy() if what != 1 else None, scores=sc if what != 0 else None)
+        elif call == "insert_and_evict":
+            got = evict_sets(*tab.insert_and_evict(kt, v, sct))
+            want = oracle_evict_sets(o.insert_and_evict(k, sc, values=v.cpu().numpy()))
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+            assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        elif call == "find_or_insert":
+            v0 = v.cpu().numpy()
+            rows, found = tab.find_or_insert(kt, v, sct)
+            orows, ofound = o.find_or_insert(k, sc, values=v0)
+            torch.cuda.synchronize()
+            assert np.array_equal(found.cpu().numpy(), ofound)
+            assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        else:
+            q = np.random.default_rng(case * 100 + step).permutation(np.concatenate([k[: max(1, n // 2)], absent]))
+            check_find(tab, o, to_dev(q))
+        assert_same_contents(tab, o)
