@@ -463,6 +463,60 @@ def test_find_or_insert_hits_and_inserts():
         check_against_model(t, model, dim)
 
 
+@hypothesis.settings(max_examples=50, deadline=None, derandomize=True,
+                     suppress_health_check=[hypothesis.HealthCheck.too_slow])
+@hypothesis.given(
+    seed=st.integers(0, 2**32 - 1),
+    B=st.integers(1, 5),
+    batches=st.integers(1, 6),
+    batch=st.integers(1, 420),
+    pool_factor=st.sampled_from([1, 2, 4]),
+    scheme=st.sampled_from(["constant", "step", "coarse", "jitter"]),
+    ops=st.lists(st.sampled_from(["insert_or_assign", "insert_and_evict", "find_or_insert"]), min_size=6,
+                 max_size=6),
+)
+def test_inserters_closed_form_property(seed, B, batches, batch, pool_factor, scheme, ops):
+    """Random tiny tables and batches, every inserter in random order: the
+    table equals the top-128 model after each call (§3.1); insert_and_evict
+    hands back exactly (resident before ∪ offered) − resident after with
+    last-written rows and scores; find_or_insert flags exactly the keys
+    resident before the call, returns their stored rows and refreshes their
+    scores, and inserts the rest (§4.1)."""
+    rng = np.random.default_rng(seed)
+    dim = 2
+    t = oracle.OracleTable(capacity=B * SLOTS, dim=dim)
+    model = TopKModel(lambda k: t.route(k)[0], dim)
+    pool = np.unique(rand_keys(rng, max(1, batch * pool_factor)))
+    for step in range(1, batches + 1):
+        keys = rng.choice(pool, size=min(batch, pool.size), replace=False)
+        sc = _scores(scheme, rng, step, keys.size)
+        vals = rng.standard_normal((keys.size, dim)).astype(np.float32)
+        before = model.resident_keys()
+        op = ops[step - 1]
+        if op == "insert_or_assign":
+            t.insert_or_assign(keys, sc, values=vals)
+            model.insert_or_assign(keys, sc, vals)
+        elif op == "insert_and_evict":
+            out = t.insert_and_evict(keys, sc, values=vals)
+            model.insert_or_assign(keys, sc, vals)
+            after = model.resident_keys()
+            got = out["keys"].tolist()
+            assert len(got) == len(set(got)) and set(got) == (before | set(keys.tolist())) - after
+            for k, s, v in zip(got, out["scores"].tolist(), out["values"]):
+                assert model.score[k] == s
+                np.testing.assert_array_equal(v, model.payload[k])
+        else:
+            rows, found = t.find_or_insert(keys, sc, values=vals)
+            hit = np.array([k in before for k in keys.tolist()], dtype=bool)
+            assert np.array_equal(found.astype(bool), hit)
+            for i in np.flatnonzero(hit):
+                np.testing.assert_array_equal(rows[i], model.payload[int(keys[i])])
+                model.score[int(keys[i])] = int(sc[i])
+            np.testing.assert_array_equal(rows[~hit], vals[~hit])
+            model.insert_or_assign(keys[~hit], sc[~hit], vals[~hit])
+        check_against_model(t, model, dim)
+
+
 def test_new_operations_tag_mode_matches_value_mode():
     rng = np.random.default_rng(16)
     tv = oracle.OracleTable(capacity=4 * SLOTS, dim=2)
