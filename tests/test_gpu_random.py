@@ -9,6 +9,8 @@ never decrease for a key, so every call's result is the same in any order of
 its keys and single-bucket mode is compared exactly after every call:
 per-bucket contents, rows and scores, find outputs (misses untouched),
 insert_and_evict's hand-back as a set, find_or_insert's flags and rows.
+In serial insert mode (single and dual bucket) scores are arbitrary and
+every key's slot position is compared as well.
 """
 
 import numpy as np
@@ -82,3 +84,66 @@ def test_random_small_configuration_exact(case):
             q = np.random.default_rng(case * 100 + step).permutation(np.concatenate([k[: max(1, n // 2)], absent]))
             check_find(tab, o, to_dev(q))
         assert_same_contents(tab, o)
+
+
+def assert_same_positions(tab, o):
+    gk, _, gs, gp = tab.export_batch(with_values=False)
+    e = o.export()
+    order = np.argsort(np_u64(gp))
+    assert np.array_equal(np_u64(gp)[order], e["pos"])
+    assert np.array_equal(np_u64(gk)[order], e["keys"])
+    assert np.array_equal(np_u64(gs)[order], e["scores"])
+
+
+@pytest.mark.parametrize("dual", [False, True])
+@pytest.mark.parametrize("case", range(8))
+def test_random_serial_mode_positions_exact(case, dual):
+    """Serial insert mode applies keys in input order, as the oracle does, so
+    scores may be anything: drawn from a small range, with ties everywhere and
+    updates that lower a key's score. Every key must sit in the oracle's slot
+    (Algorithms 2 and 3) after every call; insert_and_evict hands back the
+    oracle's departures in the oracle's order."""
+    H = hkv()
+    rng = np.random.default_rng(7000 + case + 100 * dual)
+    B = int(rng.choice([1, 2, 3, 5, 8]))
+    D = int(rng.choice([1, 4, 7, 64]))
+    C = B * SLOTS
+    tab = H.HashTable(C, D, dual_bucket=dual, serial_insert=True)
+    o = oracle.OracleTable(C, D, dual=dual)
+    pool = gen.unique_keys(case + 50 * dual, 9, 0, int(C * rng.uniform(0.5, 3.0)) + 1).numpy().view(np.uint64)
+    absent = gen.unique_keys(case, 10, 0, 64).numpy().view(np.uint64)
+    for step in range(1, int(rng.integers(4, 9)) + 1):
+        call = "insert_or_assign" if step == 1 else str(rng.choice(CALLS))
+        n = int(rng.integers(1, min(pool.size, 2 * C) + 1))
+        k = rng.choice(pool, size=n, replace=False)
+        kt = to_dev(k)
+        sc = rng.integers(0, 50, size=n).astype(np.uint64)
+        sct = to_dev(sc)
+        v = gen.values(kt, 100 * case + step, D)
+        print(f"serial case {case} dual={dual}: B={B} D={D} step={step} call={call} n={n}", flush=True)
+        if call == "insert_or_assign":
+            tab.insert_or_assign(kt, v, sct)
+            o.insert_or_assign(k, sc, values=v.cpu().numpy())
+        elif call == "assign":
+            tab.assign(kt, v, sct)
+            o.assign(k, values=v.cpu().numpy(), scores=sc)
+        elif call == "insert_and_evict":
+            ek, ev, es, cnt = tab.insert_and_evict(kt, v, sct)
+            want = o.insert_and_evict(k, sc, values=v.cpu().numpy())
+            torch.cuda.synchronize()
+            m = int(cnt.item())
+            assert np.array_equal(np_u64(ek[:m]), want["keys"])
+            assert np.array_equal(np_u64(es[:m]), want["scores"])
+            assert np.array_equal(ev[:m].cpu().numpy().view(np.uint32), want["values"].view(np.uint32))
+        elif call == "find_or_insert":
+            v0 = v.cpu().numpy()
+            rows, found = tab.find_or_insert(kt, v, sct)
+            orows, ofound = o.find_or_insert(k, sc, values=v0)
+            torch.cuda.synchronize()
+            assert np.array_equal(found.cpu().numpy(), ofound)
+            assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+        else:
+            q = np.random.default_rng(case * 100 + step).permutation(np.concatenate([k[: max(1, n // 2)], absent]))
+            check_find(tab, o, to_dev(q))
+        assert_same_positions(tab, o)
+    assert_same_contents(tab, o)
