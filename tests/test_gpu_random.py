@@ -10,7 +10,8 @@ its keys and single-bucket mode is compared exactly after every call:
 per-bucket contents, rows and scores, find outputs (misses untouched),
 insert_and_evict's hand-back as a set, find_or_insert's flags and rows.
 In serial insert mode (single and dual bucket) scores are arbitrary and
-every key's slot position is compared as well.
+every key's slot position is compared as well. Dual-bucket parallel mode is
+held to its invariants after every call.
 """
 
 import numpy as np
@@ -147,3 +148,97 @@ def test_random_serial_mode_positions_exact(case, dual):
             check_find(tab, o, to_dev(q))
         assert_same_positions(tab, o)
     assert_same_contents(tab, o)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_dual_parallel_invariants(case):
+    """Dual-bucket parallel mode picks among equally valid placements, so it is
+    held to invariants after every call of a random sequence: no key twice, at
+    most 128 per bucket, every entry in one of its two candidate buckets, each
+    resident key's score and row its last written ones, find hitting exactly
+    the resident keys, and insert_and_evict's hand-back and the table together
+    holding exactly what was resident or offered."""
+    H = hkv()
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.choice([2, 3, 5, 8, 13]))
+    D = int(rng.choice([1, 4, 7, 64]))
+    C = B * SLOTS
+    tab = H.HashTable(C, D, dual_bucket=True)
+    route = oracle.OracleTable(SLOTS * B, 1, dual=True)  # routing only
+    pool = gen.unique_keys(case + 200, 11, 0, int(C * rng.uniform(0.5, 3.0)) + 1).numpy().view(np.uint64)
+    absent = gen.unique_keys(case + 200, 12, 0, 64).numpy().view(np.uint64)
+    last_score, last_row = {}, {}
+    resident = set()
+
+    def rows_of(keys_u64):
+        ver = np.array([last_row[int(x)] for x in keys_u64.tolist()], dtype=np.int64)
+        return gen.values(to_dev(keys_u64), torch.from_numpy(ver).to(dev()), D)
+
+    for step in range(1, int(rng.integers(4, 10)) + 1):
+        call = "insert_or_assign" if step == 1 else str(rng.choice(CALLS))
+        n = int(rng.integers(1, min(pool.size, 3 * C) + 1))
+        k = rng.choice(pool, size=n, replace=False)
+        kt = to_dev(k)
+        sc = (step * 1000 + rng.integers(0, 1000, size=n)).astype(np.uint64)
+        sct = to_dev(sc)
+        ver = torch.full((n,), 1000 * case + step, dtype=torch.int64, device=dev())
+        v = gen.values(kt, ver, D)
+        print(f"dual case {case}: B={B} D={D} step={step} call={call} n={n}", flush=True)
+        before = set(resident)
+        if call == "find":
+            q = np.random.default_rng(case * 100 + step).permutation(np.concatenate([k[: max(1, n // 2)], absent]))
+            vals, found, scs = tab.find(to_dev(q), with_scores=True)
+            f = found.cpu().numpy().astype(bool)
+            assert np.array_equal(f, np.array([int(x) in resident for x in q.tolist()]))
+            hit = q[f]
+            assert np.array_equal(np_u64(scs)[f], np.array([last_score[int(x)] for x in hit.tolist()], np.uint64))
+            if hit.size:
+                assert torch.equal(vals[torch.from_numpy(f).to(dev())], rows_of(hit))
+            continue
+        if call == "assign":
+            tab.assign(kt, v, sct)
+            for x, s in zip(k.tolist(), sc.tolist()):
+                if x in resident:
+                    last_score[x], last_row[x] = s, 1000 * case + step
+        elif call == "find_or_insert":
+            rows, found = tab.find_or_insert(kt, v, sct)
+            f = found.cpu().numpy().astype(bool)
+            assert np.array_equal(f, np.array([int(x) in before for x in k.tolist()]))
+            if f.any():
+                assert torch.equal(rows[torch.from_numpy(f).to(dev())], rows_of(k[f]))
+            for x, s, hit_ in zip(k.tolist(), sc.tolist(), f.tolist()):
+                last_score[x] = s
+                if not hit_:
+                    last_row[x] = 1000 * case + step
+        else:
+            for x, s in zip(k.tolist(), sc.tolist()):
+                last_score[x], last_row[x] = s, 1000 * case + step
+            if call == "insert_or_assign":
+                tab.insert_or_assign(kt, v, sct)
+            else:
+                ek, ev, es, cnt = tab.insert_and_evict(kt, v, sct)
+                torch.cuda.synchronize()
+                m = int(cnt.item())
+                out = np_u64(ek[:m])
+                assert np.unique(out).size == m
+                assert np.array_equal(np_u64(es[:m]), np.array([last_score[int(x)] for x in out.tolist()], np.uint64))
+                if m:
+                    assert torch.equal(ev[:m], rows_of(out))
+        gk, gv, gs, gp = tab.export_batch()
+        k_, s_, p_ = np_u64(gk), np_u64(gs), np_u64(gp)
+        resident = set(k_.tolist())
+        assert np.unique(k_).size == k_.size and tab.size() == k_.size <= C
+        assert np.bincount((p_ // SLOTS).astype(np.int64), minlength=B).max() <= SLOTS
+        b1, b2, _ = route.route(k_)
+        assert np.all((p_ // SLOTS == b1) | (p_ // SLOTS == b2))
+        assert np.array_equal(s_, np.array([last_score[int(x)] for x in k_.tolist()], np.uint64))
+        if k_.size:
+            assert torch.equal(gv, rows_of(k_))
+        offered = set(k.tolist())
+        if call == "insert_and_evict":
+            assert not (set(out.tolist()) & resident)
+            assert set(out.tolist()) | resident == before | offered
+        elif call in ("insert_or_assign", "find_or_insert"):
+            assert resident <= before | offered
+        else:
+            assert resident == before
