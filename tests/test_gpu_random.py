@@ -242,3 +242,44 @@ def test_random_dual_parallel_invariants(case):
             assert resident <= before | offered
         else:
             assert resident == before
+
+
+@pytest.mark.parametrize("lanes,keys_per_group", [("4", "1"), ("16", "4"), ("4", "4"), ("16", "1")])
+@pytest.mark.parametrize("dual", [False, True])
+def test_tuning_overrides_keep_results_exact(lanes, keys_per_group, dual, monkeypatch):
+    """HKV_GROUP_LANES and HKV_KEYS_PER_GROUP change only launch shapes: the
+    probing kernels at 4 and 16 lanes per key and the key-side probes at 1
+    and 4 keys per group give the oracle's results (serial mode in dual, for
+    exact positions)."""
+    monkeypatch.setenv("HKV_GROUP_LANES", lanes)
+    monkeypatch.setenv("HKV_KEYS_PER_GROUP", keys_per_group)
+    H = hkv()
+    B, D = 5, 40  # 160-byte rows: 8 lanes by default, so both overrides change the shape
+    C = B * SLOTS
+    tab = H.HashTable(C, D, dual_bucket=dual, serial_insert=dual)
+    o = oracle.OracleTable(C, D, dual=dual)
+    pool = gen.unique_keys(31, 13, 0, 3 * C).numpy().view(np.uint64)
+    absent = gen.unique_keys(31, 14, 0, 200).numpy().view(np.uint64)
+    rng = np.random.default_rng(int(lanes) * 10 + int(keys_per_group) + dual)
+    for step in range(1, 5):
+        k = rng.choice(pool, size=C, replace=False)
+        kt = to_dev(k)
+        sc = np.full(C, step, np.uint64)
+        v = gen.values(kt, step, D)
+        tab.insert_or_assign(kt, v, to_dev(sc))
+        o.insert_or_assign(k, sc, values=v.cpu().numpy())
+        assert_same_contents(tab, o)
+        if dual:
+            assert_same_positions(tab, o)
+        q = rng.permutation(np.concatenate([rng.choice(pool, 333, replace=False), absent]))
+        qt = to_dev(q)
+        check_find(tab, o, qt)
+        ptrs = torch.zeros(q.size, dtype=torch.int64, device=dev())
+        found = torch.empty(q.size, dtype=torch.uint8, device=dev())
+        tab.find_ptr(qt, ptrs_out=ptrs, found_out=found)
+        contains = tab.contains(qt)
+        torch.cuda.synchronize()
+        ofound, _ = o.find_pos(q)
+        assert np.array_equal(found.cpu().numpy(), ofound)
+        assert np.array_equal(contains.cpu().numpy(), ofound)
+        assert np.all((ptrs.cpu().numpy() != 0) == ofound.astype(bool))
