@@ -40,6 +40,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -94,6 +96,9 @@ def parse_args():
                    help="the tiered-values workload (use with --capacity-log2 28 --dim 128)")
     p.add_argument("--hybrid", default="", metavar="FRACS",
                    help="value-placement sweep at these HBM fractions of the value rows, e.g. 1.0,0.5,0.0")
+    p.add_argument("--cold-runs", type=int, default=0, metavar="K",
+                   help="run the lambda sweep K times, each in a fresh process with fresh tables, and report "
+                        "the per-lambda medians (the paper's statistic: median of cold-start runs)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (counter calibration) and exit")
     return p.parse_args()
@@ -195,7 +200,6 @@ def pattern_ceiling(dim: int = 64):
     2^26-slot table with rows of `dim` floats, without its arithmetic, with
     and without the chain of dependent loads) in a child process; returns its
     JSON or None."""
-    import subprocess
 
     from hash_table_cache_amd import build as hb
 
@@ -1212,6 +1216,37 @@ def run_cpu_baseline(args):
                 rounds=rounds)
 
 
+def cold_runs(args):
+    """The lambda sweep K times, each in a child process of its own (a cold
+    start: new process, new tables, filled from empty), then the median over
+    the runs of every per-lambda rate and of the combined value. This process
+    never touches the GPU itself."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--no-cpu-baseline", "--no-extra-ops", "--insert-steps", "0",
+           "--dim", str(args.dim), "--capacity-log2", str(args.capacity_log2), "--batch-log2", str(args.batch_log2),
+           "--lambdas", args.lambdas, "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--hit-frac", str(args.hit_frac), "--new-frac", str(args.new_frac)]
+    runs = []
+    for r in range(args.cold_runs):
+        log(f"cold run {r + 1} of {args.cold_runs}")
+        out = subprocess.run(cmd, capture_output=True, text=True)
+        if out.returncode != 0:
+            log(out.stderr[-2000:])
+            raise SystemExit(f"cold run {r + 1} failed with status {out.returncode}")
+        runs.append(json.loads(out.stdout.strip().splitlines()[-1]))
+    med = lambda xs: float(statistics.median(xs))
+    per = {}
+    for lam in runs[0]["detail"]["per_lambda"]:
+        rows = [r["detail"]["per_lambda"][lam] for r in runs]
+        per[lam] = {k: round(med([x[k] for x in rows]), 3) for k in ("find_bkvs", "upsert_bkvs")}
+        per[lam]["find_bkvs_runs"] = [x["find_bkvs"] for x in rows]
+    fb = [v["find_bkvs"] for v in per.values()]
+    print(json.dumps({"cold_runs": args.cold_runs, "dim": args.dim, "capacity_log2": args.capacity_log2,
+                      "combined_bkvs_median": round(med([r["value"] for r in runs]), 4),
+                      "combined_bkvs_runs": [r["value"] for r in runs],
+                      "per_lambda_median": per,
+                      "find_lambda_variation": round((max(fb) - min(fb)) / max(fb), 4)}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -1244,6 +1279,9 @@ def main():
         return
     if args.graph:
         graph_run(args)
+        return
+    if args.cold_runs:
+        cold_runs(args)
         return
     g = run_gpu(args)
     g["copy_GBps"] = copy_bandwidth()

@@ -2,6 +2,7 @@
 counts behind its roofline figures, and the code hash that ties a committed
 rocprofv3 summary to the kernel source it measured."""
 
+import json
 import os
 import subprocess
 import sys
@@ -55,3 +56,35 @@ def test_code_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
     changed.write_text(src.replace("kBlock = 256", "kBlock = 512", 1))
     monkeypatch.setattr(bench, "KERNEL_SOURCE", str(changed))
     assert bench.kernel_code_sha256() != h0
+
+
+def test_cold_runs_report_medians_of_fresh_processes(monkeypatch, capsys):
+    """--cold-runs starts one child process per run (this process never
+    touches the GPU) and reports the median of each per-lambda rate."""
+    finds = [[10.0, 9.0], [12.0, 8.0], [11.0, 10.0]]
+    calls = []
+
+    class Done:
+        returncode = 0
+        stderr = ""
+
+        def __init__(self, k):
+            per = {"0.5": {"find_bkvs": finds[k][0], "upsert_bkvs": 5.0 + k},
+                   "1.0": {"find_bkvs": finds[k][1], "upsert_bkvs": 4.0}}
+            self.stdout = "log line\n" + json.dumps({"value": 6.0 + k, "detail": {"per_lambda": per}})
+
+    def fake_run(cmd, **kw):
+        calls.append(cmd)
+        return Done(len(calls) - 1)
+
+    monkeypatch.setattr(bench.subprocess, "run", fake_run)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--cold-runs", "3", "--dim", "32"])
+    bench.main()
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert len(calls) == 3 and all("--dim" in c and c[c.index("--dim") + 1] == "32" for c in calls)
+    assert all("--cold-runs" not in c for c in calls)
+    assert out["per_lambda_median"]["0.5"]["find_bkvs"] == 11.0
+    assert out["per_lambda_median"]["1.0"]["find_bkvs"] == 9.0
+    assert out["per_lambda_median"]["0.5"]["upsert_bkvs"] == 6.0
+    assert out["combined_bkvs_median"] == 7.0
+    assert out["find_lambda_variation"] == pytest.approx(round((11.0 - 9.0) / 11.0, 4))
