@@ -61,6 +61,11 @@ HKV_MIXED_API hkv_status hkv_mixed_run(hkv_table* table, uint32_t threads, const
     args[j].scores = scores ? scores[j] : nullptr;
     args[j].out = out ? out[j] : nullptr;
     args[j].found = found ? found[j] : nullptr;
+    // every role's own buffers must be given (the library itself checks
+    // that they are device-accessible and large enough)
+    if (!args[j].keys) return HKV_EINVAL;
+    if (roles[j] == kFind && (!args[j].out || !args[j].found)) return HKV_EINVAL;
+    if (roles[j] != kFind && (!args[j].values || !args[j].scores)) return HKV_EINVAL;
   }
   std::atomic<uint32_t> ready{0};
   std::atomic<bool> go{false};

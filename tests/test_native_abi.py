@@ -115,3 +115,20 @@ def test_create_without_device_reports_hip_error():
     st, h, msg = _create()
     assert st == _native.HKV_EHIP
     assert "no HIP device" in msg
+
+
+def test_mixed_driver_rejects_null_arguments():
+    from hash_table_cache_amd import _native
+    from hash_table_cache_amd import build as hb
+
+    L = ctypes.CDLL(str(hb.MIXED_LIB_PATH))
+    P = ctypes.c_void_p
+    L.hkv_mixed_run.argtypes = [P, ctypes.c_uint32, P, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint32,
+                                P, P, P, P, P, ctypes.POINTER(ctypes.c_double)]
+    L.hkv_mixed_run.restype = ctypes.c_int32
+    secs = ctypes.c_double(0)
+    roles = (ctypes.c_int32 * 1)(0)
+    # no table, no roles, no threads, no pool: rejected before any HIP call
+    assert L.hkv_mixed_run(None, 1, roles, 1, 1, 1, None, None, None, None, None, ctypes.byref(secs)) == \
+        _native.HKV_EINVAL
+    assert L.hkv_mixed_run(None, 0, None, 1, 1, 1, None, None, None, None, None, None) == _native.HKV_EINVAL
