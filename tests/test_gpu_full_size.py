@@ -87,15 +87,17 @@ def check_find_exact(tab, q, resident_sorted, version_of):
     return int(f.sum())
 
 
-@pytest.mark.parametrize("lam,cap_log2", [(0.5, 26), (1.0, 26), (1.0, 28)])
-def test_lambda_sweep_table_at_full_size(lam, cap_log2):
+@pytest.mark.parametrize("lam,cap_log2,D", [(0.5, 26, 64), (1.0, 26, 64), (1.0, 28, 64), (0.75, 26, 32),
+                                             (0.9, 26, 32)])
+def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
     """2^26 slots (and 2^28, the largest capacity of the workloads, with its
-    64 GiB of rows in HBM), dim 64, single bucket: fill with distinct uniform
-    keys in 2^20 batches (score = batch index), then exact contents of 2000
-    sampled buckets, an exact 2^20-key find (90 % resident), one upsert step
-    (90 % resident, 10 % new), and the checks again."""
+    64 GiB of rows in HBM), dim 64 and the λ-sweep workload's own dim 32,
+    single bucket: fill with distinct uniform keys in 2^20 batches (score =
+    batch index), then exact contents of 2000 sampled buckets, an exact
+    2^20-key find (90 % resident), one upsert step (90 % resident, 10 % new),
+    and the checks again."""
     H = hkv()
-    cap, D, batch = 1 << cap_log2, 64, 1 << 20
+    cap, batch = 1 << cap_log2, 1 << 20
     seed = 0x484B56000000AA00 + int(lam * 100) + cap_log2
     tab = H.HashTable(cap, D)
     t0 = time.time()
