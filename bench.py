@@ -1083,8 +1083,12 @@ def run_extra_ops(args, tables, batch, dim, hit):
         found = torch.empty(batch, dtype=torch.uint8, device=dev)
         for name in ("find_ptr", "contains"):
             ms = []
-            tab.profile_start()
             for s in range(reps + 2):
+                if s == 2:  # two warm-up calls, untimed in both measures
+                    torch.cuda.synchronize()  # no queued work ahead of the first timed launch
+                    tab.profile_start()
+                if s == reps // 2 + 2:  # kernel times above, call times below
+                    ks = tab.profile_stop()
                 q = T["finds"][s % len(T["finds"])]
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
@@ -1094,9 +1098,9 @@ def run_extra_ops(args, tables, batch, dim, hit):
                     tab.contains(q, found_out=found)
                 e1.record()
                 ms.append((e0, e1))
-            ks = tab.profile_stop()
             torch.cuda.synchronize()
-            t = sorted(a.elapsed_time(b) for a, b in ms[2:])[len(ms[2:]) // 2]
+            timed = ms[reps // 2 + 2:]
+            t = sorted(a.elapsed_time(b) for a, b in timed)[len(timed) // 2]
             kn = ks[name]
             kavg = kn[1] / kn[0]
             byts = batch * locate_bytes_per_key(hit[lam], name == "find_ptr")
@@ -1105,8 +1109,10 @@ def run_extra_ops(args, tables, batch, dim, hit):
                            frac=round(byts / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
         # find with the stored scores returned (the metric's one extra run)
         scs = torch.empty(batch, dtype=torch.int64, device=dev)
-        tab.profile_start()
         for s in range(reps + 2):
+            if s == 2:
+                torch.cuda.synchronize()
+                tab.profile_start()
             tab.find(T["finds"][s % len(T["finds"])], values_out=T["out"], found_out=found, scores_out=scs)
         ks = tab.profile_stop()
         kavg = ks["find"][1] / ks["find"][0]
@@ -1133,7 +1139,6 @@ def run_extra_ops(args, tables, batch, dim, hit):
         evk = torch.empty(batch, dtype=torch.int64, device=dev)
         evv = torch.empty((batch, dim), dtype=torch.float32, device=dev)
         evs = torch.empty(batch, dtype=torch.int64, device=dev)
-        cnt = torch.zeros(1, dtype=torch.int64, device=dev)
         score0 = 1 << 30
         batches = []
         for j in range(2 * (reps + 2)):
@@ -1144,28 +1149,38 @@ def run_extra_ops(args, tables, batch, dim, hit):
             batches.append((uk, gen.values(uk, 7000 + j, dim),
                             torch.full((batch,), score0 + j, dtype=torch.int64, device=dev)))
         torch.cuda.synchronize()
+        # Each call is timed with events around it in one pass, and its kernels
+        # with the library's per-kernel events in a second pass on fresh
+        # batches (per-kernel events add host work per launch, which would
+        # leave the GPU waiting inside the timed calls). Each
+        # insert_and_evict call writes its own hand-back count.
+        cnts = torch.zeros(reps + 2, dtype=torch.int64, device=dev)
         for name, part in (("insert_and_evict", batches[:reps + 2]), ("find_or_insert", batches[reps + 2:])):
             ms = []
-            handed = []
-            tab.profile_start()
-            for uk, uv, usc in part:
+            for j, (uk, uv, usc) in enumerate(part):
+                if j == 2:  # the first two calls (workspace growth) are warm-up in both measures
+                    torch.cuda.synchronize()  # no queued work ahead of the first timed launch
+                    tab.profile_start()
+                if j == reps // 2 + 2:  # the rest of the calls: call times only
+                    ks = tab.profile_stop()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 if name == "insert_and_evict":
-                    tab.insert_and_evict(uk, uv, usc, out=(evk, evv, evs, cnt))
+                    tab.insert_and_evict(uk, uv, usc, out=(evk, evv, evs, cnts[j:j + 1]))
                 else:
                     tab.find_or_insert(uk, uv, usc, found_out=found)
                 e1.record()
                 ms.append((e0, e1))
-                if name == "insert_and_evict":
-                    handed.append(cnt.clone())
-            ks = tab.profile_stop()
             torch.cuda.synchronize()
-            t = sorted(a.elapsed_time(b) for a, b in ms[2:])[len(ms[2:]) // 2]
+            timed = ms[reps // 2 + 2:]
+            t = sorted(a.elapsed_time(b) for a, b in timed)[len(timed) // 2]
+            # per kernel: average, fastest and slowest launch (a single slow
+            # launch moves the average, not the call-time median)
             r[name] = dict(call_ms_median=round(t, 5), bkvs=round(batch / t / 1e6, 3),
-                           kernel_avg_ms={k: round(v[1] / v[0], 5) for k, v in ks.items()})
-            if handed:
-                r[name]["handed_back_per_call"] = round(sum(int(c.item()) for c in handed[2:]) / len(handed[2:]), 1)
+                           kernel_avg_ms={k: round(v[1] / v[0], 5) for k, v in ks.items()},
+                           kernel_min_max_ms={k: [round(v[3], 5), round(v[2], 5)] for k, v in ks.items()})
+            if name == "insert_and_evict":
+                r[name]["handed_back_per_call"] = round(float(cnts[2:].double().mean().item()), 1)
         out[str(lam)] = r
         log(f"lambda={lam}: other calls {r}")
     return out
