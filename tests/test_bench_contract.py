@@ -88,3 +88,38 @@ def test_cold_runs_report_medians_of_fresh_processes(monkeypatch, capsys):
     assert out["per_lambda_median"]["0.5"]["upsert_bkvs"] == 6.0
     assert out["combined_bkvs_median"] == 7.0
     assert out["find_lambda_variation"] == pytest.approx(round((11.0 - 9.0) / 11.0, 4))
+
+
+def test_json_line_carries_the_contract_fields(monkeypatch, capsys):
+    """With the GPU work replaced by canned results, main() prints one JSON
+    line with every field the benchmark contract requires: value as keys over
+    wall time, the roofline object of the dominant kernel (its traffic from
+    the committed rocprofv3 summary of the same kernel code and workload) and
+    the CPU oracle baseline."""
+    kern = {"find": dict(avg_ms=0.117, achieved_GBps=5400.0, frac=0.675, bytes_per_launch=638_000_000),
+            "upsert_probe": dict(avg_ms=0.14, achieved_GBps=4660.0, frac=0.5825, bytes_per_launch=653_000_000)}
+    g = dict(total_keys=8 * (1 << 20) * 20, wall=20 * 1.2e-3, dominant="upsert_probe", kernels=kern,
+             wall_timed_kernels=20 * 1.25e-3, gpu_busy_frac=0.95, detail={}, find_var=0.02, insert_new=None,
+             extra_ops={}, step_bytes=5.6e9, h=0.9)
+    monkeypatch.setattr(bench, "run_gpu", lambda args: dict(g))
+    monkeypatch.setattr(bench, "copy_bandwidth", lambda: 5000.0)
+    monkeypatch.setattr(bench, "pattern_ceiling", lambda dim: None)
+    monkeypatch.setattr(bench, "run_cpu_baseline", lambda args: dict(value=0.004, secs=8.0, total=14.0, rounds=16))
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    bench.main()
+    lines = [l for l in capsys.readouterr().out.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d
+    assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 3 and d["higher_is_better"] is True
+    assert d["value"] == pytest.approx(8 * (1 << 20) / 1.2e-3 / 1e9, rel=1e-3)
+    assert d["ms_per_step"] == pytest.approx(1.2)
+    assert "workload" in d["config"] and "model" not in d["config"]
+    r = d["roofline"]
+    assert r["kernel"] == "upsert_probe" and r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-3)
+    assert r["traffic"] == bench.profiled_traffic("upsert_probe", 64, 26)
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["unit"] == d["unit"] and c["sample"]
