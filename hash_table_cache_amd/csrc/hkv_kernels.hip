@@ -185,7 +185,8 @@ __device__ __forceinline__ uint32_t candidate_mask(const uint32_t (&w)[NW], uint
 // positions base1 + j, mask m2 over base2 + j). The first two candidate keys
 // are loaded back to back so that they cost one memory round trip; a third
 // candidate in the same lane is rare (about 1 in 4000 lanes) and is looped.
-// NT: the first two loads are nontemporal (readers only). Returns the table
+// The key loads are cacheable: the key lines of recent lookups may then be
+// served by the Infinity Cache, next to the digest lines. Returns the table
 // position of the matching slot or -1.
 // The candidate-key check split in two so that several keys' loads can be
 // in flight together: cand_issue picks the first two candidate positions and
@@ -199,7 +200,6 @@ struct Cand {
   bool h0, h1;
 };
 
-template <bool NT>
 __device__ __forceinline__ void cand_issue(Cand& c, const uint64_t* __restrict__ keys, uint32_t m1,
                                            uint64_t base1, uint32_t m2, uint64_t base2) {
   // candidate positions in order: the bits of m1 (over base1), then of m2
@@ -217,8 +217,8 @@ __device__ __forceinline__ void cand_issue(Cand& c, const uint64_t* __restrict__
   }
   c.k0 = 0;
   c.k1 = 0;
-  if (c.h0) c.k0 = NT ? __builtin_nontemporal_load(keys + c.p0) : keys[c.p0];
-  if (c.h1) c.k1 = NT ? __builtin_nontemporal_load(keys + c.p1) : keys[c.p1];
+  if (c.h0) c.k0 = keys[c.p0];
+  if (c.h1) c.k1 = keys[c.p1];
   c.m1 = m1;
   c.m2 = m2;
   c.base1 = base1;
@@ -242,12 +242,11 @@ __device__ __forceinline__ int64_t cand_finish(Cand& c, const uint64_t* __restri
   return hit;
 }
 
-template <bool NT>
 __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__ keys, uint64_t k,
                                                     uint32_t m1, uint64_t base1, uint32_t m2,
                                                     uint64_t base2) {
   Cand c;
-  cand_issue<NT>(c, keys, m1, base1, m2, base2);
+  cand_issue(c, keys, m1, base1, m2, base2);
   return cand_finish(c, keys, k);
 }
 
@@ -266,7 +265,7 @@ __device__ __forceinline__ uint32_t line_occupancy(const uint32_t (&w)[NW]) {
 // Group-wide probe of the key's candidate bucket(s). Returns the hit position
 // (same value in every lane of the group) or -1. When occ1/occ2 are given they
 // receive the occupancy of the first / second candidate bucket.
-template <int G, bool DUAL, bool NT = false>
+template <int G, bool DUAL>
 __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane, uint32_t* occ1 = nullptr,
                                          uint32_t* occ2 = nullptr) {
   constexpr int NW = kSlots / G / 4;
@@ -289,7 +288,7 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
     if constexpr (DUAL) {
       if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
     }
-    hit = match_candidates<NT>(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
+    hit = match_candidates(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
                                static_cast<uint64_t>(b2) * kSlots + off);
   }
   if (occ1) *occ1 = line_occupancy<G, NW>(w1);
@@ -331,7 +330,7 @@ __device__ __forceinline__ void probe_many(const TableView& t, const uint64_t (&
     if constexpr (DUAL) {
       if (b2[j] != b1[j] && !is_reserved(k[j])) m2 = candidate_mask<NW>(w2[j], pat[j]);
     }
-    cand_issue<true>(c[j], t.keys, m1, static_cast<uint64_t>(b1[j]) * kSlots + off, m2,
+    cand_issue(c[j], t.keys, m1, static_cast<uint64_t>(b1[j]) * kSlots + off, m2,
                      static_cast<uint64_t>(b2[j]) * kSlots + off);
   }
 #pragma unroll
@@ -350,7 +349,7 @@ template <int G, bool V4, bool DUAL, bool NT>
 __device__ __forceinline__ void find_one(const TableView& t, uint64_t i, uint64_t k, float* __restrict__ out,
                                          uint8_t* __restrict__ found, uint64_t* __restrict__ scores_out,
                                          int lane) {
-  const int64_t p = probe<G, DUAL, NT>(t, k, lane);
+  const int64_t p = probe<G, DUAL>(t, k, lane);
   if (p < 0) {
     if (lane == 0) found[i] = 0;
     return;
@@ -582,7 +581,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(TableView t, uint64_t n,
   const uint64_t i = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) / G;
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   if (i >= n) return;
-  const int64_t p = probe<G, DUAL, true>(t, keys[i], lane);
+  const int64_t p = probe<G, DUAL>(t, keys[i], lane);
   if (p < 0) return;
   if (values)
     copy_row<G, V4, true>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
@@ -622,7 +621,7 @@ __device__ __forceinline__ int own_find(const Owned& o, const TableView& t, uint
   const uint32_t valid = live >= 8 ? 0xFFu : (live <= 0 ? 0u : ((1u << live) - 1));
   const uint32_t m = (zero_byte_bits(o.dig0 ^ pat) | (zero_byte_bits(o.dig1 ^ pat) << 4)) & valid;
   const uint64_t base = static_cast<uint64_t>(o.b) * kSlots + first;
-  const int64_t p = match_candidates<false>(t.keys, k, m, base, 0u, base);
+  const int64_t p = match_candidates(t.keys, k, m, base, 0u, base);
   const int hit = p >= 0 ? static_cast<int>(p - static_cast<int64_t>(o.b) * kSlots) : -1;
   const uint64_t bits = group_bits<kInsG>(__ballot(hit >= 0));
   if (bits == 0) return -1;
@@ -911,7 +910,7 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     return;
   }
   uint32_t o1 = 0, o2 = 0;
-  const int64_t p = probe<G, DUAL, NT>(t, k, lane, &o1, &o2);
+  const int64_t p = probe<G, DUAL>(t, k, lane, &o1, &o2);
   if (p >= 0) {
     if constexpr (FETCH) {
       // (host-resident rows: cacheable loads, as in find)
