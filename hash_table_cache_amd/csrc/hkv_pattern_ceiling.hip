@@ -5,7 +5,8 @@
 // ballots. For find, per key (8 lanes): the 8-byte key (sequential), a
 // 128-byte digest line (random in 64 MiB), one 8-byte candidate key (random
 // in 512 MiB), for 90 % of keys a 4*dim-byte row (random) written out
-// (sequential) and a found byte.
+// (sequential) and a found byte. Cache policies as in the kernels: digest
+// lines and keys cacheable, rows nontemporal.
 // Run twice: with every address depending on the value the previous load
 // returned (find's chain: key -> line -> candidate -> row) and with all
 // addresses computed from the key index. A benchmark tool built next to the
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void pattern_kernel(const uint64_t* __restrict
   const int owner = static_cast<int>((h >> 40) & 7);
   uint64_t c = 0;
   const uint32_t wl = w.x ^ w.y ^ w.z ^ w.w;  // the whole line is used
-  if (lane == owner) c = __builtin_nontemporal_load(cand + (mix(h + (CHAIN ? after(wl) : 0)) & (ncand - 1)));
+  if (lane == owner) c = cand[mix(h + (CHAIN ? after(wl) : 0)) & (ncand - 1)];
   c = __shfl(c, owner, 8);
   // without the chain, the line and candidate values only feed the flag
   const uint8_t sink = (!CHAIN && (k == 0xDEADBEEFull || wl == 0xDEADBEEFu || c == 0xDEADBEEFull)) ? 2 : 0;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void upsert_pattern_kernel(const uint64_t* __r
   const int owner = static_cast<int>((h >> 40) & 7);
   const uint64_t slot = mix(h + after(w.x ^ w.y ^ w.z ^ w.w)) & (ncand - 1);
   uint64_t c = 0;
-  if (lane == owner) c = __builtin_nontemporal_load(cand + slot);
+  if (lane == owner) c = cand[slot];
   c = __shfl(c, owner, 8);
   if (mix(i) % 10 == 0) {
     if (lane == 0) {
