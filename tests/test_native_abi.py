@@ -132,3 +132,20 @@ def test_mixed_driver_rejects_null_arguments():
     assert L.hkv_mixed_run(None, 1, roles, 1, 1, 1, None, None, None, None, None, ctypes.byref(secs)) == \
         _native.HKV_EINVAL
     assert L.hkv_mixed_run(None, 0, None, 1, 1, 1, None, None, None, None, None, None) == _native.HKV_EINVAL
+
+
+def test_every_hip_build_targets_gfx950_without_packed_fp32():
+    """Every hipcc compile of the package (library, mixed-workload driver,
+    access-pattern program) targets gfx950 and turns packed fp32 instructions
+    off; and the built code object holds none of them."""
+    from hash_table_cache_amd import build as hb
+
+    flags = hb.compile_flags()
+    assert "--offload-arch=gfx950" in flags
+    i = flags.index("-packed-fp32-ops")
+    assert flags[i - 3:i + 1] == ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    # the kernels' own assembly, built here from source
+    out = subprocess.run([hb.hipcc(), *flags, "--offload-device-only", "-S", "-x", "hip",
+                          str(hb.CSRC / "hkv_kernels.hip"), "-o", "-"], capture_output=True, text=True, check=True)
+    for op in ("add", "mul", "fma"):
+        assert "v_pk_" + op + "_f32" not in out.stdout
