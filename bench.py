@@ -69,6 +69,10 @@ def parse_args():
     p.add_argument("--lambdas", default="0.5,0.75,0.9,1.0")
     p.add_argument("--hit-frac", type=float, default=0.9)
     p.add_argument("--new-frac", type=float, default=0.1, help="fraction of new keys in each upsert batch")
+    p.add_argument("--hit-pool", choices=("resident", "recent"), default="resident",
+                   help="where the resident keys of the find and upsert batches come from: sampled uniformly "
+                        "from the whole resident set (default), or from the 2*batch most recently inserted keys "
+                        "(a recency-skewed mix whose key lines partly stay in the Infinity Cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--insert-steps", type=int, default=5,
                    help="extra all-new-key insert batches on the full table, reported in detail")
@@ -908,16 +912,24 @@ def run_gpu(args):
         # Inputs of every step, generated now (outside the timed region).
         n_hit = int(round(batch * args.hit_frac))
         n_new = int(round(batch * args.new_frac))
-        recent = min(cursor, 2 * batch)
-        pool = gen.unique_keys(SEED, 1 + li, cursor - recent, recent, device=dev)
+        if args.hit_pool == "resident":
+            # every resident key (the table's own export): hits sampled
+            # uniformly from the whole resident set
+            pool = tab.export_batch(with_values=False)[0]
+        else:
+            recent = min(cursor, 2 * batch)
+            pool = gen.unique_keys(SEED, 1 + li, cursor - recent, recent, device=dev)
+        n_pool = pool.numel()
         finds, ups = [], []
         vals_pool = [gen.values(pool[:batch], 1000 + j, dim, SEED) for j in range(2)]
         for s in range(total_steps):
-            pick = torch.argsort(gen.counter_words(SEED, 100 + li, s * recent, recent, dev))
+            pick = torch.argsort(gen.counter_words(SEED, 100 + li, s * n_pool, n_pool, dev))
             hits = pool[pick[:n_hit]]
             miss = gen.unique_keys(SEED, 40 + li, s * batch, batch - n_hit, device=dev)
             fk = gen.shuffle(torch.cat([hits, miss]), SEED, 200 + li * 1000 + s)
-            res = pool[pick[n_hit:n_hit + (batch - n_new)]] if batch - n_new <= recent - n_hit else pool[pick[:batch - n_new]]
+            res = (pool[pick[n_hit:n_hit + (batch - n_new)]] if batch - n_new <= n_pool - n_hit
+                   else pool[pick[:batch - n_new]])
+            del pick
             new = gen.unique_keys(SEED, 60 + li, s * batch, n_new, device=dev)
             uk = gen.shuffle(torch.cat([res, new]), SEED, 300 + li * 1000 + s)
             sc = torch.full((batch,), step + s, dtype=torch.int64, device=dev)
@@ -1212,18 +1224,24 @@ def run_cpu_baseline(args):
             o.insert_or_assign(k, np.full(n, step, np.uint64), values=zeros[:n])
             cursor += n
             step += 1
-        recent = gen.unique_keys(SEED, 1 + li, cursor - batch, batch).numpy().view(np.uint64)
+        if args.hit_pool == "resident":
+            pool = o.export()["keys"]
+        else:
+            pool = gen.unique_keys(SEED, 1 + li, cursor - batch, batch).numpy().view(np.uint64)
         n_hit = int(round(batch * args.hit_frac))
         n_new = int(round(batch * args.new_frac))
+        # one random order of the pool; round r takes consecutive windows of
+        # it (distinct keys within a window)
+        order = pool[np.random.default_rng(SEED + li).permutation(pool.size)]
         for r in range(rounds):
-            rot = np.roll(recent, r * 7919)
-            fk = np.concatenate([rot[:n_hit],
+            w = np.arange(r * (2 * batch), r * (2 * batch) + 2 * batch) % order.size
+            fk = np.concatenate([order[w[:min(n_hit, order.size)]],
                                  gen.unique_keys(SEED, 40 + li, r * batch, batch - n_hit).numpy().view(np.uint64)])
-            uk = np.concatenate([rot[:batch - n_new],
+            uk = np.concatenate([order[w[batch:batch + min(batch - n_new, order.size)]],
                                  gen.unique_keys(SEED, 60 + li, r * batch, n_new).numpy().view(np.uint64)])
             t0 = time.perf_counter()
             o.find(fk)
-            o.insert_or_assign(uk, np.full(batch, step + r, np.uint64), values=zeros)
+            o.insert_or_assign(uk, np.full(uk.size, step + r, np.uint64), values=zeros[:uk.size])
             secs += time.perf_counter() - t0
             ops += 2 * batch
         o.close()
@@ -1239,7 +1257,7 @@ def cold_runs(args):
     cmd = [sys.executable, os.path.abspath(__file__), "--no-cpu-baseline", "--no-extra-ops", "--insert-steps", "0",
            "--dim", str(args.dim), "--capacity-log2", str(args.capacity_log2), "--batch-log2", str(args.batch_log2),
            "--lambdas", args.lambdas, "--steps", str(args.steps), "--warmup", str(args.warmup),
-           "--hit-frac", str(args.hit_frac), "--new-frac", str(args.new_frac)]
+           "--hit-frac", str(args.hit_frac), "--new-frac", str(args.new_frac), "--hit-pool", args.hit_pool]
     runs = []
     for r in range(args.cold_runs):
         log(f"cold run {r + 1} of {args.cold_runs}")
@@ -1329,7 +1347,10 @@ def main():
                          f"({int(args.hit_frac * 100)}% resident)"
                          + ("" if args.find_only else
                             f" + insert_or_assign 2^{args.batch_log2} ({int(round((1 - args.new_frac) * 100))}% resident, "
-                            f"{int(round(args.new_frac * 100))}% new), scores = step counter")),
+                            f"{int(round(args.new_frac * 100))}% new), scores = step counter")
+                         + ("; resident keys sampled uniformly from the whole resident set"
+                            if args.hit_pool == "resident" else
+                            "; resident keys sampled from the 2^(batch+1) most recently inserted")),
             "capacity": 1 << args.capacity_log2,
             "dim": args.dim,
             "batch": 1 << args.batch_log2,
