@@ -199,18 +199,44 @@ def copy_bandwidth(mib: int = 2048, reps: int = 10) -> float:
     return gbs
 
 
+PATTERN_SOURCE = os.path.join(ROOT, "bench_pattern_ceiling.hip")
+PATTERN_EXE = os.path.join(ROOT, "_build", "bench_pattern_ceiling")
+
+
+def build_pattern_ceiling() -> str:
+    """Compiles the access-pattern ceiling program (a stand-alone benchmark
+    of find's and the upsert probe's memory accesses, no table involved) with
+    hipcc for gfx950, beside the other build products. Returns its path."""
+    import pathlib
+
+    hb = _load_build_module()
+    os.makedirs(os.path.dirname(PATTERN_EXE), exist_ok=True)
+    tmp = PATTERN_EXE + ".tmp"
+    flags = [f for f in hb.compile_flags() if f != "-fvisibility=hidden"]
+    subprocess.run([hb.hipcc(), *flags, "-x", "hip", PATTERN_SOURCE, "-o", tmp], check=True)
+    pathlib.Path(tmp).replace(PATTERN_EXE)
+    return PATTERN_EXE
+
+
+def _load_build_module():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "hkv_build", os.path.join(ROOT, "hash_table_cache_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def pattern_ceiling(dim: int = 64):
     """Runs the access-pattern ceiling program (find's memory accesses on a
     2^26-slot table with rows of `dim` floats, without its arithmetic, with
     and without the chain of dependent loads) in a child process; returns its
-    JSON or None."""
-
-    from hash_table_cache_amd import build as hb
-
-    if not hb.PATTERN_EXE.exists():
+    JSON, or None when the program has not been built."""
+    if not os.path.exists(PATTERN_EXE):
         return None
     try:
-        r = subprocess.run([str(hb.PATTERN_EXE), str(dim)], capture_output=True, text=True, timeout=120, check=True)
+        r = subprocess.run([PATTERN_EXE, str(dim)], capture_output=True, text=True, timeout=120, check=True)
         return json.loads(r.stdout)
     except (subprocess.SubprocessError, ValueError) as e:
         log(f"pattern ceiling program failed: {e}")

@@ -9,8 +9,8 @@
 // lines and keys cacheable, rows nontemporal.
 // Run twice: with every address depending on the value the previous load
 // returned (find's chain: key -> line -> candidate -> row) and with all
-// addresses computed from the key index. A benchmark tool built next to the
-// library; it does not use the table.
+// addresses computed from the key index. A benchmark tool, built by
+// bench.build_pattern_ceiling(); it does not use the table.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -2,8 +2,10 @@
 
 Argument marshalling only: every step of every operation runs in the HIP
 library. Tensors are passed by ``data_ptr()``; the stream defaults to torch's
-current stream on the table's device. If the library has not been built the
-import of this module fails; there is no fallback implementation.
+current stream on the table's device. The library is loaded on first use
+(``load()``), so that the build script can run from a fresh checkout; if it
+has not been built by then, the call raises ImportError. There is no
+fallback implementation.
 
 64-bit keys and scores are ``torch.int64`` (or ``torch.uint64``) tensors that
 hold the unsigned bit patterns.
@@ -120,12 +122,20 @@ def _load() -> ctypes.CDLL:
     return L
 
 
-lib = _load()
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """The loaded ``libhkv.so`` (loaded on the first call)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
 
 
 def _check(status: int) -> None:
     if status != HKV_OK:
-        raise HkvError(status, lib.hkv_last_error().decode(errors="replace"))
+        raise HkvError(status, load().hkv_last_error().decode(errors="replace"))
 
 
 _U64_DTYPES = (torch.int64, torch.uint64)
@@ -158,23 +168,23 @@ def hkv_create(capacity: int, dim: int, dual_bucket: bool = False, values_on_hos
     opt = HkvOptions(int(capacity), int(dim), BUCKET_SLOTS, int(bool(dual_bucket)),
                      int(bool(values_on_host)), int(device), int(flags), int(hbm_value_bytes))
     h = ctypes.c_void_p()
-    _check(lib.hkv_create(ctypes.byref(opt), ctypes.byref(h)))
+    _check(load().hkv_create(ctypes.byref(opt), ctypes.byref(h)))
     return h
 
 
 def hkv_destroy(table) -> None:
-    _check(lib.hkv_destroy(table))
+    _check(load().hkv_destroy(table))
 
 
 def hkv_get_options(table) -> HkvOptions:
     o = HkvOptions()
-    _check(lib.hkv_get_options(table, ctypes.byref(o)))
+    _check(load().hkv_get_options(table, ctypes.byref(o)))
     return o
 
 
 def hkv_find(table, keys, values_out, found_out, scores_out=None, stream=None, *, dim, device):
     n = keys.numel()
-    _check(lib.hkv_find(
+    _check(load().hkv_find(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values_out, (torch.float32,), n * dim, "values_out"),
@@ -186,7 +196,7 @@ def hkv_find(table, keys, values_out, found_out, scores_out=None, stream=None, *
 def hkv_find_ptr(table, keys, ptrs_out, found_out=None, scores_out=None, stream=None, *, device):
     """ptrs_out: int64 tensor of n row addresses (0 on a miss)."""
     n = keys.numel()
-    _check(lib.hkv_find_ptr(
+    _check(load().hkv_find_ptr(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(ptrs_out, _U64_DTYPES, n, "ptrs_out"),
@@ -197,7 +207,7 @@ def hkv_find_ptr(table, keys, ptrs_out, found_out=None, scores_out=None, stream=
 
 def hkv_contains(table, keys, found_out, stream=None, *, device):
     n = keys.numel()
-    _check(lib.hkv_contains(
+    _check(load().hkv_contains(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(found_out, (torch.uint8, torch.bool), n, "found_out"),
@@ -207,7 +217,7 @@ def hkv_contains(table, keys, found_out, stream=None, *, device):
 def hkv_insert_and_evict(table, keys, values, scores, ev_keys, ev_values, ev_scores, ev_count, stream=None, *,
                          dim, device):
     n = keys.numel()
-    _check(lib.hkv_insert_and_evict(
+    _check(load().hkv_insert_and_evict(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values, (torch.float32,), n * dim, "values"),
@@ -221,7 +231,7 @@ def hkv_insert_and_evict(table, keys, values, scores, ev_keys, ev_values, ev_sco
 
 def hkv_find_or_insert(table, keys, values, scores, found_out=None, stream=None, *, dim, device):
     n = keys.numel()
-    _check(lib.hkv_find_or_insert(
+    _check(load().hkv_find_or_insert(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values, (torch.float32,), n * dim, "values"),
@@ -232,7 +242,7 @@ def hkv_find_or_insert(table, keys, values, scores, found_out=None, stream=None,
 
 def hkv_insert_or_assign(table, keys, values, scores, stream=None, *, dim, device):
     n = keys.numel()
-    _check(lib.hkv_insert_or_assign(
+    _check(load().hkv_insert_or_assign(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values, (torch.float32,), n * dim, "values"),
@@ -242,7 +252,7 @@ def hkv_insert_or_assign(table, keys, values, scores, stream=None, *, dim, devic
 
 def hkv_assign(table, keys, values=None, scores=None, stream=None, *, dim, device):
     n = keys.numel()
-    _check(lib.hkv_assign(
+    _check(load().hkv_assign(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values, (torch.float32,), n * dim, "values", nullable=True),
@@ -252,14 +262,14 @@ def hkv_assign(table, keys, values=None, scores=None, stream=None, *, dim, devic
 
 def hkv_size(table, stream=None, *, device) -> int:
     out = ctypes.c_uint64(0)
-    _check(lib.hkv_size(table, ctypes.byref(out), _stream(stream, device)))
+    _check(load().hkv_size(table, ctypes.byref(out), _stream(stream, device)))
     return int(out.value)
 
 
 def hkv_export_batch(table, offset, n_slots, keys_out, values_out, scores_out, pos_out, count_out,
                      stream=None, *, dim, device):
     m = int(n_slots)
-    _check(lib.hkv_export_batch(
+    _check(load().hkv_export_batch(
         table, int(offset), m,
         _ptr(keys_out, _U64_DTYPES, 0, "keys_out"),
         _ptr(values_out, (torch.float32,), 0, "values_out", nullable=True),
@@ -270,7 +280,7 @@ def hkv_export_batch(table, offset, n_slots, keys_out, values_out, scores_out, p
 
 
 def hkv_profile_start(table) -> None:
-    _check(lib.hkv_profile_start(table))
+    _check(load().hkv_profile_start(table))
 
 
 def hkv_profile_stop(table) -> dict:
@@ -278,7 +288,7 @@ def hkv_profile_stop(table) -> dict:
     cap = 16
     out = (HkvKernelStat * cap)()
     count = ctypes.c_uint32(0)
-    _check(lib.hkv_profile_stop(table, out, cap, ctypes.byref(count)))
+    _check(load().hkv_profile_stop(table, out, cap, ctypes.byref(count)))
     return {out[j].name.decode(): (int(out[j].launches), float(out[j].total_ms), float(out[j].max_ms),
                                    float(out[j].min_ms), float(out[j].sumsq_ms2))
             for j in range(min(cap, count.value))}

@@ -1,10 +1,13 @@
-"""Builds the HIP library ``_lib/libhkv.so`` for gfx950 with hipcc.
+"""Builds the HIP library ``_lib/libhkv.so`` for gfx950 with hipcc, and the
+multi-threaded mixed-workload driver ``_lib/libhkv_mixed.so`` on top of it.
 
 Run as ``python -m hash_table_cache_amd.build``. Cross-compiles without a GPU.
+The objects compile in parallel.
 """
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import pathlib
 import subprocess
@@ -22,9 +25,6 @@ SOURCES = [CSRC / "hkv_kernels.hip", CSRC / "hkv_runtime.cpp"]
 # library of its own on top of the C ABI
 MIXED_SOURCE = CSRC / "hkv_mixed_driver.cpp"
 MIXED_LIB_PATH = PKG / "_lib" / "libhkv_mixed.so"
-# access-pattern ceiling of find (a stand-alone benchmark program)
-PATTERN_SOURCE = CSRC / "hkv_pattern_ceiling.hip"
-PATTERN_EXE = PKG / "_lib" / "hkv_pattern_ceiling"
 ARCH = "gfx950"
 
 
@@ -48,37 +48,37 @@ def compile_flags() -> list[str]:
     ]
 
 
+def _run(cmd: list[str], verbose: bool) -> None:
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    if verbose and r.stderr:
+        sys.stderr.write(r.stderr)
+
+
+def _compile(src: pathlib.Path, verbose: bool) -> pathlib.Path:
+    obj = BUILD_DIR / (src.name + ".o")
+    lang = ["-x", "hip"] if src.suffix == ".hip" else []
+    _run([hipcc(), *compile_flags(), *lang, "-c", str(src), "-o", str(obj)], verbose)
+    return obj
+
+
 def build(verbose: bool = False) -> pathlib.Path:
     BUILD_DIR.mkdir(parents=True, exist_ok=True)
     LIB_PATH.parent.mkdir(parents=True, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = BUILD_DIR / (src.name + ".o")
-        lang = ["-x", "hip"] if src.suffix == ".hip" else []
-        cmd = [hipcc(), *compile_flags(), *lang, "-c", str(src), "-o", str(obj)]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-        objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=3) as pool:
+        futs = [pool.submit(_compile, src, verbose) for src in (*SOURCES, MIXED_SOURCE)]
+        objs = [f.result() for f in futs]
     tmp = LIB_PATH.with_suffix(".so.tmp")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs[:2])], verbose)
     tmp.replace(LIB_PATH)
-    obj = BUILD_DIR / (MIXED_SOURCE.name + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", str(MIXED_SOURCE), "-o", str(obj)]
-    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
     tmp = MIXED_LIB_PATH.with_suffix(".so.tmp")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), str(obj),
-           f"-L{LIB_PATH.parent}", "-lhkv", "-Wl,-rpath,$ORIGIN", "-pthread"]
-    subprocess.run(cmd, check=True)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), str(objs[2]),
+          f"-L{LIB_PATH.parent}", "-lhkv", "-Wl,-rpath,$ORIGIN", "-pthread"], verbose)
     tmp.replace(MIXED_LIB_PATH)
-    tmp = PATTERN_EXE.with_suffix(".tmp")
-    cmd = [hipcc(), *[f for f in compile_flags() if f != "-fvisibility=hidden"], "-x", "hip", str(PATTERN_SOURCE),
-           "-o", str(tmp)]
-    subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-    tmp.replace(PATTERN_EXE)
     return LIB_PATH
 
 

@@ -121,8 +121,13 @@ typedef struct hkv_options {
  */
 hkv_status hkv_create(const hkv_options* options, hkv_table** out);
 
-/* hkv_destroy - wait for the table's outstanding work, free everything.
- * NULL is accepted and ignored. */
+/* hkv_destroy - end of the table's lifetime: waits for the table's
+ * outstanding work on every stream, then frees all storage hkv_create
+ * allocated (the §3.2 bucket arrays, the §3.6 host-memory value rows) and the
+ * inserter workspaces. The paper's API (§4.1) is that of a container object
+ * and names no explicit teardown call; releasing everything the table owns
+ * at its end is the reading taken here. NULL is accepted and ignored; the
+ * handle must not be used afterwards. Always returns HKV_OK. */
 hkv_status hkv_destroy(hkv_table* table);
 
 /* hkv_get_options - copy the options the table was created with. */

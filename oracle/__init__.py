@@ -107,8 +107,6 @@ def lib():
     L.oracle_size.restype = u64
     L.oracle_export.argtypes = [vp, u64, u64, P64, PF, P64, P64, P64]
     L.oracle_export.restype = u64
-    L.oracle_digests.argtypes = [vp, P8]
-    L.oracle_digests.restype = None
     L.oracle_probe_stats.argtypes = [vp, P64]
     L.oracle_probe_stats.restype = None
     L.oracle_reset_probe_stats.argtypes = [vp]
@@ -302,11 +300,6 @@ class OracleTable:
         values = np.empty((m_max, self.dim), np.float32)
         m = self._lib.oracle_export(self._h, offset, n_slots, _u64p(keys), _f32p(values), _u64p(scores), _u64p(pos), None)
         return dict(keys=keys[:m], scores=scores[:m], pos=pos[:m], values=values[:m])
-
-    def digests(self) -> np.ndarray:
-        out = np.empty(self.capacity, np.uint8)
-        self._lib.oracle_digests(self._h, _u8p(out))
-        return out
 
     def probe_stats(self) -> tuple[int, int]:
         out = np.zeros(2, np.uint64)

@@ -24,7 +24,6 @@
 // verification value, which exercises the same 64-bit finalizer.
 
 #include <cstdint>
-#include <cstring>
 #include <new>
 #include <vector>
 
@@ -566,12 +565,6 @@ uint64_t oracle_export(const oracle_table* h, uint64_t offset, uint64_t n_slots,
     ++m;
   }
   return m;
-}
-
-// Raw digest of every slot (capacity bytes), for checks on the digest line.
-void oracle_digests(const oracle_table* h, uint8_t* out) {
-  const Table& t = *reinterpret_cast<const Table*>(h);
-  std::memcpy(out, t.digest.data(), t.capacity);
 }
 
 // Find instrumentation: [bucket scans, digest false positives].

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     for name in declared_functions():
         assert name in exported, name
-        assert getattr(_native.lib, name) is not None
+        assert getattr(_native.load(), name) is not None
     assert set(_native.EXPORTS) == set(declared_functions())
     # nothing but the ABI is exported from the library's own code
     assert {n for n in exported if n.startswith("hkv")} == set(declared_functions())
@@ -65,8 +65,8 @@ def _create(**kw):
     opt = _native.HkvOptions(o["capacity"], o["dim"], o["bucket_slots"], o["dual_bucket"],
                              o["values_on_host"], o["device"], o["flags"])
     h = ctypes.c_void_p()
-    st = _native.lib.hkv_create(ctypes.byref(opt), ctypes.byref(h))
-    return st, h, _native.lib.hkv_last_error().decode()
+    st = _native.load().hkv_create(ctypes.byref(opt), ctypes.byref(h))
+    return st, h, _native.load().hkv_last_error().decode()
 
 
 @pytest.mark.parametrize("kw,needle", [
@@ -89,7 +89,7 @@ def test_create_rejects_bad_options(kw, needle):
 def test_null_arguments():
     from hash_table_cache_amd import _native
 
-    L = _native.lib
+    L = _native.load()
     assert L.hkv_create(None, None) == _native.HKV_EINVAL
     assert L.hkv_find(None, 1, None, None, None, None, None) == _native.HKV_EINVAL
     assert L.hkv_insert_or_assign(None, 1, None, None, None, None) == _native.HKV_EINVAL
