@@ -1,16 +1,19 @@
 """Full-size GPU checks, in the launch configuration the benchmark uses.
 
 At these sizes the oracle cannot replay whole workloads in test time, so the
-checks are (a) exact on samples the closed form fixes one by one - the contents
-of sampled buckets are the top 128 by (score, key) of every key routed there
-(single-bucket mode, distinct keys, scores never decreasing) - and exact on
-every find output (found iff exported, row = the row generated for the
-key's last write, score = last written score), and (b) invariants at any size:
-no key resident twice, at most 128 entries per bucket, every entry in one of
-its candidate buckets, size = exported count <= capacity, and for dual-bucket
+checks are (a) exact against the closed form of single-bucket mode (distinct
+keys per batch, scores never decreasing): every bucket holds exactly the top
+128 by (score, key) of every key routed there, compared on all buckets with
+library sorts (tests/closed_form.py), and exact on every find output (found
+iff resident by the closed form, row = the row generated for the key's last
+write, score = last written score), and (b) invariants at any size: no key
+resident twice, at most 128 entries per bucket, every entry in one of its
+candidate buckets, size = exported count <= capacity, and for dual-bucket
 mode top-N retention against the ideal top N by (score, key).
 
 Bucket routing of the expected sets comes from the oracle's route function.
+The inputs of every step (resident keys to query, update or re-insert) are
+drawn from the closed form's resident set, not from the table.
 """
 
 import time
@@ -19,6 +22,7 @@ import numpy as np
 import pytest
 import torch
 
+import closed_form as cf
 import hkv_inputs as gen
 import oracle
 from conftest import gpu_available
@@ -93,9 +97,10 @@ def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
     """2^26 slots (and 2^28, the largest capacity of the workloads, with its
     64 GiB of rows in HBM), dim 64 and the λ-sweep workload's own dim 32,
     single bucket: fill with distinct uniform keys in 2^20 batches (score =
-    batch index), then exact contents of 2000 sampled buckets, an exact
-    2^20-key find (90 % resident), one upsert step (90 % resident, 10 % new),
-    and the checks again."""
+    batch index; the size after every batch equal to the closed form's),
+    then the exact contents of every bucket, an exact 2^20-key find (90 %
+    resident), one upsert step (90 % resident, 10 % new), and the checks
+    again."""
     H = hkv()
     cap, batch = 1 << cap_log2, 1 << 20
     seed = 0x484B56000000AA00 + int(lam * 100) + cap_log2
@@ -104,13 +109,15 @@ def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
     target = int(lam * cap)
     cursor, step = 0, 0
     score_parts = []
-    while tab.size() < target:
-        n = batch if lam >= 1.0 else min(batch, target - tab.size())
+    fill = cf.FillCount(cap, dev())
+    while fill.size() < target:
+        n = batch if lam >= 1.0 else min(batch, target - fill.size())
         step += 1
         k = gen.unique_keys(seed, 1, cursor, n, device=dev())
         tab.insert_or_assign(k, gen.values(k, step, D), torch.full((n,), step, dtype=torch.int64, device=dev()))
         score_parts.append((cursor, n, step))
         cursor += n
+        assert tab.size() == fill.add(k), f"size after batch {step} differs from the closed form"
     log(f"lambda {lam}, 2^{cap_log2} slots: {cursor} keys in {step} batches, size {tab.size()}, "
         f"{time.time() - t0:.1f}s")
     allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
@@ -125,32 +132,11 @@ def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
         pos = torch.searchsorted(sk, k)
         assert torch.equal(sk[pos], k)
         assert torch.equal(ss[pos], s)
-        # sampled buckets: exact top-128 by (score, key) of every key routed there
-        B = cap // SLOTS
-        rng = np.random.default_rng(int(lam * 1000) + allk.numel())
-        sample = np.sort(rng.choice(B, size=2000, replace=False)).astype(np.uint64)
-        akn, asn = u64(allk), alls.cpu().numpy().astype(np.uint64)
-        b1, _ = route_all(akn, cap)
-        sel = np.zeros(B, bool)
-        sel[sample.astype(np.int64)] = True
-        m = sel[b1.astype(np.int64)]
-        kk, ssel, bb = akn[m], asn[m], b1[m]
-        o = np.lexsort((kk, ssel, bb))
-        kk, bb = kk[o], bb[o]
-        expect = {}
-        for b in sample.tolist():
-            expect[b] = set()
-        ub, start, cnt = np.unique(bb, return_index=True, return_counts=True)
-        for b, st, c in zip(ub.tolist(), start.tolist(), cnt.tolist()):
-            expect[b] = set(kk[st + max(0, c - SLOTS):st + c].tolist())
-        kn, pn = u64(k), u64(p)
-        bk = pn // SLOTS
-        msk = sel[bk.astype(np.int64)]
-        got = {b: set() for b in sample.tolist()}
-        for key, b in zip(kn[msk].tolist(), bk[msk].tolist()):
-            got[b].add(key)
-        assert got == expect
-        return torch.sort(k).values
+        # every bucket: exactly the top 128 by (score, key) of the keys routed there
+        resident = cf.assert_table_matches(k, p, allk, alls, cap)
+        log(f"lambda {lam}, 2^{cap_log2} slots: all {cap // SLOTS} buckets equal the closed form "
+            f"({resident.numel()} entries)")
+        return resident
 
     resident = check(allk, alls)
     # exact find, 90 % resident (recent keys), 10 % never inserted
@@ -268,14 +254,15 @@ def test_continuous_online_dual_bucket_zipf_retention():
 
 def test_tiered_values_dual_bucket_zipf():
     """Values in pinned, GPU-mapped host memory, dual bucket, dim 128, keys
-    Zipf(1.2) over 2^32 ids, LRU scores (value version = score). Capacity 2^26
-    (32 GiB of pinned rows; the workload's 2^28 needs 128 GiB). Warm cache:
-    ranks 1 .. 1.0625 * capacity in 2^19 batches from the coldest down to the
-    hottest, so that with LRU scores the hottest ranks are the most recent;
-    then 3 steps of a 2^20-draw find and a 2^19-draw upsert. Invariants and
-    exact find."""
+    Zipf(1.2) over 2^32 ids, LRU scores (value version = score). Capacity 2^27
+    as in the benchmark (64 GiB of pinned rows; the workload's 2^28 needs
+    128 GiB, more than the host pins). Warm cache: ranks 1 .. 1.0625 *
+    capacity in 2^19 batches from the coldest down to the hottest, so that
+    with LRU scores the hottest ranks are the most recent; then 5 + 20 steps
+    of a 2^20-draw find and a 2^19-draw upsert, the benchmark's step count.
+    Invariants, and an exact find every step against the exported table."""
     H = hkv()
-    cap, D = 1 << 26, 128
+    cap, D = 1 << 27, 128
     seed = 0x484B560000000005
     tab = H.HashTable(cap, D, dual_bucket=True, values_on_host=True)
     t0 = time.time()
@@ -289,9 +276,9 @@ def test_tiered_values_dual_bucket_zipf():
         tab.insert_or_assign(k, gen.values(k, step, D), torch.full((k.numel(),), step, dtype=torch.int64, device=dev()))
     log(f"tiered: filled ranks {cap + cap // 16}..1 in {step} batches, size {tab.size()}, {time.time() - t0:.1f}s")
     zipf = gen.Zipf(1.2, 1 << 32)
-    last = {}
     f_ms, f_keys = 0.0, 0
-    for j in range(3):
+    warm, steps = 5, 20
+    for j in range(warm + steps):
         step += 1
         q = zipf.draw(seed, 1, j * (1 << 20), 1 << 20, device=dev())
         k, _, s, p = export_all(tab)
@@ -309,10 +296,12 @@ def test_tiered_values_dual_bucket_zipf():
         tab.find(q, values_out=out, found_out=fnd)
         e1.record()
         torch.cuda.synchronize()
-        f_ms += e0.elapsed_time(e1)
-        f_keys += q.numel()
+        if j >= warm:
+            f_ms += e0.elapsed_time(e1)
+            f_keys += q.numel()
         hits = check_find_exact(tab, q, resident, version)
-        log(f"tiered: step {j}: {hits}/{q.numel()} hits")
+        if j % 5 == 4:
+            log(f"tiered: step {j}: {hits}/{q.numel()} hits, size {k.numel()}")
         u = torch.unique(zipf.draw(seed, 2, j * (1 << 19), 1 << 19, device=dev()))
         tab.insert_or_assign(u, gen.values(u, step, D), torch.full((u.numel(),), step, dtype=torch.int64, device=dev()))
     k, _, s, p = export_all(tab)
@@ -320,39 +309,45 @@ def test_tiered_values_dual_bucket_zipf():
     b1, b2 = route_all(u64(k), cap, dual=True)
     bk = u64(p) // SLOTS
     assert np.all((bk == b1) | (bk == b2))
-    log(f"tiered: find {f_keys / f_ms / 1e6:.4f} B-KV/s ({f_ms / 3:.2f} ms per 2^20-key batch, rows over the host link)")
+    log(f"tiered: find {f_keys / f_ms / 1e6:.4f} B-KV/s ({f_ms / steps:.2f} ms per 2^20-key batch, "
+        f"rows over the host link)")
     tab.close()
 
 
 def test_mixed_reader_updater_inserter_at_full_size():
     """2^27 slots, dim 64, single bucket, lambda = 1: fill with distinct
-    uniform keys (score = step), then per step, in this order: a find of 2^20
-    keys (90 % resident), an assign of 2^19 resident keys (new row, score =
-    step), an insert_or_assign of 2^18 keys (half new, half resident, score =
-    step). Exact find after every step against the tracked last writes;
-    invariants at the end. Throughput of each call is logged."""
+    uniform keys (score = step; size after every batch = the closed form's),
+    then 5 + 20 steps, each in this order: a find of 2^20 keys (90 %
+    resident), an assign of 2^19 resident keys (new row, score = step), an
+    insert_or_assign of 2^18 keys (half new, half resident, score = step).
+    Resident keys are drawn from the closed form's resident set. Exact find
+    after every step (found iff resident by the closed form, rows of the last
+    writes); at the end every bucket equals the closed form and every score
+    is the last written one. Throughput of each call is logged."""
     H = hkv()
     cap, D = 1 << 27, 64
     seed = 0x484B560000000004
     tab = H.HashTable(cap, D)
     step, cursor = 0, 0
-    while tab.size() < cap:
+    fill = cf.FillCount(cap, dev())
+    while fill.size() < cap:
         step += 1
         k = gen.unique_keys(seed, 1, cursor, 1 << 20, device=dev())
         cursor += 1 << 20
         tab.insert_or_assign(k, gen.values(k, step, D), torch.full((k.numel(),), step, dtype=torch.int64, device=dev()))
+        assert tab.size() == fill.add(k)
     log(f"mixed: filled with {cursor} keys in {step} batches")
-    # last-write version of every key ever written (version = score = step)
+    # every key ever written, its bucket and its last-write version (= score)
     allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
-    allv = torch.repeat_interleave(torch.arange(1, step + 1, dtype=torch.int64, device=dev()), 1 << 20)
-    order = torch.argsort(allk)
-    sk, sv = allk[order], allv[order].clone()
+    allb = cf.buckets_of(allk, cap)
+    alls = torch.repeat_interleave(torch.arange(1, step + 1, dtype=torch.int64, device=dev()), 1 << 20)
     times = {"find": 0.0, "assign": 0.0, "insert_or_assign": 0.0}
-    steps = 5
-    for j in range(steps):
+    warm, steps = 5, 20
+    for j in range(warm + steps):
         step += 1
-        k, _, s, p = export_all(tab)
-        resident = torch.sort(k).values
+        resident = cf.resident_keys(allk, alls, cap, allb)
+        o = torch.argsort(allk)
+        sk, sv = allk[o], alls[o]
         perm = torch.randperm(resident.numel(), device=dev())
         q = gen.shuffle(torch.cat([resident[perm[: 943718]], gen.unique_keys(seed, 2, j << 20, 104858, device=dev())]),
                         seed, 10 + j)
@@ -376,26 +371,32 @@ def test_mixed_reader_updater_inserter_at_full_size():
         tab.insert_or_assign(uk, uv, usc)
         ev[3].record()
         torch.cuda.synchronize()
-        times["find"] += ev[0].elapsed_time(ev[1])
-        times["assign"] += ev[1].elapsed_time(ev[2])
-        times["insert_or_assign"] += ev[2].elapsed_time(ev[3])
+        if j >= warm:
+            times["find"] += ev[0].elapsed_time(ev[1])
+            times["assign"] += ev[1].elapsed_time(ev[2])
+            times["insert_or_assign"] += ev[2].elapsed_time(ev[3])
         # the find saw the table before this step's writes
         idx = torch.clamp(torch.searchsorted(resident, q), max=resident.numel() - 1)
         expect = resident[idx] == q
         assert torch.equal(fnd.bool(), expect)
         ver = sv[torch.searchsorted(sk, q[expect])]
         assert torch.equal(out[expect].view(torch.int32), gen.values(q[expect], ver, D).view(torch.int32))
-        # record this step's writes
-        sk = torch.cat([sk, new])
-        sv = torch.cat([sv, torch.zeros(new.numel(), dtype=torch.int64, device=dev())])
-        o = torch.argsort(sk)
-        sk, sv = sk[o], sv[o]
-        sv[torch.searchsorted(sk, ak)] = step
-        sv[torch.searchsorted(sk, uk)] = step
+        # this step's writes: assigned and re-inserted keys take the step as
+        # score, new keys join with it
+        alls = alls.clone()
+        o_all = torch.argsort(allk)
+        at = o_all[torch.searchsorted(allk[o_all], torch.cat([ak, uk[~torch.isin(uk, new)]]))]
+        alls[at] = step
+        allk = torch.cat([allk, new])
+        allb = torch.cat([allb, cf.buckets_of(new, cap)])
+        alls = torch.cat([alls, torch.full((new.numel(),), step, dtype=torch.int64, device=dev())])
     k, _, s, p = export_all(tab)
     check_invariants(tab, k, p, cap)
+    o = torch.argsort(allk)
+    sk, sv = allk[o], alls[o]
     assert torch.equal(s, sv[torch.searchsorted(sk, k)])
-    resident = torch.sort(k).values
+    resident = cf.assert_table_matches(k, p, allk, alls, cap, allb)
+    log(f"mixed: after {warm + steps} steps all {cap // SLOTS} buckets equal the closed form")
     check_find_exact(tab, gen.shuffle(resident[: 1 << 20], seed, 99), resident,
                      lambda kk: sv[torch.searchsorted(sk, kk)])
     n = {"find": 1 << 20, "assign": 1 << 19, "insert_or_assign": 1 << 18}
@@ -413,19 +414,22 @@ def test_other_calls_at_full_size():
     after, each entry with the row and score of its last write.
     find_or_insert (90 % resident, 10 % new): found iff resident before, hits
     return the stored row, misses keep theirs; afterwards every resident key
-    carries its last written score."""
+    carries its last written score. After every write call every bucket
+    equals the closed form, and resident keys are drawn from it."""
     H = hkv()
     cap, D, batch = 1 << 26, 64, 1 << 20
     seed = 0x484B56000000BB00
     tab = H.HashTable(cap, D)
     cursor, step = 0, 0
     parts = []
-    while tab.size() < cap:
+    fill = cf.FillCount(cap, dev())
+    while fill.size() < cap:
         step += 1
         k = gen.unique_keys(seed, 1, cursor, batch, device=dev())
         tab.insert_or_assign(k, gen.values(k, step, D), torch.full((batch,), step, dtype=torch.int64, device=dev()))
         parts.append((batch, step))
         cursor += batch
+        assert tab.size() == fill.add(k)
     allk = gen.unique_keys(seed, 1, 0, cursor, device=dev())
     alls = torch.cat([torch.full((n,), st, dtype=torch.int64, device=dev()) for n, st in parts])
     order = torch.argsort(allk)
@@ -437,7 +441,9 @@ def test_other_calls_at_full_size():
     k, _, s, p = export_all(tab)
     check_invariants(tab, k, p, cap)
     ko = torch.argsort(k)
-    rk, rp = k[ko], p[ko]  # resident keys sorted, with their positions
+    rp = p[ko]  # positions of the exported keys in sorted key order
+    rk = cf.assert_table_matches(k, p, sk, ss, cap)  # resident keys by the closed form, sorted
+    assert torch.equal(rk, k[ko])
     assert torch.equal(s, last(k))
     log(f"other calls: table full after {step} batches")
 
@@ -479,7 +485,7 @@ def test_other_calls_at_full_size():
     k2, _, s2, p2 = export_all(tab)
     check_invariants(tab, k2, p2, cap)
     assert torch.equal(s2, last(k2))
-    post = torch.sort(k2).values
+    post = cf.assert_table_matches(k2, p2, sk, ss, cap)
     union = torch.unique(torch.cat([pre, uk]))
     gone = union[~torch.isin(union, post)]
     out = torch.sort(ek[:m]).values
@@ -510,5 +516,6 @@ def test_other_calls_at_full_size():
     k3, v3, s3, p3 = export_all(tab, with_values=False)
     check_invariants(tab, k3, p3, cap)
     assert torch.equal(s3, last(k3))
+    cf.assert_table_matches(k3, p3, sk, ss, cap)
     log("other calls: find_or_insert exact")
     tab.close()
