@@ -16,6 +16,7 @@ from ._native import (  # noqa: F401
     EMPTY_KEY,
     HKV_FLAG_RW_LOCK,
     HKV_FLAG_SERIAL_INSERT,
+    HKV_FLAG_UNIQUE_KEYS,
     LOCKED_KEY,
     HkvError,
     hkv_assign,
@@ -35,7 +36,7 @@ from ._native import (  # noqa: F401
 )
 
 __all__ = ["HashTable", "HkvError", "BUCKET_SLOTS", "EMPTY_KEY", "LOCKED_KEY", "HKV_FLAG_SERIAL_INSERT",
-           "HKV_FLAG_RW_LOCK"]
+           "HKV_FLAG_RW_LOCK", "HKV_FLAG_UNIQUE_KEYS"]
 
 
 class HashTable:
@@ -45,18 +46,22 @@ class HashTable:
     dual_bucket: score-based dual-bucket mode; values_on_host: value rows in
     pinned host memory mapped into the GPU, except the first hbm_value_bytes'
     worth of buckets, which stay in HBM; serial_insert: apply inserts one key
-    at a time in input order (deterministic placement, slow); flags: further
-    HKV_FLAG_* bits (HKV_FLAG_RW_LOCK: reader/writer call ordering).
+    at a time in input order (deterministic placement, slow); unique_keys:
+    the caller guarantees distinct keys in every write batch
+    (HKV_FLAG_UNIQUE_KEYS); flags: further HKV_FLAG_* bits
+    (HKV_FLAG_RW_LOCK: reader/writer call ordering).
     """
 
     def __init__(self, capacity: int, dim: int, dual_bucket: bool = False, values_on_host: bool = False,
-                 device: int = 0, serial_insert: bool = False, hbm_value_bytes: int = 0, flags: int = 0):
+                 device: int = 0, serial_insert: bool = False, hbm_value_bytes: int = 0, flags: int = 0,
+                 unique_keys: bool = False):
         self.capacity = int(capacity)
         self.dim = int(dim)
         self.dual_bucket = bool(dual_bucket)
         self.values_on_host = bool(values_on_host)
         self.device = int(device)
-        flags = int(flags) | (HKV_FLAG_SERIAL_INSERT if serial_insert else 0)
+        flags = (int(flags) | (HKV_FLAG_SERIAL_INSERT if serial_insert else 0)
+                 | (HKV_FLAG_UNIQUE_KEYS if unique_keys else 0))
         self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags, hbm_value_bytes)
 
     def close(self) -> None:

@@ -27,6 +27,7 @@ HKV_EHIP = -3
 HKV_EUNSUPPORTED = -4
 HKV_FLAG_SERIAL_INSERT = 0x1
 HKV_FLAG_RW_LOCK = 0x2
+HKV_FLAG_UNIQUE_KEYS = 0x4
 BUCKET_SLOTS = 128
 EMPTY_KEY = 0xFFFFFFFFFFFFFFFF
 LOCKED_KEY = 0xFFFFFFFFFFFFFFFE

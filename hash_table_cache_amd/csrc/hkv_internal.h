@@ -22,6 +22,10 @@ struct TableView {
   uint32_t* head;     // [nb]  inserter chain heads; all 0xFFFFFFFF between calls
   uint64_t* bmin;     // [2*nb] dual mode: lowest (score, key) of each full bucket
                       // as its last owner left it; key ~0 = not known
+  uint32_t* claim;    // [nb*4] one bit per slot (bit p%32 of word p/32): taken by the
+                      // occurrence of a resident key that updates it in an inserter
+                      // call, so one occurrence alone writes the row and score;
+                      // all 0 between calls
   uint64_t nb;        // number of buckets
   uint64_t nb_mask;   // nb - 1 when nb is a power of two
   uint32_t dim;
@@ -29,6 +33,8 @@ struct TableView {
   uint32_t dual;      // dual-bucket mode
   uint32_t lanes;     // lanes per key of find/assign/insert probes; 0 = by dim
   uint32_t keys_per_group;  // keys each group of the key-side probes serves (1, 2 or 4)
+  uint32_t claims;    // inserters claim slots they update in place (0: the caller
+                      // promised distinct keys per write batch)
 };
 
 // Optional per-kernel timing: when a timer is passed, each kernel is launched

@@ -47,6 +47,8 @@ constexpr int kSlots = 128;
 constexpr uint64_t kLockedKey = ~0ull - 1;  // keys >= this are reserved
 constexpr uint32_t kNoIdx = 0xFFFFFFFFu;    // chain end / empty chain head
 constexpr uint32_t kSkipIdx = 0xFFFFFFFEu;  // key takes no part in the insert
+constexpr uint32_t kHitIdx = 0xFFFFFFFDu;   // resident key updated by this occurrence;
+                                            // target[i] = its bucket (claim to clear)
 constexpr uint32_t kFullBit = 0x80000000u;  // target word: the bucket was full at probe time
 constexpr uint64_t kSecondSalt = 0x9E3779B97F4A7C15ull;
 constexpr int kBlock = 256;
@@ -142,6 +144,47 @@ __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* _
   } else {
     for (uint32_t c = lane; c < dim; c += G) dst[c] = src[c];
   }
+}
+
+// A row of up to R*G 16-byte pieces held in the registers of the G lanes of a
+// group (R as in copy_row), so that its load can be issued before a decision
+// that its store waits for.
+template <int G>
+struct GroupRow {
+  static constexpr int R = G >= 16 ? 2 : 4;
+  f32x4 v[R];
+  __device__ static bool fits(uint32_t dim) { return (dim >> 2) <= static_cast<uint32_t>(R * G); }
+};
+
+template <int G>
+__device__ __forceinline__ void group_row_load(GroupRow<G>& r, const float* __restrict__ src, uint32_t dim,
+                                               int lane) {
+  const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+  const uint32_t n4 = dim >> 2;
+#pragma unroll
+  for (int u = 0; u < GroupRow<G>::R; ++u) {
+    const uint32_t c = lane + u * G;
+    if (c < n4) r.v[u] = __builtin_nontemporal_load(s4 + c);
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void group_row_store(const GroupRow<G>& r, float* __restrict__ dst, uint32_t dim,
+                                                int lane) {
+  f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+  const uint32_t n4 = dim >> 2;
+#pragma unroll
+  for (int u = 0; u < GroupRow<G>::R; ++u) {
+    const uint32_t c = lane + u * G;
+    if (c < n4) __builtin_nontemporal_store(r.v[u], d4 + c);
+  }
+}
+
+// Takes slot p's claim bit for this call; true for the first taker only.
+__device__ __forceinline__ bool claim_slot(const TableView& t, uint64_t p) {
+  const uint32_t bit = 1u << (p & 31);
+  const uint32_t old = __hip_atomic_fetch_or(t.claim + (p >> 5), bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (old & bit) == 0;
 }
 
 // Loads this lane's share (NW dwords) of a bucket's 128-byte digest line.
@@ -339,6 +382,43 @@ __device__ __forceinline__ void probe_many(const TableView& t, const uint64_t (&
     const uint64_t bits = group_bits<G>(__ballot(hj >= 0));
     hit[j] = bits == 0 ? -1 : __shfl(hj, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
   }
+}
+
+// probe() that also requests a row of the caller's (src, dim floats) into
+// registers as soon as the digest lines show the group a candidate slot, so
+// that its load overlaps the candidate-key loads (keys with no candidate are
+// misses and load nothing).
+template <int G, bool DUAL>
+__device__ __forceinline__ int64_t probe_prefetch(const TableView& t, uint64_t k, int lane, uint32_t* occ1,
+                                                  uint32_t* occ2, bool load_row, const float* src,
+                                                  GroupRow<G>& rr) {
+  constexpr int NW = kSlots / G / 4;
+  const uint64_t h = fmix64(k);
+  const uint32_t pat = digest_of(h) * 0x01010101u;
+  const uint32_t b1 = bucket_of(t, h);
+  uint32_t w1[NW];
+  load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
+  uint32_t b2 = b1;
+  uint32_t w2[NW];
+  if constexpr (DUAL) {
+    b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+    if (b2 != b1) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
+  }
+  const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
+  const uint32_t m1 = candidate_mask<NW>(w1, pat);
+  uint32_t m2 = 0;
+  if constexpr (DUAL) {
+    if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
+  }
+  Cand c;
+  cand_issue(c, t.keys, m1, static_cast<uint64_t>(b1) * kSlots + off, m2, static_cast<uint64_t>(b2) * kSlots + off);
+  if (load_row && group_bits<G>(__ballot(c.h0)) != 0) group_row_load<G>(rr, src, t.dim, lane);
+  const int64_t hit = cand_finish(c, t.keys, k);
+  *occ1 = line_occupancy<G, NW>(w1);
+  if constexpr (DUAL) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
+  const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
+  if (bits == 0) return -1;
+  return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
 }
 
 // ---------------------------------------------------------------- readers --
@@ -910,7 +990,16 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     return;
   }
   uint32_t o1 = 0, o2 = 0;
-  const int64_t p = probe<G, DUAL>(t, k, lane, &o1, &o2);
+  int64_t p;
+  // (insert_or_assign: the input row, needed by a hit, is requested together
+  // with the candidate keys, as soon as the digest lines show a candidate)
+  const bool in_regs = !FETCH && V4 && GroupRow<G>::fits(t.dim);
+  GroupRow<G> rr;
+  if constexpr (FETCH) {
+    p = probe<G, DUAL>(t, k, lane, &o1, &o2);
+  } else {
+    p = probe_prefetch<G, DUAL>(t, k, lane, &o1, &o2, in_regs, values + i * t.dim, rr);
+  }
   if (p >= 0) {
     if constexpr (FETCH) {
       // (host-resident rows: cacheable loads, as in find)
@@ -919,13 +1008,34 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
       } else {
         copy_row<G, V4, NT>(values + i * t.dim, row_of(t, static_cast<uint64_t>(p)), t.dim, lane);
       }
+      if (lane == 0) {
+        t.scores[p] = score;
+        next[i] = kSkipIdx;
+        if (found) found[i] = 1;
+      }
     } else {
-      copy_row<G, V4, NT>(row_of(t, static_cast<uint64_t>(p)), values + i * t.dim, t.dim, lane);
-    }
-    if (lane == 0) {
-      t.scores[p] = score;
-      next[i] = kSkipIdx;
-      if (FETCH && found) found[i] = 1;
+      // In-place update. Occurrences of one key in a batch would otherwise
+      // write its row piece by piece at once; the slot's claim bit lets the
+      // first one alone write the row and the score.
+      const float* src = values + i * t.dim;
+      float* dst = row_of(t, static_cast<uint64_t>(p));
+      uint32_t won = 1;
+      if (t.claims) {
+        if (lane == 0) won = claim_slot(t, static_cast<uint64_t>(p)) ? 1u : 0u;
+        won = __shfl(won, 0, G);
+      }
+      if (won) {
+        if (in_regs) {
+          group_row_store<G>(rr, dst, t.dim, lane);
+        } else {
+          copy_row<G, V4, NT>(dst, src, t.dim, lane);
+        }
+      }
+      if (lane == 0) {
+        if (won) t.scores[p] = score;
+        if (won && t.claims) target[i] = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
+        next[i] = won && t.claims ? kHitIdx : kSkipIdx;
+      }
     }
     return;
   }
@@ -957,6 +1067,11 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
   next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Resets the claim bits of bucket b's 128 slots (one 16-byte store).
+__device__ __forceinline__ void clear_claims(const TableView& t, uint32_t b) {
+  *reinterpret_cast<uint4*>(t.claim + 4 * static_cast<uint64_t>(b)) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // State of a bucket owned by a 16-lane group in the owner kernel: its
@@ -1141,7 +1256,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
                                                               const uint64_t* __restrict__ scores,
                                                               const uint32_t* __restrict__ next,
                                                               const uint32_t* __restrict__ target,
-                                                              EvictStage st) {
+                                                              EvictStage st, bool clear_all) {
   // The block's owners (keys with next == kNoIdx) are listed in LDS and dealt
   // out to its 16 groups in turn, so that every group serves about the same
   // number of buckets.
@@ -1154,12 +1269,25 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (threadIdx.x == 0) s_count = 0;
   __syncthreads();
-  if (mine < n && next[mine] == kNoIdx) {
-    const uint32_t e = atomicAdd(&s_count, 1u);
-    s_idx[e] = static_cast<uint32_t>(mine);
-    s_tgt[e] = target[mine];
-    s_key[e] = keys[mine];
-    s_score[e] = scores[mine];
+  if (mine < n) {
+    const uint32_t nx = next[mine];
+    if (nx == kNoIdx) {
+      const uint32_t e = atomicAdd(&s_count, 1u);
+      s_idx[e] = static_cast<uint32_t>(mine);
+      s_tgt[e] = target[mine];
+      s_key[e] = keys[mine];
+      s_score[e] = scores[mine];
+    } else if (nx == kHitIdx && !clear_all) {
+      clear_claims(t, target[mine]);
+    }
+  }
+  if (clear_all) {
+    // the claims of the probe kernel, cleared wholesale: this block's share of
+    // the buckets (chosen when that is cheaper than one store per update)
+    const uint64_t per = (t.nb + gridDim.x - 1) / gridDim.x;
+    const uint64_t b0 = static_cast<uint64_t>(blockIdx.x) * per;
+    const uint64_t b1 = b0 + per < t.nb ? b0 + per : t.nb;
+    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kBlock) clear_claims(t, static_cast<uint32_t>(b));
   }
   __syncthreads();
   const uint32_t owners = s_count;
@@ -1232,7 +1360,7 @@ constexpr int kChunk = 4 * kBlock;
 __device__ __forceinline__ bool departs(uint64_t i, uint64_t n, const uint32_t* next, const EvictStage& st,
                                         uint32_t* kd) {
   *kd = 0;
-  if (i < n && next[i] != kSkipIdx) *kd = st.kind[i];
+  if (i < n && next[i] != kSkipIdx && next[i] != kHitIdx) *kd = st.kind[i];
   return *kd != 0;
 }
 
@@ -1331,13 +1459,18 @@ __global__ __launch_bounds__(64) void upsert_serial_kernel(TableView t, uint64_t
                                                            const uint64_t* __restrict__ keys,
                                                            const float* __restrict__ values,
                                                            const uint64_t* __restrict__ scores,
-                                                           const uint32_t* __restrict__ skip, Evicted ev) {
+                                                           const uint32_t* __restrict__ skip,
+                                                           const uint32_t* __restrict__ skip_bucket, Evicted ev) {
   if (threadIdx.x >= kInsG) return;
   const int lane = static_cast<int>(threadIdx.x);
   for (uint64_t i = 0; i < n; ++i) {
+    if (skip && skip[i] != kNoIdx) {
+      // an update of the probe pass: its claim is released here
+      if (skip[i] == kHitIdx && lane == 0) clear_claims(t, skip_bucket[i]);
+      continue;
+    }
     const uint64_t k = keys[i];
     if (is_reserved(k)) continue;
-    if (skip && skip[i] != kNoIdx) continue;
     const float* row = values + i * t.dim;
     const uint64_t score = scores[i];
     const uint64_t h = fmix64(k);
@@ -1405,6 +1538,7 @@ __global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
     t.keys[p] = ~0ull;
     t.scores[p] = 0;
     t.digests[p] = 0;
+    if (p < t.nb * 4) t.claim[p] = 0;
     if (p < t.nb) {
       t.occ[p] = 0;
       t.head[p] = kNoIdx;
@@ -1479,13 +1613,17 @@ template <bool V4, bool DUAL>
 hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const uint32_t* next,
                    const uint32_t* target, hipStream_t s, KernelTimer* tm) {
   const EvictStage st{c.st_kind, c.st_keys, c.st_scores, c.st_rows};
+  // Claims of the probe kernel: cleared wholesale (16 bytes per bucket) when
+  // that costs less than one 16-byte store per update, else per update.
+  // (find_or_insert takes no claims.)
+  const bool clear_all = t.claims && !c.fetch && t.nb <= 4 * n;
   if (!c.ev_keys) {
     HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false>), dim3(grid_for(n)), dim3(kBlock), s,
-               t, n, c.keys, c.values, c.scores, next, target, st);
+               t, n, c.keys, c.values, c.scores, next, target, st, clear_all);
     return hipGetLastError();
   }
   HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true>), dim3(grid_for(n)), dim3(kBlock), s, t,
-             n, c.keys, c.values, c.scores, next, target, st);
+             n, c.keys, c.values, c.scores, next, target, st, clear_all);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const Evicted out{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
@@ -1551,7 +1689,7 @@ hipError_t upsert_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_
   if (serial) {
     const Evicted ev{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
     HKV_LAUNCH(tm, "upsert_serial", (upsert_serial_kernel<V4, DUAL>), dim3(1), dim3(64), s, t, n, c.keys,
-               c.values, c.scores, two_phase ? next : nullptr, ev);
+               c.values, c.scores, two_phase ? next : nullptr, two_phase ? target : nullptr, ev);
     return hipGetLastError();
   }
   return owner_l<V4, DUAL>(t, n, c, next, target, s, tm);

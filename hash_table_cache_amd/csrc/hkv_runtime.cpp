@@ -164,6 +164,7 @@ void free_storage(hkv_table* t) {
   if (v.occ) (void)hipFree(v.occ);
   if (v.head) (void)hipFree(v.head);
   if (v.bmin) (void)hipFree(v.bmin);
+  if (v.claim) (void)hipFree(v.claim);
   if (t->values_host) (void)hipHostFree(t->values_host);
   if (t->values_dev) (void)hipFree(t->values_dev);
   if (t->ws_next) (void)hipFree(t->ws_next);
@@ -288,15 +289,17 @@ hkv_status ensure_workspace(hkv_table* t, uint64_t n) {
   uint64_t cap = t->ws_cap ? t->ws_cap : 1024;
   while (cap < n) cap *= 2;
   if (cap > kMaxBatch) cap = kMaxBatch;
-  if (t->ws_next) (void)hipFree(t->ws_next);
-  if (t->ws_target) (void)hipFree(t->ws_target);
-  t->ws_next = t->ws_target = nullptr;
-  t->ws_cap = 0;
+  auto release = [t]() {
+    if (t->ws_next) (void)hipFree(t->ws_next);
+    if (t->ws_target) (void)hipFree(t->ws_target);
+    t->ws_next = t->ws_target = nullptr;
+    t->ws_cap = 0;
+  };
+  release();
   if (hipMalloc(&t->ws_next, cap * sizeof(uint32_t)) != hipSuccess ||
       hipMalloc(&t->ws_target, cap * sizeof(uint32_t)) != hipSuccess) {
     (void)hipGetLastError();
-    if (t->ws_next) (void)hipFree(t->ws_next);
-    t->ws_next = nullptr;
+    release();
     return fail(HKV_ENOMEM, "inserter workspace of %llu entries", static_cast<unsigned long long>(cap));
   }
   t->ws_cap = cap;
@@ -391,7 +394,8 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (o->bucket_slots != 0 && o->bucket_slots != kSlots)
     return fail(HKV_EINVAL, "bucket_slots %u: only 128-slot buckets exist", o->bucket_slots);
   if (o->dual_bucket > 1 || o->values_on_host > 1) return fail(HKV_EINVAL, "dual_bucket/values_on_host must be 0 or 1");
-  if (o->flags & ~(HKV_FLAG_SERIAL_INSERT | HKV_FLAG_RW_LOCK)) return fail(HKV_EINVAL, "unknown flags 0x%x", o->flags);
+  if (o->flags & ~(HKV_FLAG_SERIAL_INSERT | HKV_FLAG_RW_LOCK | HKV_FLAG_UNIQUE_KEYS))
+    return fail(HKV_EINVAL, "unknown flags 0x%x", o->flags);
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
   if (e != hipSuccess || ndev == 0) {
@@ -416,6 +420,7 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   v.nb_mask = v.pow2 ? nb - 1 : 0;
   v.dim = o->dim;
   v.dual = o->dual_bucket;
+  v.claims = (o->flags & HKV_FLAG_UNIQUE_KEYS) ? 0u : 1u;
   // Tuning overrides: lanes serving one key (4, 8 or 16; anything else keeps
   // the default chosen from dim) and keys per group of the key-side probes of
   // find* and contains (1, 2 or 4; default 2).
@@ -424,7 +429,8 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (const char* g = std::getenv("HKV_KEYS_PER_GROUP")) v.keys_per_group = static_cast<uint32_t>(std::atoi(g));
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
-            hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&t->size_dev, 8) == hipSuccess &&
+            hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&v.claim, nb * 16) == hipSuccess &&
+            hipMalloc(&t->size_dev, 8) == hipSuccess &&
             (!o->dual_bucket || hipMalloc(&v.bmin, nb * 16) == hipSuccess) &&
             hipHostMalloc(&t->size_host, 8, hipHostMallocDefault) == hipSuccess;
   // Value rows: the first `split` positions in HBM, the rest in pinned host

@@ -91,6 +91,14 @@ typedef int32_t hkv_status;
  * baseline of the paper's concurrency ablation, §5.4): readers may overlap
  * readers, every updater and inserter call is exclusive. */
 #define HKV_FLAG_RW_LOCK 0x2u
+/* The caller guarantees that the keys of every write batch (insert_or_assign,
+ * insert_and_evict) are distinct, as the paper's benchmarks and the DynamicEmb
+ * API's unique-key inputs have them. The inserter then takes no per-slot claim
+ * when it updates a resident key in place (one device atomic per update
+ * saved). A batch that breaks the promise still leaves every key resident at
+ * most once, but a duplicated resident key's row may combine 16-byte pieces
+ * of several occurrences. */
+#define HKV_FLAG_UNIQUE_KEYS 0x4u
 
 typedef struct hkv_options {
   uint64_t capacity;        /* slots; a positive multiple of 128 (§3.2). B = capacity / 128 buckets */
@@ -113,7 +121,9 @@ typedef struct hkv_options {
  * hkv_create - allocate an empty table (§3.2 layout, §4.2 placement).
  * Storage per slot: key 8 B + score 8 B + digest 1 B in HBM (§5.1, memory
  * overhead), plus a value row of 4*dim bytes in HBM or in pinned host memory
- * (split at a bucket boundary by hbm_value_bytes, see hkv_options).
+ * (split at a bucket boundary by hbm_value_bytes, see hkv_options). Per
+ * bucket, 24 bytes of bookkeeping in HBM (occupancy, inserter chain head, one
+ * claim bit per slot) and, in dual-bucket mode, 16 more (its lowest entry).
  * Every slot starts empty. The table owns all of its storage.
  * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128,
  * dim == 0, bucket_slots not 128, bad device), HKV_ENOMEM, HKV_EHIP.
@@ -157,9 +167,12 @@ hkv_status hkv_find(hkv_table* table, uint64_t n, const uint64_t* keys, float* v
  * incoming key ranks higher, and the key is rejected otherwise. Rank is the
  * pair (score, key) ordered lexicographically, which fixes ties. None of these
  * outcomes is an error.
- * Keys within one batch must be distinct for a deterministic result; with
- * duplicates, which occurrence ends up stored is unspecified (the table stays
- * consistent). For single-bucket tables and batches of distinct keys whose
+ * Keys within one batch must be distinct for a deterministic result. With
+ * duplicates, the key ends up stored (or not) as if exactly one of its
+ * occurrences had been applied, whole: its row and score come from that one
+ * occurrence, which one is unspecified, and the key is resident at most once
+ * (unless the table was created with HKV_FLAG_UNIQUE_KEYS, see there).
+ * For single-bucket tables and batches of distinct keys whose
  * scores never decrease over time, the resulting bucket contents equal those
  * of applying the batch one key at a time, whatever the in-batch order.
  *   keys   [n] uint64, input
@@ -176,6 +189,11 @@ hkv_status hkv_insert_or_assign(hkv_table* table, uint64_t n, const uint64_t* ke
  * NULL) and the score (when scores is not NULL) of keys already resident.
  * Absent and reserved keys are ignored; the bucket structure never changes.
  * values and scores may not both be NULL (HKV_EINVAL).
+ * Keys within one batch should be distinct. Every occurrence of a duplicated
+ * key writes in place, as concurrent updater calls on different streams do
+ * (§3.5 lets updaters overlap and takes no lock for them): its score is one
+ * occurrence's, and with dim > 4 its row may combine 16-byte pieces of
+ * several occurrences.
  *   keys   [n] uint64, input
  *   values [n*dim] float32, input, nullable
  *   scores [n] uint64, input, nullable

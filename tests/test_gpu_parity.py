@@ -130,13 +130,13 @@ def test_tiny_single_bucket_workload_exact():
     assert found.sum() == 8192
 
 
-@pytest.mark.parametrize("lam", [0.5, 0.75, 0.9, 1.0])
-def test_lambda_sweep_reduced_exact(lam):
+@pytest.mark.parametrize("lam,unique_keys", [(0.5, False), (0.75, False), (0.9, False), (1.0, False), (1.0, True)])
+def test_lambda_sweep_reduced_exact(lam, unique_keys):
     """Load-factor sweep at reduced capacity (2^20 slots, dim 32, batches of
     2^16 distinct uniform keys, score = batch index), then find with 90 % hits."""
     H = hkv()
     C, D, nb = 1 << 20, 32, 1 << 16
-    tab = H.HashTable(C, D)
+    tab = H.HashTable(C, D, unique_keys=unique_keys)
     o = oracle.OracleTable(C, D)
     target = int(round(lam * C))
     step, start = 0, 0
@@ -218,13 +218,15 @@ def test_single_new_key_per_full_bucket_exact(resident_scores):
     check_find(tab, o, mixed_queries(o, 4096, 0.5, seed, 9))
 
 
-def test_mixed_find_assign_upsert_reduced_exact():
+@pytest.mark.parametrize("unique_keys", [False, True])
+def test_mixed_find_assign_upsert_reduced_exact(unique_keys):
     """Reader / updater / inserter steps at lambda = 1 (2^17 slots, dim 64):
     per step a find, an assign of resident keys, an upsert of half fresh and
-    half resident keys; exact after every step."""
+    half resident keys; exact after every step. Also on a table created with
+    the distinct-keys promise (no per-slot claims on in-place updates)."""
     H = hkv()
     C, D = 1 << 17, 64
-    tab = H.HashTable(C, D)
+    tab = H.HashTable(C, D, unique_keys=unique_keys)
     o = oracle.OracleTable(C, D)
     step, start = 0, 0
     while o.size() < C:
@@ -606,14 +608,16 @@ def test_dual_bucket_invariants_and_retention():
     assert all(freq[x] == s for x, s in zip(qn[f].tolist(), np_u64(scs)[f].tolist()))
 
 
-@pytest.mark.parametrize("dual", [False, True])
-def test_duplicate_keys_in_a_batch_keep_the_table_consistent(dual):
+@pytest.mark.parametrize("dual,unique_keys", [(False, False), (True, False), (False, True)])
+def test_duplicate_keys_in_a_batch_keep_the_table_consistent(dual, unique_keys):
     """Duplicates within one write batch: which occurrence wins is unspecified,
     but no key may become resident twice and every stored row must be one of
-    the rows written for that key (full buckets, so evictions happen too)."""
+    the rows written for that key (full buckets, so evictions happen too).
+    The key-level part holds even on a table whose caller promised distinct
+    keys and broke the promise."""
     H = hkv()
     C, D = 32 * SLOTS, 4
-    tab = H.HashTable(C, D, dual_bucket=dual)
+    tab = H.HashTable(C, D, dual_bucket=dual, unique_keys=unique_keys)
     rng = np.random.default_rng(17)
     pool = rng.integers(1, 1 << 62, size=3 * C, dtype=np.int64)
     written = {}
@@ -640,3 +644,45 @@ def test_duplicate_keys_in_a_batch_keep_the_table_consistent(dual):
             cand = gen.values(torch.full((vers.numel(),), int(np.uint64(key).view(np.int64)), dtype=torch.int64),
                               vers, D).numpy()
             assert any(np.array_equal(cand[r].view(np.uint32), gvn[j].view(np.uint32)) for r in range(len(vers)))
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_duplicate_keys_store_one_occurrence_whole(dual):
+    """Each key of a write batch occurring many times, dim 64 (16 lanes'
+    worth of 16-byte pieces per row), every occurrence with its own row and
+    score: afterwards each key is resident once and its stored (row, score)
+    is exactly one occurrence's pair, whole, for resident keys updated in
+    place and for new keys alike. Checked on every touched key."""
+    H = hkv()
+    C, D = 1 << 15, 64
+    tab = H.HashTable(C, D, dual_bucket=dual)
+    rng = np.random.default_rng(23)
+    # half full: no key leaves, so every touched key stays resident
+    base = gen.unique_keys(23, 1, 0, C // 2, device=dev())
+    tab.insert_or_assign(base, gen.values(base, 1, D), torch.ones(base.numel(), dtype=torch.int64, device=dev()))
+    fresh_pool = gen.unique_keys(23, 2, 0, 4096, device=dev())
+    for step in range(2, 6):
+        res = base[torch.from_numpy(rng.choice(base.numel(), size=2048, replace=False)).to(dev())]
+        new = fresh_pool[(step - 2) * 256:(step - 1) * 256]
+        k = torch.cat([res.repeat(8), new.repeat(8)])
+        k = k[torch.from_numpy(rng.permutation(k.numel())).to(dev())]
+        ver = torch.arange(k.numel(), dtype=torch.int64, device=dev()) + step * 1_000_000
+        tab.insert_or_assign(k, gen.values(k, ver, D), ver)
+        gk, gv, gs, gp = tab.export_batch()
+        assert torch.unique(gk).numel() == gk.numel()
+        assert tab.size() == gk.numel() == base.numel() + (step - 1) * 256
+        touched = torch.unique(k)
+        pos = torch.searchsorted(torch.sort(gk).values, touched)
+        order = torch.argsort(gk)
+        sk, sv, ss = gk[order], gv[order], gs[order]
+        assert torch.equal(sk[pos], touched), "a touched key is not resident"
+        s = ss[pos]
+        # the stored score is one of this key's occurrences' (versions are
+        # distinct and ascending, one per occurrence) ...
+        idx = torch.clamp(torch.searchsorted(ver, s), max=ver.numel() - 1)
+        assert torch.equal(ver[idx], s)
+        assert torch.equal(k[idx], touched), "stored score belongs to another key's occurrence"
+        # ... and the stored row is that same occurrence's row, whole
+        assert torch.equal(sv[pos].view(torch.int32), gen.values(touched, s, D).view(torch.int32)), \
+            "a stored row mixes occurrences"
+    tab.close()
