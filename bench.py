@@ -73,7 +73,11 @@ def parse_args():
                    help="where the resident keys of the find and upsert batches come from: sampled uniformly "
                         "from the whole resident set (default), or from the 2*batch most recently inserted keys "
                         "(a recency-skewed mix whose key lines partly stay in the Infinity Cache)")
+    p.add_argument("--unique-keys", action="store_true",
+                   help="create the tables with HKV_FLAG_UNIQUE_KEYS (every write batch is distinct by construction)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-steps", type=int, default=6,
+                   help="timed steps of the first table that the CPU oracle baseline replays")
     p.add_argument("--insert-steps", type=int, default=5,
                    help="extra all-new-key insert batches on the full table, reported in detail")
     p.add_argument("--find-only", action="store_true", help="time find batches only")
@@ -914,6 +918,7 @@ def fill_table(tab, lam, cap, batch, dim, seed, stream_id, device):
 
 
 def run_gpu(args):
+    import numpy as np
     import torch
 
     import hash_table_cache_amd as H
@@ -928,9 +933,10 @@ def run_gpu(args):
     # with kernel timing on (per-kernel times, roofline, per-lambda rates)
     total_steps = args.warmup + 2 * args.steps
     tables = []
+    cpu_sample = None
     for li, lam in enumerate(lams):
         t0 = time.perf_counter()
-        tab = H.HashTable(cap, dim, device=0)
+        tab = H.HashTable(cap, dim, device=0, unique_keys=args.unique_keys)
         cursor, step, size = fill_table(tab, lam, cap, batch, dim, SEED, 1 + li, dev)
         torch.cuda.synchronize()
         log(f"lambda={lam}: filled to size {size} ({size / cap:.4f}) with {cursor} keys "
@@ -961,6 +967,13 @@ def run_gpu(args):
             sc = torch.full((batch,), step + s, dtype=torch.int64, device=dev)
             finds.append(fk)
             ups.append((uk, sc))
+        if li == 0 and not args.no_cpu_baseline and not args.find_only:
+            # the batches the CPU oracle replays: the warm-up steps and the
+            # first timed steps of this table, copied to the host
+            cpu_steps = args.warmup + min(args.steps, args.cpu_steps)
+            cpu_sample = dict(lam=lam, li=li, warmup=args.warmup, batches=[
+                (finds[s].cpu().numpy().view(np.uint64), ups[s][0].cpu().numpy().view(np.uint64),
+                 ups[s][1].cpu().numpy().view(np.uint64)) for s in range(cpu_steps)])
         out = torch.empty((batch, dim), dtype=torch.float32, device=dev)
         found = [torch.empty(batch, dtype=torch.uint8, device=dev) for _ in range(total_steps)]
         tables.append(dict(lam=lam, tab=tab, finds=finds, ups=ups, vals=vals_pool, out=out, found=found,
@@ -1095,7 +1108,7 @@ def run_gpu(args):
     return dict(wall=wall, total_keys=total_keys, detail=detail, find_var=find_var, kernels=kernels,
                 dominant=dominant, h=h_avg, gpu_busy_frac=busy / (wall_timed_kernels * 1e3),
                 wall_timed_kernels=wall_timed_kernels, insert_new=insert_new, extra_ops=extra_ops,
-                step_bytes=step_bytes)
+                step_bytes=step_bytes, cpu_sample=cpu_sample)
 
 
 def run_extra_ops(args, tables, batch, dim, hit):
@@ -1224,55 +1237,71 @@ def run_extra_ops(args, tables, batch, dim, hit):
     return out
 
 
-def run_cpu_baseline(args):
-    """The CPU oracle, single-threaded, on a bounded sample of the same workload."""
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def run_cpu_baseline(args, sample):
+    """The CPU oracle, single-threaded and pinned to one core, on the
+    benchmark's own batches: the oracle builds the first load factor's table
+    at the benchmark's capacity from the same fill batches (rows kept as
+    8-byte version tags, the oracle's tag mode), replays the warm-up steps
+    untimed, then applies the first timed steps' find and insert_or_assign
+    batches (copied from the GPU run), each timed on its own. value = median
+    over those steps of (keys of the step's two batches) / (their time)."""
     import numpy as np
 
     import hkv_inputs as gen
     import oracle
 
-    cap = 1 << 22
-    batch = 1 << 18
-    rounds = 16
-    dim = args.dim
-    lams = [float(x) for x in args.lambdas.split(",")]
-    zeros = np.zeros((batch, dim), np.float32)
-    ops = 0
-    secs = 0.0
-    t_all = time.perf_counter()
-    for li, lam in enumerate(lams):
-        o = oracle.OracleTable(cap, dim)
+    cap = 1 << args.capacity_log2
+    batch = 1 << args.batch_log2
+    lam, li = sample["lam"], sample["li"]
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    try:
+        t_all = time.perf_counter()
+        o = oracle.OracleTable(cap, args.dim, tag_mode=True)
         target = int(round(lam * cap))
-        cursor, step = 0, 1
-        while o.size() < target:
-            n = batch if lam >= 1.0 else min(batch, target - o.size())
+        cursor, step, size = 0, 1, 0
+        while size < target:  # the same fill batches as fill_table()
+            n = batch if lam >= 1.0 else min(batch, target - size)
             k = gen.unique_keys(SEED, 1 + li, cursor, n).numpy().view(np.uint64)
-            o.insert_or_assign(k, np.full(n, step, np.uint64), values=zeros[:n])
+            tags = np.full(n, step, np.uint64)
+            o.insert_or_assign(k, tags, tags=tags)
             cursor += n
             step += 1
-        if args.hit_pool == "resident":
-            pool = o.export()["keys"]
-        else:
-            pool = gen.unique_keys(SEED, 1 + li, cursor - batch, batch).numpy().view(np.uint64)
-        n_hit = int(round(batch * args.hit_frac))
-        n_new = int(round(batch * args.new_frac))
-        # one random order of the pool; round r takes consecutive windows of
-        # it (distinct keys within a window)
-        order = pool[np.random.default_rng(SEED + li).permutation(pool.size)]
-        for r in range(rounds):
-            w = np.arange(r * (2 * batch), r * (2 * batch) + 2 * batch) % order.size
-            fk = np.concatenate([order[w[:min(n_hit, order.size)]],
-                                 gen.unique_keys(SEED, 40 + li, r * batch, batch - n_hit).numpy().view(np.uint64)])
-            uk = np.concatenate([order[w[batch:batch + min(batch - n_new, order.size)]],
-                                 gen.unique_keys(SEED, 60 + li, r * batch, n_new).numpy().view(np.uint64)])
+            size = o.size()
+        t_fill = time.perf_counter() - t_all
+        find_s, up_s = [], []
+        for s, (fk, uk, sc) in enumerate(sample["batches"]):
             t0 = time.perf_counter()
             o.find(fk)
-            o.insert_or_assign(uk, np.full(uk.size, step + r, np.uint64), values=zeros[:uk.size])
-            secs += time.perf_counter() - t0
-            ops += 2 * batch
+            t1 = time.perf_counter()
+            o.insert_or_assign(uk, sc, tags=sc)
+            t2 = time.perf_counter()
+            if s >= sample["warmup"]:
+                find_s.append(t1 - t0)
+                up_s.append(t2 - t1)
         o.close()
-    return dict(value=ops / secs / 1e9, secs=secs, total=time.perf_counter() - t_all, cap=cap, batch=batch,
-                rounds=rounds)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    per_step = [2 * batch / (a + b) / 1e9 for a, b in zip(find_s, up_s)]
+    return dict(value=statistics.median(per_step), secs=sum(find_s) + sum(up_s), total=time.perf_counter() - t_all,
+                fill_s=t_fill, steps=len(per_step), lam=lam, cap=cap, batch=batch, core=core,
+                find_bkvs=statistics.median(batch / t / 1e9 for t in find_s),
+                upsert_bkvs=statistics.median(batch / t / 1e9 for t in up_s),
+                cpu_model=cpu_model(), nproc=os.cpu_count(), allowed=len(allowed))
 
 
 def cold_runs(args):
@@ -1348,10 +1377,11 @@ def main():
     g["pattern"] = (pattern_ceiling(args.dim) if args.dim in (32, 64, 128) and args.capacity_log2 == 26
                     else None)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and g.get("cpu_sample"):
         log("running the CPU oracle baseline")
-        cpu = run_cpu_baseline(args)
-        log(f"cpu baseline: {cpu['value'] * 1e3:.3f} M-KV/s over {cpu['secs']:.1f}s timed, {cpu['total']:.1f}s total")
+        cpu = run_cpu_baseline(args, g["cpu_sample"])
+        log(f"cpu baseline: {cpu['value'] * 1e3:.3f} M-KV/s over {cpu['secs']:.1f}s timed, {cpu['total']:.1f}s total "
+            f"({cpu['fill_s']:.1f}s to fill)")
     value = g["total_keys"] / g["wall"] / 1e9
     n_lams = len(args.lambdas.split(","))
     line = {
@@ -1401,9 +1431,17 @@ def main():
             "unit": "B-KV/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": (f"single-threaded oracle, capacity 2^22 dim {args.dim} tables at lambda {args.lambdas}, "
-                       f"{cpu['rounds']} rounds of one 2^18-key find (same hit mix) + one 2^18-key insert_or_assign "
-                       f"(same resident/new mix) per lambda; {cpu['secs']:.1f}s timed of {cpu['total']:.1f}s"),
+            "sample": (f"the oracle single-threaded, pinned to core {cpu['core']} of {cpu['allowed']} "
+                       f"({cpu['cpu_model']}, nproc {cpu['nproc']}), on the benchmark's own lambda {cpu['lam']} "
+                       f"table: capacity 2^{args.capacity_log2}, rows as 8-byte version tags, filled from the same "
+                       f"batches ({cpu['fill_s']:.0f}s), the {args.warmup} warm-up steps replayed, then the first "
+                       f"{cpu['steps']} timed steps' 2^{args.batch_log2}-key find and insert_or_assign batches "
+                       f"copied from the GPU run, median over steps; {cpu['secs']:.1f}s timed"),
+            "cpu_model": cpu["cpu_model"],
+            "nproc": cpu["nproc"],
+            "capacity": cpu["cap"],
+            "find_bkvs_median": round(cpu["find_bkvs"], 6),
+            "upsert_bkvs_median": round(cpu["upsert_bkvs"], 6),
         },
         "detail": {
             "kernels": g["kernels"],

@@ -104,7 +104,11 @@ def test_json_line_carries_the_contract_fields(monkeypatch, capsys):
     monkeypatch.setattr(bench, "run_gpu", lambda args: dict(g))
     monkeypatch.setattr(bench, "copy_bandwidth", lambda: 5000.0)
     monkeypatch.setattr(bench, "pattern_ceiling", lambda dim: None)
-    monkeypatch.setattr(bench, "run_cpu_baseline", lambda args: dict(value=0.004, secs=8.0, total=14.0, rounds=16))
+    g["cpu_sample"] = dict(lam=0.5, li=0, warmup=3, batches=[])
+    monkeypatch.setattr(bench, "run_cpu_baseline",
+                        lambda args, sample: dict(value=0.004, secs=8.0, total=14.0, fill_s=20.0, steps=6, lam=0.5,
+                                                  cap=1 << 26, batch=1 << 20, core=7, find_bkvs=0.005,
+                                                  upsert_bkvs=0.0015, cpu_model="x", nproc=8, allowed=8))
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     bench.main()
     lines = [l for l in capsys.readouterr().out.splitlines() if l.strip()]
