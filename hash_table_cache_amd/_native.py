@@ -28,6 +28,7 @@ HKV_EUNSUPPORTED = -4
 HKV_FLAG_SERIAL_INSERT = 0x1
 HKV_FLAG_RW_LOCK = 0x2
 HKV_FLAG_UNIQUE_KEYS = 0x4
+NOALLOC_MAX_KEYS = 1 << 21
 BUCKET_SLOTS = 128
 EMPTY_KEY = 0xFFFFFFFFFFFFFFFF
 LOCKED_KEY = 0xFFFFFFFFFFFFFFFE
@@ -41,6 +42,7 @@ EXPORTS = (
     "hkv_find_ptr",
     "hkv_contains",
     "hkv_insert_or_assign",
+    "hkv_insert_or_assign_noalloc",
     "hkv_insert_and_evict",
     "hkv_find_or_insert",
     "hkv_assign",
@@ -103,6 +105,8 @@ def _load() -> ctypes.CDLL:
     L.hkv_contains.restype = st
     L.hkv_insert_or_assign.argtypes = [vp, u64, vp, vp, vp, vp]
     L.hkv_insert_or_assign.restype = st
+    L.hkv_insert_or_assign_noalloc.argtypes = [vp, u64, vp, vp, vp, vp]
+    L.hkv_insert_or_assign_noalloc.restype = st
     L.hkv_insert_and_evict.argtypes = [vp, u64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.hkv_insert_and_evict.restype = st
     L.hkv_find_or_insert.argtypes = [vp, u64, vp, vp, vp, vp, vp]
@@ -244,6 +248,16 @@ def hkv_find_or_insert(table, keys, values, scores, found_out=None, stream=None,
 def hkv_insert_or_assign(table, keys, values, scores, stream=None, *, dim, device):
     n = keys.numel()
     _check(load().hkv_insert_or_assign(
+        table, n,
+        _ptr(keys, _U64_DTYPES, n, "keys"),
+        _ptr(values, (torch.float32,), n * dim, "values"),
+        _ptr(scores, _U64_DTYPES, n, "scores"),
+        _stream(stream, device)))
+
+
+def hkv_insert_or_assign_noalloc(table, keys, values, scores, stream=None, *, dim, device):
+    n = keys.numel()
+    _check(load().hkv_insert_or_assign_noalloc(
         table, n,
         _ptr(keys, _U64_DTYPES, n, "keys"),
         _ptr(values, (torch.float32,), n * dim, "values"),

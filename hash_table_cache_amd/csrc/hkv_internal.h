@@ -54,6 +54,12 @@ struct KernelTimer {
 
 hipError_t launch_init(const TableView& t, hipStream_t s);
 
+// Device address, on the current device, of the library's fixed scratch array
+// for calls that may not allocate, and its capacity in keys (the array holds
+// 2 u32 words per key: next, then target).
+hipError_t scratch_address(uint32_t** out);
+uint64_t noalloc_max_keys();
+
 hipError_t launch_find(const TableView& t, uint64_t n, const uint64_t* keys, float* values_out,
                        uint8_t* found_out, uint64_t* scores_out, bool vec4, hipStream_t s,
                        KernelTimer* timer);

@@ -1715,7 +1715,21 @@ hipError_t locate_g(const TableView& t, uint64_t n, const uint64_t* keys, uint64
   return hipGetLastError();
 }
 
+// Scratch of hkv_insert_or_assign_noalloc: the inserter's per-key chain and
+// target words (next[0..max), target[max..2*max)) for calls that may not
+// allocate. Each GPU the library runs on holds its own copy until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (scratch_address below).
+constexpr uint64_t kNoallocMaxKeys = 1ull << 21;
+__device__ __align__(256) uint32_t scratch[2 * kNoallocMaxKeys];
+
 }  // namespace
+
+hipError_t scratch_address(uint32_t** out) {
+  return hipGetSymbolAddress(reinterpret_cast<void**>(out), HIP_SYMBOL(scratch));
+}
+
+uint64_t noalloc_max_keys() { return kNoallocMaxKeys; }
 
 hipError_t launch_init(const TableView& t, hipStream_t s) {
   const uint64_t cap = t.nb * kSlots;

@@ -130,6 +130,7 @@ class Profiler final : public hkv::KernelTimer {
 
 struct hkv_table {
   hkv_options opt{};
+  uint32_t* scratch = nullptr;  // the device's fixed no-alloc scratch (not owned)
   hkv::TableView view{};
   void* values_host = nullptr;  // hipHostMalloc base of the host-resident rows
   float* values_dev = nullptr;  // hipMalloc base of the HBM-resident rows
@@ -339,19 +340,67 @@ hkv_status ensure_evict_stage(hkv_table* t, uint64_t n) {
   return HKV_OK;
 }
 
+// Address of the fixed no-alloc scratch array on each device, looked up once
+// per device (with that device current) and kept for the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch[kMaxDevices] = {};
+
+hkv_status device_scratch(int device, uint32_t** out) {
+  if (device < 0 || device >= kMaxDevices) return fail(HKV_EUNSUPPORTED, "device %d beyond %d", device, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[device]) {
+    uint32_t* p = nullptr;
+    const hipError_t e = hkv::scratch_address(&p);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    }
+    g_scratch[device] = p;
+  }
+  *out = g_scratch[device];
+  return HKV_OK;
+}
+
+// True when a call on stream s would have to create an ordering event (the
+// table is, or by this call becomes, used from several streams, and s has no
+// inserter event yet). Caller holds t->mu.
+bool would_create_event(const hkv_table* t, hipStream_t s) {
+  const bool multi = t->multi_stream || (t->any_call && s != t->first_stream);
+  if (!multi) return false;
+  for (const auto& r : t->last[kInserter])
+    if (r.stream == s) return false;
+  return true;
+}
+
 }  // namespace
 
 // Shared tail of the inserter calls (arguments already validated): workspace,
-// ordering after incompatible groups, launch, completion event.
+// ordering after incompatible groups, launch, completion event. `fixed`: the
+// no-alloc variant: the chain and target words come from the device's fixed
+// scratch array and nothing is allocated.
 static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool vec4, const char* what,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool fixed = false) {
   const bool serial = (t->opt.flags & HKV_FLAG_SERIAL_INSERT) != 0;
   const bool needs_ws = !serial || c.fetch || c.ev_keys;
   std::lock_guard<std::mutex> lk(t->mu);
   DeviceGuard dg(t->opt.device);
   if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
   hkv_status st;
-  if (needs_ws && (st = ensure_workspace(t, n)) != HKV_OK) return st;
+  uint32_t* ws_next = t->ws_next;
+  uint32_t* ws_target = t->ws_target;
+  if (fixed) {
+    if (would_create_event(t, stream))
+      return fail(HKV_EINVAL, "%s: the table is used from several streams and this stream has no inserter event "
+                  "yet; issue one hkv_insert_or_assign on it first", what);
+    ws_next = t->scratch;
+    ws_target = t->scratch + hkv::noalloc_max_keys();
+  } else if (needs_ws && (st = ensure_workspace(t, n)) != HKV_OK) {
+    return st;
+  } else {
+    ws_next = t->ws_next;
+    ws_target = t->ws_target;
+  }
   if (c.ev_keys && !serial && n > 0) {
     if ((st = ensure_evict_stage(t, n)) != HKV_OK) return st;
     c.st_kind = t->ev_kind;
@@ -361,7 +410,7 @@ static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool
     c.chunk_count = t->ev_chunks;
   }
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
-  const hipError_t e = hkv::launch_upsert(t->view, n, c, t->ws_next, t->ws_target, vec4, serial, stream, t->timer());
+  const hipError_t e = hkv::launch_upsert(t->view, n, c, ws_next, ws_target, vec4, serial, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, what);
   return record_after(t, kInserter, stream);
 }
@@ -480,6 +529,12 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
     delete t;
     return fail_hip(e, "table initialisation");
   }
+  const hkv_status sst = device_scratch(o->device, &t->scratch);
+  if (sst != HKV_OK) {
+    free_storage(t);
+    delete t;
+    return sst;
+  }
   *out = t;
   return HKV_OK;
 }
@@ -565,6 +620,27 @@ HKV_API hkv_status hkv_insert_or_assign(hkv_table* t, uint64_t n, const uint64_t
   c.values = const_cast<float*>(values);  // read only: fetch and eviction output are off
   c.scores = scores;
   return run_inserter(t, n, c, vec4, "insert_or_assign", stream);
+}
+
+HKV_API hkv_status hkv_insert_or_assign_noalloc(hkv_table* t, uint64_t n, const uint64_t* keys,
+                                                const float* values, const uint64_t* scores,
+                                                hipStream_t stream) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (n == 0) return HKV_OK;
+  if (n > hkv::noalloc_max_keys())
+    return fail(HKV_EINVAL, "insert_or_assign_noalloc: batch of %llu keys exceeds its limit of %llu",
+                static_cast<unsigned long long>(n), static_cast<unsigned long long>(hkv::noalloc_max_keys()));
+  const uint64_t dim = t->opt.dim;
+  hkv_status st;
+  if ((st = check_buffer(t, keys, n * 8, "keys")) != HKV_OK) return st;
+  if ((st = check_buffer(t, values, n * dim * 4, "values")) != HKV_OK) return st;
+  if ((st = check_buffer(t, scores, n * 8, "scores")) != HKV_OK) return st;
+  const bool vec4 = dim % 4 == 0 && aligned16(values);
+  hkv::InsertCall c{};
+  c.keys = keys;
+  c.values = const_cast<float*>(values);  // read only
+  c.scores = scores;
+  return run_inserter(t, n, c, vec4, "insert_or_assign_noalloc", stream, true);
 }
 
 HKV_API hkv_status hkv_insert_and_evict(hkv_table* t, uint64_t n, const uint64_t* keys, const float* values,

@@ -185,6 +185,25 @@ hkv_status hkv_insert_or_assign(hkv_table* table, uint64_t n, const uint64_t* ke
                                 hipStream_t stream);
 
 /*
+ * hkv_insert_or_assign_noalloc - hkv_insert_or_assign for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, result and ordering as
+ * hkv_insert_or_assign, but the per-key scratch of its kernels (8 bytes per
+ * key) is a fixed array that the library holds in each GPU's memory for the
+ * life of the process (HKV_NOALLOC_MAX_KEYS keys, 16 MiB), instead of the
+ * table-owned workspace that hkv_insert_or_assign grows with hipMalloc; the
+ * call allocates nothing.
+ * Limits: n > HKV_NOALLOC_MAX_KEYS is HKV_EINVAL. Every no-alloc call on one
+ * GPU, from any table, uses that GPU's one array: calls that overlap on a
+ * GPU (different streams without ordering between them) race, so order them.
+ * On a table used from several streams, the stream must already have issued
+ * an inserter call (which creates its ordering event), else HKV_EINVAL.
+ */
+#define HKV_NOALLOC_MAX_KEYS (1ull << 21)
+hkv_status hkv_insert_or_assign_noalloc(hkv_table* table, uint64_t n, const uint64_t* keys,
+                                        const float* values, const uint64_t* scores, hipStream_t stream);
+
+/*
  * hkv_assign - updater (§3.5): overwrites the value row (when values is not
  * NULL) and the score (when scores is not NULL) of keys already resident.
  * Absent and reserved keys are ignored; the bucket structure never changes.

@@ -22,7 +22,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted([
         "hkv_create", "hkv_destroy", "hkv_get_options", "hkv_find", "hkv_find_ptr", "hkv_contains",
-        "hkv_insert_or_assign", "hkv_insert_and_evict", "hkv_find_or_insert", "hkv_assign", "hkv_size",
+        "hkv_insert_or_assign", "hkv_insert_or_assign_noalloc", "hkv_insert_and_evict", "hkv_find_or_insert", "hkv_assign", "hkv_size",
         "hkv_export_batch", "hkv_profile_start", "hkv_profile_stop", "hkv_last_error"])
 
 
@@ -93,6 +93,7 @@ def test_null_arguments():
     assert L.hkv_create(None, None) == _native.HKV_EINVAL
     assert L.hkv_find(None, 1, None, None, None, None, None) == _native.HKV_EINVAL
     assert L.hkv_insert_or_assign(None, 1, None, None, None, None) == _native.HKV_EINVAL
+    assert L.hkv_insert_or_assign_noalloc(None, 1, None, None, None, None) == _native.HKV_EINVAL
     assert L.hkv_assign(None, 1, None, None, None, None) == _native.HKV_EINVAL
     assert L.hkv_export_batch(None, 0, 1, None, None, None, None, None, None) == _native.HKV_EINVAL
     assert L.hkv_find_ptr(None, 1, None, None, None, None, None) == _native.HKV_EINVAL
