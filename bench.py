@@ -557,7 +557,8 @@ def online_run(args) -> None:
     (key = id), 2^20 draws per batch deduplicated, score = the key's
     cumulative frequency (LFU), until it is full, then 200 more batches.
     Before each batch's insert_or_assign, contains() looks up the batch's raw
-    draws: the cache hit ratio. find (rows copied out) is timed on a batch of
+    draws (the cache hit ratio) and its distinct keys (the fraction the upsert
+    updates in place). find (rows copied out) is timed on a batch of
     raw draws once the table is half full and again at the end. Reported per
     mode: batches to fill,
     load factor at the first eviction (first batch that adds fewer keys than
@@ -603,6 +604,8 @@ def online_run(args) -> None:
                 first_evict = size / cap
             size = new_size
             b += 1
+            if b % 200 == 0:
+                log(f"online {mode}: {b} batches, lambda {size / cap:.4f}")
             if find_half is None and size >= cap // 2:
                 find_half = (size / cap, find_ms(zipf.draw(seed, 1, b * draws, draws, device=dev)))
             if b > 4000:
@@ -617,7 +620,9 @@ def online_run(args) -> None:
             sc = freq[uniq]
             batches.append((r, uniq, gen.values(uniq, sc, dim, seed), sc))
         found = torch.empty(draws, dtype=torch.uint8, device=dev)
+        found_u = torch.empty(draws, dtype=torch.uint8, device=dev)
         hits = torch.zeros(1, dtype=torch.int64, device=dev)
+        resident_u = torch.zeros(1, dtype=torch.int64, device=dev)
         torch.cuda.synchronize()
         log(f"online {mode}: full after {fill_batches} batches ({time.perf_counter() - t0:.1f}s), first eviction "
             f"at lambda {first_evict}")
@@ -627,6 +632,10 @@ def online_run(args) -> None:
         for r, uniq, v, sc in batches:
             tab.contains(r, found_out=found)
             hits += found.sum()
+            # the batch's distinct keys already resident (the upsert's update
+            # fraction, for its algorithmic bytes)
+            tab.contains(uniq, found_out=found_u[:uniq.numel()])
+            resident_u += found_u[:uniq.numel()].sum()
             tab.insert_or_assign(uniq, v, sc)
             keys += uniq.numel()
         torch.cuda.synchronize()
@@ -646,6 +655,7 @@ def online_run(args) -> None:
         retention = int(mark[k].sum()) / cap
         res = dict(fill_batches=fill_batches, first_eviction_lambda=round(first_evict, 4) if first_evict else None,
                    hit_ratio=round(int(hits.item()) / (steady_batches * draws), 4),
+                   resident_fraction_of_distinct=round(int(resident_u.item()) / max(keys, 1), 4),
                    top_n_retention=round(retention, 5), distinct_keys_per_batch=int(keys / steady_batches),
                    upsert_bkvs=round(keys / steady_batches / up_ms / 1e6, 3),
                    lookup_bkvs=round(draws / look_ms / 1e6, 3) if look_ms else None,
@@ -942,31 +952,45 @@ def run_gpu(args):
         log(f"lambda={lam}: filled to size {size} ({size / cap:.4f}) with {cursor} keys "
             f"in {time.perf_counter() - t0:.1f}s")
         # Inputs of every step, generated now (outside the timed region).
+        # --hit-pool resident: each step's resident keys are sampled uniformly
+        # from the table's resident set as it is at that step: an untimed dry
+        # run on this table applies every step's upsert and exports the
+        # resident set before each step; a fresh table filled the same way
+        # (the same contents, single-bucket mode) then runs the steps. So the
+        # find batches hold exactly the hit fraction at every load factor.
+        # --hit-pool recent: from the 2^(batch+1) most recently inserted keys.
         n_hit = int(round(batch * args.hit_frac))
         n_new = int(round(batch * args.new_frac))
-        if args.hit_pool == "resident":
-            # every resident key (the table's own export): hits sampled
-            # uniformly from the whole resident set
-            pool = tab.export_batch(with_values=False)[0]
-        else:
-            recent = min(cursor, 2 * batch)
-            pool = gen.unique_keys(SEED, 1 + li, cursor - recent, recent, device=dev)
-        n_pool = pool.numel()
         finds, ups = [], []
-        vals_pool = [gen.values(pool[:batch], 1000 + j, dim, SEED) for j in range(2)]
+        vals_pool = None
         for s in range(total_steps):
+            if args.hit_pool == "resident":
+                pool = tab.export_batch(with_values=False)[0]
+            else:
+                recent = min(cursor, 2 * batch)
+                pool = gen.unique_keys(SEED, 1 + li, cursor - recent, recent, device=dev)
+            n_pool = pool.numel()
+            if vals_pool is None:
+                vals_pool = [gen.values(pool[:batch], 1000 + j, dim, SEED) for j in range(2)]
             pick = torch.argsort(gen.counter_words(SEED, 100 + li, s * n_pool, n_pool, dev))
             hits = pool[pick[:n_hit]]
             miss = gen.unique_keys(SEED, 40 + li, s * batch, batch - n_hit, device=dev)
             fk = gen.shuffle(torch.cat([hits, miss]), SEED, 200 + li * 1000 + s)
             res = (pool[pick[n_hit:n_hit + (batch - n_new)]] if batch - n_new <= n_pool - n_hit
                    else pool[pick[:batch - n_new]])
-            del pick
+            del pick, pool
             new = gen.unique_keys(SEED, 60 + li, s * batch, n_new, device=dev)
             uk = gen.shuffle(torch.cat([res, new]), SEED, 300 + li * 1000 + s)
             sc = torch.full((batch,), step + s, dtype=torch.int64, device=dev)
             finds.append(fk)
             ups.append((uk, sc))
+            if args.hit_pool == "resident" and not args.find_only:
+                tab.insert_or_assign(uk, vals_pool[s % 2], sc)
+        if args.hit_pool == "resident" and not args.find_only:
+            tab.close()
+            torch.cuda.synchronize()
+            tab = H.HashTable(cap, dim, device=0, unique_keys=args.unique_keys)
+            fill_table(tab, lam, cap, batch, dim, SEED, 1 + li, dev)
         if li == 0 and not args.no_cpu_baseline and not args.find_only:
             # the batches the CPU oracle replays: the warm-up steps and the
             # first timed steps of this table, copied to the host
@@ -1204,13 +1228,19 @@ def run_extra_ops(args, tables, batch, dim, hit):
         # with the library's per-kernel events in a second pass on fresh
         # batches (per-kernel events add host work per launch, which would
         # leave the GPU waiting inside the timed calls). Each
-        # insert_and_evict call writes its own hand-back count.
+        # insert_and_evict call writes its own hand-back count. The per-kernel
+        # events start one call after the synchronize: a kernel's event pair
+        # opens when the stream reaches its start marker, and on an idle GPU
+        # (just synchronized) that can precede the kernel's own dispatch by a
+        # host submission gap (up to ~1 ms seen for insert_and_evict's probe,
+        # whose dispatches all take 0.15-0.2 ms in rocprofv3's kernel trace).
         cnts = torch.zeros(reps + 2, dtype=torch.int64, device=dev)
         for name, part in (("insert_and_evict", batches[:reps + 2]), ("find_or_insert", batches[reps + 2:])):
             ms = []
             for j, (uk, uv, usc) in enumerate(part):
                 if j == 2:  # the first two calls (workspace growth) are warm-up in both measures
-                    torch.cuda.synchronize()  # no queued work ahead of the first timed launch
+                    torch.cuda.synchronize()
+                if j == 3:
                     tab.profile_start()
                 if j == reps // 2 + 2:  # the rest of the calls: call times only
                     ks = tab.profile_stop()

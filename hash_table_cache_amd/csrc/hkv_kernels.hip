@@ -146,38 +146,25 @@ __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* _
   }
 }
 
-// A row of up to R*G 16-byte pieces held in the registers of the G lanes of a
-// group (R as in copy_row), so that its load can be issued before a decision
-// that its store waits for.
+// A row of at most one 16-byte piece per lane (dim <= 4*G) held in the
+// registers of the G lanes of a group, so that its load can be issued before
+// a decision that its store waits for.
 template <int G>
 struct GroupRow {
-  static constexpr int R = G >= 16 ? 2 : 4;
-  f32x4 v[R];
-  __device__ static bool fits(uint32_t dim) { return (dim >> 2) <= static_cast<uint32_t>(R * G); }
+  f32x4 v;
 };
 
 template <int G>
 __device__ __forceinline__ void group_row_load(GroupRow<G>& r, const float* __restrict__ src, uint32_t dim,
                                                int lane) {
-  const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
-  const uint32_t n4 = dim >> 2;
-#pragma unroll
-  for (int u = 0; u < GroupRow<G>::R; ++u) {
-    const uint32_t c = lane + u * G;
-    if (c < n4) r.v[u] = __builtin_nontemporal_load(s4 + c);
-  }
+  if (static_cast<uint32_t>(lane) < (dim >> 2))
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + lane);
 }
 
 template <int G>
 __device__ __forceinline__ void group_row_store(const GroupRow<G>& r, float* __restrict__ dst, uint32_t dim,
                                                 int lane) {
-  f32x4* d4 = reinterpret_cast<f32x4*>(dst);
-  const uint32_t n4 = dim >> 2;
-#pragma unroll
-  for (int u = 0; u < GroupRow<G>::R; ++u) {
-    const uint32_t c = lane + u * G;
-    if (c < n4) __builtin_nontemporal_store(r.v[u], d4 + c);
-  }
+  if (static_cast<uint32_t>(lane) < (dim >> 2)) __builtin_nontemporal_store(r.v, reinterpret_cast<f32x4*>(dst) + lane);
 }
 
 // Takes slot p's claim bit for this call; true for the first taker only.
@@ -414,10 +401,14 @@ __device__ __forceinline__ int64_t probe_prefetch(const TableView& t, uint64_t k
   cand_issue(c, t.keys, m1, static_cast<uint64_t>(b1) * kSlots + off, m2, static_cast<uint64_t>(b2) * kSlots + off);
   if (load_row && group_bits<G>(__ballot(c.h0)) != 0) group_row_load<G>(rr, src, t.dim, lane);
   const int64_t hit = cand_finish(c, t.keys, k);
-  *occ1 = line_occupancy<G, NW>(w1);
-  if constexpr (DUAL) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
   const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
-  if (bits == 0) return -1;
+  if (bits == 0) {
+    // a miss: the occupancies choose its bucket (the result is group-uniform,
+    // so the whole group takes this branch together)
+    *occ1 = line_occupancy<G, NW>(w1);
+    if constexpr (DUAL) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
+    return -1;
+  }
   return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
 }
 
@@ -991,9 +982,13 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   }
   uint32_t o1 = 0, o2 = 0;
   int64_t p;
-  // (insert_or_assign: the input row, needed by a hit, is requested together
-  // with the candidate keys, as soon as the digest lines show a candidate)
-  const bool in_regs = !FETCH && V4 && GroupRow<G>::fits(t.dim);
+  // (insert_or_assign with rows of one 16-byte piece per lane: the input
+  // row, needed by a hit, is requested together with the candidate keys, as
+  // soon as the digest lines show a candidate. Measured at 2^26 slots: dim 32
+  // (8 lanes) 131 vs 134 us per 2^20 keys; at dim 64 the overlap no longer
+  // pays for the rows read for missing keys with a false candidate, 160 vs
+  // 157 us, so larger rows are read after the match.)
+  const bool in_regs = !FETCH && V4 && t.dim <= 4 * G;
   GroupRow<G> rr;
   if constexpr (FETCH) {
     p = probe<G, DUAL>(t, k, lane, &o1, &o2);
@@ -1302,8 +1297,11 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     o.scols = false;
     o.kval = 0;
     o.wmask = 0;
+    // The head was set by the probe kernel's exchanges and is published by
+    // the kernel boundary; in this kernel only this group reads or resets it,
+    // so plain accesses suffice.
     uint32_t head = 0;
-    if (lane == 0) head = __hip_atomic_load(t.head + o.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) head = t.head[o.b];
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
     RowRegs rr;
     const float* row = values + static_cast<uint64_t>(i) * t.dim;
@@ -1331,8 +1329,10 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, st, cur, lane);
       cur = after;
     }
-    if (DUAL && o.occ >= kSlots) {
+    if (DUAL && o.occ >= kSlots && group_bits<kInsG>(__ballot(o.wmask != 0)) != 0) {
       // record the bucket's lowest (score, key) for later dual-bucket choices
+      // (a chain that wrote nothing - every key turned away - leaves the
+      // bucket, and so its record, as it was)
       uint64_t gs, gk;
       (void)bucket_lowest(o, t, lane, &gs, &gk);
       if (lane == 0) {
@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     }
     if (lane == 0) {
       if (o.occ != occ0) t.occ[o.b] = o.occ;
-      __hip_atomic_store(t.head + o.b, kNoIdx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t.head[o.b] = kNoIdx;
     }
   }
 }

@@ -29,6 +29,7 @@ namespace {
 constexpr uint64_t kSlots = HKV_BUCKET_SLOTS;
 constexpr uint64_t kMaxBatch = 0xFFFFFFFDull;  // indices 0xFFFFFFFE/F are chain markers
 constexpr uint32_t kMaxDim = 1u << 20;
+constexpr size_t kProfileEvents = 512;  // timing events made ready by hkv_profile_start
 
 enum Group { kReader = 0, kUpdater = 1, kInserter = 2 };
 
@@ -101,6 +102,28 @@ class Profiler final : public hkv::KernelTimer {
   }
   std::vector<Rec>& records() { return recs_; }
   void give_back(hipEvent_t e) { pool_.push_back(e); }
+  // Creates events until the pool holds `count`, and records each new one
+  // once (on a private stream, waited for), so that no event is created or
+  // used for the first time while launches are being timed.
+  void prewarm(size_t count) {
+    if (pool_.size() >= count) return;
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    while (pool_.size() < count) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        break;
+      }
+      (void)hipEventRecord(e, s);
+      pool_.push_back(e);
+    }
+    (void)hipStreamSynchronize(s);
+    (void)hipStreamDestroy(s);
+  }
   void destroy_all() {
     for (auto& r : recs_) {
       (void)hipEventDestroy(r.start);
@@ -776,6 +799,7 @@ HKV_API hkv_status hkv_profile_start(hkv_table* t) {
     t->prof.give_back(r.stop);
   }
   t->prof.records().clear();
+  t->prof.prewarm(kProfileEvents);
   t->profiling = true;
   return HKV_OK;
 }

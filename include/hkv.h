@@ -326,7 +326,9 @@ typedef struct hkv_kernel_stat {
   double sumsq_ms2;   /* sum of their squared times (spread across launches) */
 } hkv_kernel_stat;
 
-/* hkv_profile_start - discards earlier records and turns timing on. */
+/* hkv_profile_start - discards earlier records and turns timing on. The
+ * timing events are created (a pool of 512, grown if needed) and recorded
+ * once here, so that none is created during the timed launches. */
 hkv_status hkv_profile_start(hkv_table* table);
 
 /* hkv_profile_stop - turns timing off, waits for every timed launch, writes
