@@ -1060,8 +1060,11 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     }
   }
   target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
-  next[i] = __hip_atomic_exchange(t.head + tb, static_cast<uint32_t>(i), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+  // the head carries this call's epoch, so a head left by an earlier call
+  // reads as an empty chain and no kernel has to reset it
+  const uint64_t old = __hip_atomic_exchange(t.head + tb, (static_cast<uint64_t>(t.epoch) << 32) | i,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  next[i] = static_cast<uint32_t>(old >> 32) == t.epoch ? static_cast<uint32_t>(old) : kNoIdx;
 }
 
 // Resets the claim bits of bucket b's 128 slots (one 16-byte store).
@@ -1297,11 +1300,10 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     o.scols = false;
     o.kval = 0;
     o.wmask = 0;
-    // The head was set by the probe kernel's exchanges and is published by
-    // the kernel boundary; in this kernel only this group reads or resets it,
-    // so plain accesses suffice.
+    // The head was set by the probe kernel's exchanges (this call's epoch,
+    // as the bucket has an owner) and is published by the kernel boundary.
     uint32_t head = 0;
-    if (lane == 0) head = t.head[o.b];
+    if (lane == 0) head = static_cast<uint32_t>(t.head[o.b]);
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
     RowRegs rr;
     const float* row = values + static_cast<uint64_t>(i) * t.dim;
@@ -1342,10 +1344,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
         *reinterpret_cast<ulonglong2*>(t.bmin + 2 * static_cast<uint64_t>(o.b)) = rec;
       }
     }
-    if (lane == 0) {
-      if (o.occ != occ0) t.occ[o.b] = o.occ;
-      t.head[o.b] = kNoIdx;
-    }
+    if (lane == 0 && o.occ != occ0) t.occ[o.b] = o.occ;
   }
 }
 
@@ -1541,13 +1540,18 @@ __global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
     if (p < t.nb * 4) t.claim[p] = 0;
     if (p < t.nb) {
       t.occ[p] = 0;
-      t.head[p] = kNoIdx;
+      t.head[p] = 0;
       if (t.bmin) {
         t.bmin[2 * p] = 0;
         t.bmin[2 * p + 1] = ~0ull;
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kBlock) void reset_heads_kernel(TableView t) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; b < t.nb; b += stride) t.head[b] = 0;
 }
 
 uint32_t grid_for(uint64_t threads) {
@@ -1736,6 +1740,13 @@ hipError_t launch_init(const TableView& t, hipStream_t s) {
   uint64_t blocks = (cap + kBlock - 1) / kBlock;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(init_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_heads(const TableView& t, hipStream_t s) {
+  uint64_t blocks = (t.nb + kBlock - 1) / kBlock;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(reset_heads_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s, t);
   return hipGetLastError();
 }
 

@@ -433,6 +433,13 @@ static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool
     c.chunk_count = t->ev_chunks;
   }
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
+  // A new epoch per call: chain heads of earlier calls then read as empty.
+  // After 2^32 - 1 calls the counter wraps and every head is reset first.
+  if (++t->view.epoch == 0) {
+    const hipError_t er = hkv::launch_reset_heads(t->view, stream);
+    if (er != hipSuccess) return fail_hip(er, what);
+    t->view.epoch = 1;
+  }
   const hipError_t e = hkv::launch_upsert(t->view, n, c, ws_next, ws_target, vec4, serial, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, what);
   return record_after(t, kInserter, stream);
@@ -499,9 +506,13 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (const char* g = std::getenv("HKV_GROUP_LANES")) v.lanes = static_cast<uint32_t>(std::atoi(g));
   v.keys_per_group = 2;
   if (const char* g = std::getenv("HKV_KEYS_PER_GROUP")) v.keys_per_group = static_cast<uint32_t>(std::atoi(g));
+  // Inserter-call counter (the first call takes epoch 1); a start value lets
+  // tests reach its wrap.
+  v.epoch = 0;
+  if (const char* g = std::getenv("HKV_EPOCH_START")) v.epoch = static_cast<uint32_t>(std::strtoul(g, nullptr, 0));
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&
             hipMalloc(&v.scores, cap * 8) == hipSuccess && hipMalloc(&v.occ, nb * 4) == hipSuccess &&
-            hipMalloc(&v.head, nb * 4) == hipSuccess && hipMalloc(&v.claim, nb * 16) == hipSuccess &&
+            hipMalloc(&v.head, nb * 8) == hipSuccess && hipMalloc(&v.claim, nb * 16) == hipSuccess &&
             hipMalloc(&t->size_dev, 8) == hipSuccess &&
             (!o->dual_bucket || hipMalloc(&v.bmin, nb * 16) == hipSuccess) &&
             hipHostMalloc(&t->size_host, 8, hipHostMallocDefault) == hipSuccess;

@@ -55,7 +55,9 @@
  *     serve one key in the probing kernels (4, 8 or 16; any other value keeps
  *     the default chosen from dim). HKV_KEYS_PER_GROUP: keys each group serves
  *     in the key-side probes of hkv_find_ptr and hkv_contains (1, 2 or 4;
- *     default 2).
+ *     default 2). A third, HKV_EPOCH_START, sets the table's inserter-call
+ *     counter (it tags the chain heads and wraps after 2^32 - 1 calls) to a
+ *     start value, so that tests can reach the wrap quickly.
  */
 #ifndef HKV_H_
 #define HKV_H_
@@ -122,8 +124,8 @@ typedef struct hkv_options {
  * Storage per slot: key 8 B + score 8 B + digest 1 B in HBM (§5.1, memory
  * overhead), plus a value row of 4*dim bytes in HBM or in pinned host memory
  * (split at a bucket boundary by hbm_value_bytes, see hkv_options). Per
- * bucket, 24 bytes of bookkeeping in HBM (occupancy, inserter chain head, one
- * claim bit per slot) and, in dual-bucket mode, 16 more (its lowest entry).
+ * bucket, 28 bytes of bookkeeping in HBM (occupancy 4, inserter chain head 8,
+ * one claim bit per slot) and, in dual-bucket mode, 16 more (its lowest entry).
  * Every slot starts empty. The table owns all of its storage.
  * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128,
  * dim == 0, bucket_slots not 128, bad device), HKV_ENOMEM, HKV_EHIP.

@@ -363,6 +363,36 @@ def test_contention_few_buckets_mixed_with_updates(hot_buckets):
     check_find(tab, o, to_dev(keys[:2400]))
 
 
+def test_inserter_epoch_wrap_keeps_chains_exact(monkeypatch):
+    """Chain heads carry the inserter call's epoch and are never reset; the
+    per-table call counter starts just below its wrap here, so the calls run
+    at epochs 2^32-2, 2^32-1, then (heads reset) 1, 2, ... Every batch sends
+    many keys to the same few buckets (long chains, heads left by the
+    previous call in every one of them); contents exact after each call."""
+    monkeypatch.setenv("HKV_EPOCH_START", str(0xFFFFFFFD))
+    H = hkv()
+    C, D = 16 * SLOTS, 8
+    tab = H.HashTable(C, D)
+    monkeypatch.delenv("HKV_EPOCH_START")
+    o = oracle.OracleTable(C, D)
+    rng = np.random.default_rng(77)
+    cand = rng.integers(1, 1 << 62, size=200000, dtype=np.int64).view(np.uint64)
+    keys = cand[np.isin(o.route(cand)[0], [2, 5, 11])][:2400]
+    for step in range(1, 7):
+        k = keys[(step - 1) * 400: step * 400]
+        sc = (step * 2 + rng.integers(0, 2, size=k.size)).astype(np.uint64)
+        kt, st = to_dev(k), to_dev(sc)
+        v = gen.values(kt, step, D)
+        if step == 4:
+            f, _ = tab.find_or_insert(kt, v, st)
+            o.find_or_insert(k, sc, values=v.cpu().numpy())
+        else:
+            tab.insert_or_assign(kt, v, st)
+            o.insert_or_assign(k, sc, values=v.cpu().numpy())
+        assert_same_contents(tab, o)
+    check_find(tab, o, to_dev(keys))
+
+
 def test_edge_cases_reserved_empty_duplicates():
     H = hkv()
     C, D = 4 * SLOTS, 4
