@@ -32,6 +32,7 @@ from ._native import (  # noqa: F401
     hkv_insert_or_assign,
     hkv_profile_start,
     hkv_profile_stop,
+    hkv_set_outcome_counters,
     hkv_size,
 )
 
@@ -62,6 +63,7 @@ class HashTable:
         self.device = int(device)
         flags = (int(flags) | (HKV_FLAG_SERIAL_INSERT if serial_insert else 0)
                  | (HKV_FLAG_UNIQUE_KEYS if unique_keys else 0))
+        self._outcomes = None
         self._h = hkv_create(capacity, dim, dual_bucket, values_on_host, device, flags, hbm_value_bytes)
 
     def close(self) -> None:
@@ -147,6 +149,26 @@ class HashTable:
 
     def size(self, stream=None) -> int:
         return hkv_size(self._h, stream, device=self.device)
+
+    OUTCOMES = ("updated", "inserted", "evicted", "rejected")
+
+    def count_outcomes(self, enable: bool = True) -> None:
+        """Start (from zero) or stop counting the inserter calls' outcomes."""
+        if enable:
+            self._outcomes = torch.zeros(4, dtype=torch.int64, device=self._dev())
+            torch.cuda.synchronize(self._dev())
+            hkv_set_outcome_counters(self._h, self._outcomes)
+        else:
+            hkv_set_outcome_counters(self._h, None)
+            self._outcomes = None
+
+    def outcomes(self) -> dict:
+        """{updated, inserted, evicted, rejected} added up since
+        count_outcomes(); waits for the device."""
+        if self._outcomes is None:
+            raise RuntimeError("outcomes are not being counted; call count_outcomes() first")
+        torch.cuda.synchronize(self._dev())
+        return dict(zip(self.OUTCOMES, (int(v) for v in self._outcomes.cpu().tolist())))
 
     def profile_start(self) -> None:
         """Time every kernel this table launches from now on (events on its stream)."""

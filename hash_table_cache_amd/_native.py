@@ -48,6 +48,7 @@ EXPORTS = (
     "hkv_assign",
     "hkv_size",
     "hkv_export_batch",
+    "hkv_set_outcome_counters",
     "hkv_profile_start",
     "hkv_profile_stop",
     "hkv_last_error",
@@ -117,6 +118,8 @@ def _load() -> ctypes.CDLL:
     L.hkv_size.restype = st
     L.hkv_export_batch.argtypes = [vp, u64, u64, vp, vp, vp, vp, vp, vp]
     L.hkv_export_batch.restype = st
+    L.hkv_set_outcome_counters.argtypes = [vp, vp]
+    L.hkv_set_outcome_counters.restype = st
     L.hkv_profile_start.argtypes = [vp]
     L.hkv_profile_start.restype = st
     L.hkv_profile_stop.argtypes = [vp, ctypes.POINTER(HkvKernelStat), ctypes.c_uint32,
@@ -292,6 +295,12 @@ def hkv_export_batch(table, offset, n_slots, keys_out, values_out, scores_out, p
         _ptr(pos_out, _U64_DTYPES, 0, "pos_out", nullable=True),
         _ptr(count_out, _U64_DTYPES, 1, "count_out"),
         _stream(stream, device)))
+
+
+def hkv_set_outcome_counters(table, counts) -> None:
+    """counts: a device tensor of 4 int64 (updated, inserted, evicted,
+    rejected) that the inserter calls add to, or None to stop counting."""
+    _check(load().hkv_set_outcome_counters(table, _ptr(counts, _U64_DTYPES, 4, "counts", nullable=True)))
 
 
 def hkv_profile_start(table) -> None:

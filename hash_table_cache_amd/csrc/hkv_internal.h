@@ -82,6 +82,12 @@ hipError_t launch_locate(const TableView& t, uint64_t n, const uint64_t* keys, u
 // find_or_insert: fetch = true, values is in/out, found optional.
 // insert_and_evict: ev_keys/ev_count set (ev_values, ev_scores optional);
 // ev_count is zeroed by the launch.
+// Outcome counters: each of the four counts (updated, inserted, evicted,
+// rejected) is accumulated over kStatSlots device words (block b adds to word
+// b mod kStatSlots) and summed into the caller's counters at the end of the
+// call, which also clears the words.
+constexpr int kStatSlots = 256;
+
 struct InsertCall {
   const uint64_t* keys;
   float* values;
@@ -99,6 +105,10 @@ struct InsertCall {
   uint64_t* st_scores;
   float* st_rows;
   uint32_t* chunk_count;  // [ceil(n / 1024)]
+  // outcome counters (parallel inserter): the table's 4 * kStatSlots words,
+  // all zero between calls, and the caller's 4 counters; nullptr: not counted
+  unsigned long long* stat_slots;
+  unsigned long long* outcomes;
 };
 
 // next, target: [n] u32 workspaces (not used by insert_or_assign in serial mode).

@@ -47,6 +47,8 @@ constexpr int kSlots = 128;
 constexpr uint64_t kLockedKey = ~0ull - 1;  // keys >= this are reserved
 constexpr uint32_t kNoIdx = 0xFFFFFFFFu;    // chain end / empty chain head
 constexpr uint32_t kSkipIdx = 0xFFFFFFFEu;  // key takes no part in the insert
+constexpr uint32_t kUpdIdx = 0xFFFFFFFCu;   // resident key updated (or its row read by
+                                            // find_or_insert) with no claim to release
 constexpr uint32_t kHitIdx = 0xFFFFFFFDu;   // resident key updated by this occurrence;
                                             // target[i] = its bucket (claim to clear)
 constexpr uint32_t kFullBit = 0x80000000u;  // target word: the bucket was full at probe time
@@ -57,6 +59,9 @@ constexpr int kInsG = 16;  // lanes per key in the inserter (8 slots per lane)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool is_reserved(uint64_t k) { return k >= kLockedKey; }
+
+// A key whose chain word is a batch index or kNoIdx was pushed onto a chain.
+__device__ __forceinline__ bool in_chain(uint32_t nx) { return nx == kNoIdx || nx < kUpdIdx; }
 
 // MurmurHash3's 64-bit finalizer, the table's hash (§3.2 names a Murmur3
 // variant without giving it).
@@ -1005,7 +1010,7 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
       }
       if (lane == 0) {
         t.scores[p] = score;
-        next[i] = kSkipIdx;
+        next[i] = kUpdIdx;
         if (found) found[i] = 1;
       }
     } else {
@@ -1029,7 +1034,7 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
       if (lane == 0) {
         if (won) t.scores[p] = score;
         if (won && t.claims) target[i] = static_cast<uint32_t>(static_cast<uint64_t>(p) / kSlots);
-        next[i] = won && t.claims ? kHitIdx : kSkipIdx;
+        next[i] = !won ? kSkipIdx : t.claims ? kHitIdx : kUpdIdx;
       }
     }
     return;
@@ -1174,7 +1179,7 @@ __device__ __forceinline__ void bucket_write(Bucket& o, const TableView& t, int 
 // loaded. `fresh`: the key is known to be absent (a chain's first key, which
 // the probe kernel found missing, before anything was inserted).
 template <bool V4, bool EVICT>
-__device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint64_t k, uint64_t score,
+__device__ __forceinline__ bool bucket_apply(Bucket& o, const TableView& t, uint64_t k, uint64_t score,
                                              const RowRegs& rr, const float* row, bool in_regs, bool fresh,
                                              const EvictStage& st, uint32_t idx, int lane) {
   const uint32_t d = digest_of(fmix64(k));
@@ -1203,7 +1208,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
     bucket_write(o, t, hit, false, k, d, score, lane);
     write_row(hit);
     if (EVICT && lane == 0) st.kind[idx] = 0;
-    return;
+    return true;
   }
   if (o.occ < kSlots) {
     const int s = static_cast<int>(o.occ);
@@ -1211,7 +1216,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
     write_row(s);
     o.occ += 1;
     if (EVICT && lane == 0) st.kind[idx] = 0;
-    return;
+    return false;
   }
   uint64_t gs, gk;
   const int vs = bucket_lowest(o, t, lane, &gs, &gk);
@@ -1236,6 +1241,7 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
       st.kind[idx] = 2;
     }
   }
+  return false;
 }
 
 // Insert, second kernel: the first-pushed key of each chain (next ==
@@ -1247,14 +1253,17 @@ __device__ __forceinline__ void bucket_apply(Bucket& o, const TableView& t, uint
 // chain from its head down to itself (Algorithm 2, each chain key costing one
 // round trip for its inputs), writes the occupancy and resets the chain head.
 // With distinct keys any order within a chain gives the same bucket contents.
-template <bool V4, bool DUAL, bool EVICT>
+// STATS: the block's outcome counts (updated, inserted, evicted, rejected)
+// are added to stat_slots[c * kStatSlots + block mod kStatSlots].
+template <bool V4, bool DUAL, bool EVICT, bool STATS>
 __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
                                                               const float* __restrict__ values,
                                                               const uint64_t* __restrict__ scores,
                                                               const uint32_t* __restrict__ next,
                                                               const uint32_t* __restrict__ target,
-                                                              EvictStage st, bool clear_all) {
+                                                              EvictStage st, bool clear_all,
+                                                              unsigned long long* __restrict__ stat_slots) {
   // The block's owners (keys with next == kNoIdx) are listed in LDS and dealt
   // out to its 16 groups in turn, so that every group serves about the same
   // number of buckets.
@@ -1263,10 +1272,19 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
   __shared__ uint64_t s_key[kBlock];
   __shared__ uint64_t s_score[kBlock];
   __shared__ uint32_t s_count;
+  __shared__ uint32_t s_stat[4];
   const uint64_t mine = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (threadIdx.x == 0) s_count = 0;
+  if (STATS && threadIdx.x < 4) s_stat[threadIdx.x] = 0;
   __syncthreads();
+  if constexpr (STATS) {
+    // keys found resident by the probe kernel: updated in place (the claim
+    // winner alone when claims are taken), or read by find_or_insert
+    const uint32_t nx = mine < n ? next[mine] : kSkipIdx;
+    const uint64_t upd = __ballot(nx == kHitIdx || nx == kUpdIdx);
+    if (wave_lane() == 0 && upd) atomicAdd(&s_stat[0], static_cast<uint32_t>(__popcll(upd)));
+  }
   if (mine < n) {
     const uint32_t nx = next[mine];
     if (nx == kNoIdx) {
@@ -1319,6 +1337,7 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     // A chain holds only keys the probe found missing, so the owner's own
     // key, applied first, is known to be absent.
     bucket_apply<V4, EVICT>(o, t, k, score, rr, row, in_regs, true, st, i, lane);
+    uint32_t occurrences = 1, repeats = 0;  // (outcome counts)
     // The chain holds at most n keys and ends at this owner's own key; the
     // index and step bounds only guard against a corrupted chain.
     uint32_t cur = __shfl(head, 0, kInsG);
@@ -1328,8 +1347,31 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
       const uint64_t scc = scores[cur];
       const float* rowc = values + static_cast<uint64_t>(cur) * t.dim;
       if (in_regs) row_regs_load(rr, rowc, t.dim, lane);
-      bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, st, cur, lane);
+      const bool again = bucket_apply<V4, EVICT>(o, t, kc, scc, rr, rowc, in_regs, false, st, cur, lane);
+      if constexpr (STATS) {
+        occurrences += 1;
+        repeats += again ? 1u : 0u;
+      }
       cur = after;
+    }
+    if constexpr (STATS) {
+      // Every slot written by this kernel holds one of the chain's keys at the
+      // end (inserted); a written slot below the occupancy the call started
+      // with held a key resident before the call, which has left (evicted);
+      // the chain's other keys are not resident (rejected).
+      const int first = lane * 8;
+      const uint32_t before = occ0 >= static_cast<uint32_t>(first + 8) ? 0xFFu
+                              : occ0 > static_cast<uint32_t>(first) ? (1u << (occ0 - first)) - 1u
+                                                                     : 0u;
+      uint32_t packed = static_cast<uint32_t>(__popc(o.wmask)) | (static_cast<uint32_t>(__popc(o.wmask & before)) << 16);
+#pragma unroll
+      for (int sh = kInsG / 2; sh > 0; sh >>= 1) packed += __shfl_xor(packed, sh, kInsG);
+      if (lane == 0) {
+        const uint32_t ins = packed & 0xFFFFu;
+        atomicAdd(&s_stat[1], ins);
+        atomicAdd(&s_stat[2], packed >> 16);
+        atomicAdd(&s_stat[3], occurrences - repeats - ins);
+      }
     }
     if (DUAL && o.occ >= kSlots && group_bits<kInsG>(__ballot(o.wmask != 0)) != 0) {
       // record the bucket's lowest (score, key) for later dual-bucket choices
@@ -1346,6 +1388,35 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     }
     if (lane == 0 && o.occ != occ0) t.occ[o.b] = o.occ;
   }
+  if constexpr (STATS) {
+    __syncthreads();
+    if (threadIdx.x < 4 && s_stat[threadIdx.x] != 0)
+      atomicAdd(stat_slots + threadIdx.x * kStatSlots + blockIdx.x % kStatSlots,
+                static_cast<unsigned long long>(s_stat[threadIdx.x]));
+  }
+}
+
+// Sums the outcome slots into the caller's four counters and clears them
+// (one block of kStatSlots threads).
+__global__ __launch_bounds__(kStatSlots) void outcome_flush_kernel(unsigned long long* __restrict__ slots,
+                                                                   unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long part[4][kStatSlots / 64];
+  const int w = static_cast<int>(threadIdx.x / 64);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    unsigned long long v = slots[c * kStatSlots + threadIdx.x];
+    slots[c * kStatSlots + threadIdx.x] = 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (wave_lane() == 0) part[c][w] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    unsigned long long sum = 0;
+#pragma unroll
+    for (int v = 0; v < kStatSlots / 64; ++v) sum += part[threadIdx.x][v];
+    atomicAdd(out + threadIdx.x, sum);
+  }
 }
 
 // insert_and_evict, parallel inserter: the staged departures are compacted
@@ -1359,7 +1430,7 @@ constexpr int kChunk = 4 * kBlock;
 __device__ __forceinline__ bool departs(uint64_t i, uint64_t n, const uint32_t* next, const EvictStage& st,
                                         uint32_t* kd) {
   *kd = 0;
-  if (i < n && next[i] != kSkipIdx && next[i] != kHitIdx) *kd = st.kind[i];
+  if (i < n && in_chain(next[i])) *kd = st.kind[i];
   return *kd != 0;
 }
 
@@ -1613,7 +1684,7 @@ hipError_t probe_g(const TableView& t, uint64_t n, const InsertCall& c, uint32_t
   return hipGetLastError();
 }
 
-template <bool V4, bool DUAL>
+template <bool V4, bool DUAL, bool STATS>
 hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const uint32_t* next,
                    const uint32_t* target, hipStream_t s, KernelTimer* tm) {
   const EvictStage st{c.st_kind, c.st_keys, c.st_scores, c.st_rows};
@@ -1621,22 +1692,29 @@ hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const ui
   // that costs less than one 16-byte store per update, else per update.
   // (find_or_insert takes no claims.)
   const bool clear_all = t.claims && !c.fetch && t.nb <= 4 * n;
+  hipError_t e = hipSuccess;
   if (!c.ev_keys) {
-    HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false>), dim3(grid_for(n)), dim3(kBlock), s,
-               t, n, c.keys, c.values, c.scores, next, target, st, clear_all);
-    return hipGetLastError();
+    HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false, STATS>), dim3(grid_for(n)),
+               dim3(kBlock), s, t, n, c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true, STATS>), dim3(grid_for(n)),
+               dim3(kBlock), s, t, n, c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const Evicted out{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
+    const uint32_t chunks = static_cast<uint32_t>((n + kChunk - 1) / kChunk);
+    HKV_LAUNCH(tm, "evict_count", evict_count_kernel, dim3(chunks), dim3(kBlock), s, n, next, st,
+               c.chunk_count);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    HKV_LAUNCH(tm, "evict_write", (evict_write_kernel<V4>), dim3(chunks), dim3(kBlock), s, t, n, next, st,
+               c.values, c.chunk_count, out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true>), dim3(grid_for(n)), dim3(kBlock), s, t,
-             n, c.keys, c.values, c.scores, next, target, st, clear_all);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const Evicted out{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
-  const uint32_t chunks = static_cast<uint32_t>((n + kChunk - 1) / kChunk);
-  HKV_LAUNCH(tm, "evict_count", evict_count_kernel, dim3(chunks), dim3(kBlock), s, n, next, st, c.chunk_count);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  HKV_LAUNCH(tm, "evict_write", (evict_write_kernel<V4>), dim3(chunks), dim3(kBlock), s, t, n, next, st,
-             c.values, c.chunk_count, out);
-  return hipGetLastError();
+  if constexpr (STATS) {
+    HKV_LAUNCH(tm, "outcomes", outcome_flush_kernel, dim3(1), dim3(kStatSlots), s, c.stat_slots, c.outcomes);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <bool V4, bool DUAL>
@@ -1696,7 +1774,8 @@ hipError_t upsert_d(const TableView& t, uint64_t n, const InsertCall& c, uint32_
                c.values, c.scores, two_phase ? next : nullptr, two_phase ? target : nullptr, ev);
     return hipGetLastError();
   }
-  return owner_l<V4, DUAL>(t, n, c, next, target, s, tm);
+  return c.stat_slots ? owner_l<V4, DUAL, true>(t, n, c, next, target, s, tm)
+                      : owner_l<V4, DUAL, false>(t, n, c, next, target, s, tm);
 }
 
 template <int G, bool DUAL>

@@ -27,7 +27,7 @@
 namespace {
 
 constexpr uint64_t kSlots = HKV_BUCKET_SLOTS;
-constexpr uint64_t kMaxBatch = 0xFFFFFFFDull;  // indices 0xFFFFFFFE/F are chain markers
+constexpr uint64_t kMaxBatch = 0xFFFFFFFCull;  // indices 0xFFFFFFFC..F are chain markers
 constexpr uint32_t kMaxDim = 1u << 20;
 constexpr size_t kProfileEvents = 512;  // timing events made ready by hkv_profile_start
 
@@ -168,6 +168,8 @@ struct hkv_table {
   uint64_t ev_cap = 0;
   unsigned long long* size_dev = nullptr;
   unsigned long long* size_host = nullptr;  // pinned
+  unsigned long long* stat_slots = nullptr;  // outcome counting words (4 * kStatSlots)
+  unsigned long long* outcomes = nullptr;    // the caller's 4 counters, or nullptr
   std::mutex mu;
   std::vector<StreamEvent> last[3];  // per group: last event recorded on each stream
   bool any_call = false;             // a call has been issued
@@ -198,6 +200,7 @@ void free_storage(hkv_table* t) {
   if (t->ev_scores) (void)hipFree(t->ev_scores);
   if (t->ev_rows) (void)hipFree(t->ev_rows);
   if (t->ev_chunks) (void)hipFree(t->ev_chunks);
+  if (t->stat_slots) (void)hipFree(t->stat_slots);
   if (t->size_dev) (void)hipFree(t->size_dev);
   if (t->size_host) (void)hipHostFree(t->size_host);
   for (auto& list : t->last)
@@ -431,6 +434,10 @@ static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool
     c.st_scores = t->ev_scores;
     c.st_rows = t->ev_rows;
     c.chunk_count = t->ev_chunks;
+  }
+  if (!serial && t->outcomes) {
+    c.stat_slots = t->stat_slots;
+    c.outcomes = t->outcomes;
   }
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
   // A new epoch per call: chain heads of earlier calls then read as empty.
@@ -798,6 +805,52 @@ HKV_API hkv_status hkv_export_batch(hkv_table* t, uint64_t offset, uint64_t n_sl
                                           t->timer());
   if (e != hipSuccess) return fail_hip(e, "export launch");
   return record_after(t, kReader, stream);
+}
+
+HKV_API hkv_status hkv_set_outcome_counters(hkv_table* t, uint64_t* counts) {
+  if (!t) return fail(HKV_EINVAL, "table is NULL");
+  if (counts && (t->opt.flags & HKV_FLAG_SERIAL_INSERT))
+    return fail(HKV_EINVAL, "outcome counters: the table inserts serially (HKV_FLAG_SERIAL_INSERT); "
+                "they are kept by the parallel inserter only");
+  hkv_status st;
+  if (counts) {
+    if ((st = check_buffer(t, counts, 4 * sizeof(uint64_t), "counts")) != HKV_OK) return st;
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof(a));
+    if (hipPointerGetAttributes(&a, counts) != hipSuccess || a.type != hipMemoryTypeDevice) {
+      (void)hipGetLastError();
+      return fail(HKV_EINVAL, "counts (%p) must be device memory of the table's GPU", static_cast<void*>(counts));
+    }
+    if (reinterpret_cast<uintptr_t>(counts) & 7) return fail(HKV_EINVAL, "counts is not 8-byte aligned");
+  }
+  std::lock_guard<std::mutex> lk(t->mu);
+  DeviceGuard dg(t->opt.device);
+  if (dg.error() != hipSuccess) return fail_hip(dg.error(), "hipSetDevice");
+  if (counts && !t->stat_slots) {
+    // the counting words start at zero; every counted call leaves them so
+    const size_t bytes = 4 * hkv::kStatSlots * sizeof(unsigned long long);
+    hipError_t e = hipMalloc(&t->stat_slots, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      t->stat_slots = nullptr;
+      return fail(HKV_ENOMEM, "outcome counters (%zu bytes)", bytes);
+    }
+    hipStream_t s = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) {
+      e = hipMemsetAsync(t->stat_slots, 0, bytes, s);
+      const hipError_t e2 = hipStreamSynchronize(s);
+      if (e == hipSuccess) e = e2;
+      (void)hipStreamDestroy(s);
+    }
+    if (e != hipSuccess) {
+      (void)hipFree(t->stat_slots);
+      t->stat_slots = nullptr;
+      return fail_hip(e, "outcome counters");
+    }
+  }
+  t->outcomes = reinterpret_cast<unsigned long long*>(counts);
+  return HKV_OK;
 }
 
 HKV_API hkv_status hkv_profile_start(hkv_table* t) {

@@ -46,7 +46,7 @@
  *     cannot do).
  *   - Arguments are validated synchronously; on any error nothing is enqueued,
  *     the call returns a negative status and hkv_last_error() describes it.
- *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 3 keys.
+ *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 4 keys.
  *   - The reserved keys HKV_EMPTY_KEY and HKV_LOCKED_KEY always miss in the
  *     readers and are skipped by the updaters and inserters.
  *   - No C++ exception crosses this boundary.
@@ -312,6 +312,36 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
                             uint64_t* pos_out, uint64_t* count_out, hipStream_t stream);
 
 /*
+ * hkv_set_outcome_counters - optional outcome counts of the inserter calls
+ * (a metrics aid the paper's API does not have; the DynamicEmb API page, in
+ * its DynamicEmbCheckMode section, counts the keys a lookup could not
+ * insert, which is `rejected` below).
+ * After this call, every insert_or_assign (and its no-alloc variant),
+ * insert_and_evict and find_or_insert on the table adds to counts[0..3]:
+ *   counts[0] updated:  keys of the batch resident when the call started
+ *                       (updated in place, or their stored row returned by
+ *                       find_or_insert);
+ *   counts[1] inserted: keys absent when the call started, resident at its end;
+ *   counts[2] evicted:  keys resident when the call started, absent at its end;
+ *   counts[3] rejected: keys of the batch absent when the call started and at
+ *                       its end (turned away by admission, or admitted and
+ *                       displaced by a later key of the same call).
+ * So size after = size before + inserted - evicted. For batches of distinct
+ * keys these are properties of the call's start and end states alone. With a
+ * key repeated in a batch, updated counts it once in insert_or_assign and
+ * insert_and_evict, once per occurrence in find_or_insert; rejected counts a
+ * key again when an occurrence arrives after its earlier one was displaced.
+ * counts: 4 uint64 in device memory of the table's GPU, owned by the caller
+ * and valid while set; the calls add to them (zero them to start) with
+ * device atomics, after the call's other kernels, on the call's stream.
+ * NULL turns counting off. Counting adds one small kernel per call.
+ * Errors: HKV_EINVAL (NULL table, counts not device memory of that GPU or
+ * shorter than 32 bytes, a table with HKV_FLAG_SERIAL_INSERT), HKV_ENOMEM
+ * (the table's 8 KiB of counting words, allocated on the first call).
+ */
+hkv_status hkv_set_outcome_counters(hkv_table* table, uint64_t* counts);
+
+/*
  * Kernel timing (tracing aid; not part of the paper's API).
  * While profiling is on, every kernel the table launches carries a start and
  * a stop event that its own dispatch records (hipExtLaunchKernelGGL), so no
@@ -320,7 +350,8 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
  */
 typedef struct hkv_kernel_stat {
   char name[32];      /* find, find_ptr, contains, assign, upsert_probe, probe_fetch, upsert_owner,
-                         owner_evict, upsert_serial, size, export, zero */
+                         owner_evict, evict_count, evict_write, outcomes, upsert_serial, size,
+                         export, zero */
   uint64_t launches;  /* timed launches of that kernel */
   double total_ms;    /* sum of their times */
   double max_ms;      /* longest one */

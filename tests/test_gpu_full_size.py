@@ -157,6 +157,7 @@ def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
     res = resident[torch.randperm(resident.numel(), generator=rng)[: int(0.9 * batch)].to(dev())]
     new = gen.unique_keys(seed, 1, cursor, batch - res.numel(), device=dev())
     uk = gen.shuffle(torch.cat([res, new]), seed, 9)
+    tab.count_outcomes()
     tab.insert_or_assign(uk, gen.values(uk, step, D), torch.full((batch,), step, dtype=torch.int64, device=dev()))
     allk2 = torch.cat([allk, new])
     alls2 = torch.cat([alls, torch.full((new.numel(),), step, dtype=torch.int64, device=dev())])
@@ -164,7 +165,13 @@ def test_lambda_sweep_table_at_full_size(lam, cap_log2, D):
     o2 = torch.argsort(allk2)
     sk2, ss2 = allk2[o2], alls2[o2].clone()
     ss2[torch.searchsorted(sk2, res)] = step
-    check(sk2, ss2)
+    resident2 = check(sk2, ss2)
+    # the step's outcome counts, from the closed form's states before and after
+    want = {"updated": res.numel(), "inserted": int((~torch.isin(resident2, resident)).sum()),
+            "evicted": int((~torch.isin(resident, resident2)).sum()),
+            "rejected": int((~torch.isin(new, resident2)).sum())}
+    assert tab.outcomes() == want
+    log(f"lambda {lam}, 2^{cap_log2} slots: upsert step outcomes {want}")
     tab.close()
 
 

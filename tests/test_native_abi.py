@@ -23,7 +23,8 @@ def test_header_declares_the_abi():
     assert names == sorted([
         "hkv_create", "hkv_destroy", "hkv_get_options", "hkv_find", "hkv_find_ptr", "hkv_contains",
         "hkv_insert_or_assign", "hkv_insert_or_assign_noalloc", "hkv_insert_and_evict", "hkv_find_or_insert", "hkv_assign", "hkv_size",
-        "hkv_export_batch", "hkv_profile_start", "hkv_profile_stop", "hkv_last_error"])
+        "hkv_export_batch", "hkv_set_outcome_counters", "hkv_profile_start", "hkv_profile_stop",
+        "hkv_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -102,6 +103,7 @@ def test_null_arguments():
     assert L.hkv_find_or_insert(None, 1, None, None, None, None, None) == _native.HKV_EINVAL
     out = ctypes.c_uint64()
     assert L.hkv_size(None, ctypes.byref(out), None) == _native.HKV_EINVAL
+    assert L.hkv_set_outcome_counters(None, None) == _native.HKV_EINVAL
     assert L.hkv_profile_start(None) == _native.HKV_EINVAL
     cnt = ctypes.c_uint32()
     assert L.hkv_profile_stop(None, None, 0, ctypes.byref(cnt)) == _native.HKV_EINVAL
