@@ -151,25 +151,30 @@ __device__ __forceinline__ void copy_row(float* __restrict__ dst, const float* _
   }
 }
 
-// A row of at most one 16-byte piece per lane (dim <= 4*G) held in the
+// A row of at most P 16-byte pieces per lane (dim <= 4*G*P) held in the
 // registers of the G lanes of a group, so that its load can be issued before
 // a decision that its store waits for.
-template <int G>
+template <int G, int P = 1>
 struct GroupRow {
-  f32x4 v;
+  f32x4 v[P];
 };
 
-template <int G>
-__device__ __forceinline__ void group_row_load(GroupRow<G>& r, const float* __restrict__ src, uint32_t dim,
+template <int G, int P>
+__device__ __forceinline__ void group_row_load(GroupRow<G, P>& r, const float* __restrict__ src, uint32_t dim,
                                                int lane) {
-  if (static_cast<uint32_t>(lane) < (dim >> 2))
-    r.v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + lane);
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+    if (static_cast<uint32_t>(lane + q * G) < (dim >> 2))
+      r.v[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + lane + q * G);
 }
 
-template <int G>
-__device__ __forceinline__ void group_row_store(const GroupRow<G>& r, float* __restrict__ dst, uint32_t dim,
+template <int G, int P>
+__device__ __forceinline__ void group_row_store(const GroupRow<G, P>& r, float* __restrict__ dst, uint32_t dim,
                                                 int lane) {
-  if (static_cast<uint32_t>(lane) < (dim >> 2)) __builtin_nontemporal_store(r.v, reinterpret_cast<f32x4*>(dst) + lane);
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+    if (static_cast<uint32_t>(lane + q * G) < (dim >> 2))
+      __builtin_nontemporal_store(r.v[q], reinterpret_cast<f32x4*>(dst) + lane + q * G);
 }
 
 // Takes slot p's claim bit for this call; true for the first taker only.
@@ -1016,17 +1021,25 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
     } else {
       // In-place update. Occurrences of one key in a batch would otherwise
       // write its row piece by piece at once; the slot's claim bit lets the
-      // first one alone write the row and the score.
+      // first one alone write the row and the score. A row of up to two
+      // pieces per lane is loaded while the claim is in flight (one round
+      // trip for both).
       const float* src = values + i * t.dim;
       float* dst = row_of(t, static_cast<uint64_t>(p));
       uint32_t won = 1;
+      const bool pair = V4 && !in_regs && t.claims && t.dim <= 8 * G;
+      GroupRow<G, 2> r2;
       if (t.claims) {
-        if (lane == 0) won = claim_slot(t, static_cast<uint64_t>(p)) ? 1u : 0u;
-        won = __shfl(won, 0, G);
+        uint32_t mine = 0;
+        if (lane == 0) mine = claim_slot(t, static_cast<uint64_t>(p)) ? 1u : 0u;
+        if (pair) group_row_load<G, 2>(r2, src, t.dim, lane);
+        won = __shfl(mine, 0, G);
       }
       if (won) {
         if (in_regs) {
           group_row_store<G>(rr, dst, t.dim, lane);
+        } else if (pair) {
+          group_row_store<G, 2>(r2, dst, t.dim, lane);
         } else {
           copy_row<G, V4, NT>(dst, src, t.dim, lane);
         }
