@@ -130,7 +130,9 @@ def kernel_code_sha256() -> str:
 
 
 def profiled_traffic(kernel: str, dim: int, capacity_log2: int):
-    """HBM bytes per launch of `kernel` from a committed rocprofv3 summary of
+    """Bytes per launch of `kernel` between the L2s and the data fabric
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counters;
+    Infinity Cache hits included) from a committed rocprofv3 summary of
     this workload, or None when no summary matches the current kernel code."""
     import glob
 
