@@ -13,6 +13,8 @@
 #include <atomic>
 #include <chrono>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -33,10 +35,35 @@ struct ThreadArgs {
   uint8_t* found;          // batch (find)
 };
 
+// The worker streams, per device, created on first use and kept for the
+// process: a table keeps the last event it recorded on each stream and
+// queries or waits on it in later calls, so the streams its calls ran on
+// stay alive (and their handles stable from one run to the next).
+std::mutex g_streams_mu;
+std::map<int, std::vector<hipStream_t>> g_streams;
+
+hipError_t worker_streams(int device, uint32_t count, std::vector<hipStream_t>* out) {
+  std::lock_guard<std::mutex> lk(g_streams_mu);
+  std::vector<hipStream_t>& v = g_streams[device];
+  int prev = -1;
+  hipError_t e = hipGetDevice(&prev);
+  if (e == hipSuccess) e = hipSetDevice(device);
+  while (e == hipSuccess && v.size() < count) {
+    hipStream_t s = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) v.push_back(s);
+  }
+  if (prev >= 0) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return e;
+  out->assign(v.begin(), v.begin() + count);
+  return hipSuccess;
+}
+
 }  // namespace
 
 // Runs `threads` host threads. Thread j issues `batches` calls of role
-// roles[j] (0 find, 1 assign, 2 insert_or_assign) on its own stream, cycling
+// roles[j] (0 find, 1 assign, 2 insert_or_assign) on stream j of the
+// driver's worker streams (created once per device and kept), cycling
 // through `pool` pre-made device batches of `batch` keys: batch b uses
 // keys[j] + (b % pool) * batch, and likewise for values and scores. find
 // writes its rows and flags to out[j] / found[j]. All threads start together;
@@ -67,6 +94,8 @@ HKV_MIXED_API hkv_status hkv_mixed_run(hkv_table* table, uint32_t threads, const
     if (roles[j] == kFind && (!args[j].out || !args[j].found)) return HKV_EINVAL;
     if (roles[j] != kFind && (!args[j].values || !args[j].scores)) return HKV_EINVAL;
   }
+  std::vector<hipStream_t> streams;
+  if (worker_streams(opt.device, threads, &streams) != hipSuccess) return HKV_EHIP;
   std::atomic<uint32_t> ready{0};
   std::atomic<bool> go{false};
   std::vector<hkv_status> result(threads, HKV_OK);
@@ -75,8 +104,8 @@ HKV_MIXED_API hkv_status hkv_mixed_run(hkv_table* table, uint32_t threads, const
   for (uint32_t j = 0; j < threads; ++j) {
     pool_threads.emplace_back([&, j]() {
       const ThreadArgs& a = args[j];
-      hipStream_t s = nullptr;
-      if (hipSetDevice(opt.device) != hipSuccess || hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+      const hipStream_t s = streams[j];
+      if (hipSetDevice(opt.device) != hipSuccess) {
         result[j] = HKV_EHIP;
         ready.fetch_add(1);
         return;
@@ -98,7 +127,6 @@ HKV_MIXED_API hkv_status hkv_mixed_run(hkv_table* table, uint32_t threads, const
         }
       }
       if (hipStreamSynchronize(s) != hipSuccess && result[j] == HKV_OK) result[j] = HKV_EHIP;
-      (void)hipStreamDestroy(s);
     });
   }
   while (ready.load() < threads) std::this_thread::yield();

@@ -39,6 +39,11 @@
  *     from a single stream they record no events (stream order suffices), so
  *     the first call from a second stream waits once for the device
  *     (hipDeviceSynchronize). Several host threads may call concurrently.
+ *     The table keeps the last event it recorded on each stream, and later
+ *     calls from other streams query or wait on it; so a stream that has
+ *     carried calls on the table must not be destroyed while another thread
+ *     is inside a call on that table (destroy it once those calls have
+ *     returned).
  *   - The calls may be captured into a HIP graph when every call on the table
  *     is issued on the capturing stream and, for each inserter call captured,
  *     a call of the same kind with at least as many keys ran before the
