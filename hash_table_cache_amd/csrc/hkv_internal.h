@@ -21,7 +21,8 @@ struct TableView {
   uint32_t* occ;      // [nb]  occupied slots; slots [0, occ) are the occupied ones
   uint64_t* head;     // [nb]  inserter chain heads: low word the batch index last
                       // pushed, high word the epoch of the call that pushed it; a
-                      // head of another epoch is an empty chain (never reset)
+                      // head of another epoch is an empty chain (reset only by
+                      // calls captured into a graph, which run at epoch 0)
   uint64_t* bmin;     // [2*nb] dual mode: lowest (score, key) of each full bucket
                       // as its last owner left it; key ~0 = not known
   uint32_t* claim;    // [nb*4] one bit per slot (bit p%32 of word p/32): taken by the
@@ -37,7 +38,8 @@ struct TableView {
   uint32_t keys_per_group;  // keys each group of the key-side probes serves (1, 2 or 4)
   uint32_t claims;    // inserters claim slots they update in place (0: the caller
                       // promised distinct keys per write batch)
-  uint32_t epoch;     // this inserter call's epoch (1 .. 2^32-1; 0 marks no call)
+  uint32_t epoch;     // this inserter call's epoch (1 .. 2^32-1; 0 for calls
+                      // captured into a graph)
 };
 
 // Optional per-kernel timing: when a timer is passed, each kernel is launched
@@ -57,7 +59,8 @@ struct KernelTimer {
 
 hipError_t launch_init(const TableView& t, hipStream_t s);
 
-// Sets every chain head to epoch 0 (no call), when the epoch counter wraps.
+// Sets every chain head to the empty head (epoch 0, no index), when the
+// epoch counter wraps.
 hipError_t launch_reset_heads(const TableView& t, hipStream_t s);
 
 // Device address, on the current device, of the library's fixed scratch array

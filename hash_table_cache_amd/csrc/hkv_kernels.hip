@@ -46,6 +46,9 @@ namespace {
 constexpr int kSlots = 128;
 constexpr uint64_t kLockedKey = ~0ull - 1;  // keys >= this are reserved
 constexpr uint32_t kNoIdx = 0xFFFFFFFFu;    // chain end / empty chain head
+// A chain head word: (epoch << 32) | batch index. This one is empty under
+// every epoch: epoch 0 with no index.
+constexpr uint64_t kEmptyHead = kNoIdx;
 constexpr uint32_t kSkipIdx = 0xFFFFFFFEu;  // key takes no part in the insert
 constexpr uint32_t kUpdIdx = 0xFFFFFFFCu;   // resident key updated (or its row read by
                                             // find_or_insert) with no claim to release
@@ -1079,7 +1082,8 @@ __global__ __launch_bounds__(kBlock) void upsert_probe_kernel(TableView t, uint6
   }
   target[i] = tb | (tocc >= kSlots ? kFullBit : 0u);
   // the head carries this call's epoch, so a head left by an earlier call
-  // reads as an empty chain and no kernel has to reset it
+  // reads as an empty chain and no kernel has to reset it (epoch 0, the
+  // epoch of calls captured into a graph, whose owners reset their heads)
   const uint64_t old = __hip_atomic_exchange(t.head + tb, (static_cast<uint64_t>(t.epoch) << 32) | i,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   next[i] = static_cast<uint32_t>(old >> 32) == t.epoch ? static_cast<uint32_t>(old) : kNoIdx;
@@ -1333,8 +1337,13 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     o.wmask = 0;
     // The head was set by the probe kernel's exchanges (this call's epoch,
     // as the bucket has an owner) and is published by the kernel boundary.
+    // A call replayed from a graph runs with the epoch it was captured with
+    // (0), so its owners reset the heads they used for the next replay.
     uint32_t head = 0;
-    if (lane == 0) head = static_cast<uint32_t>(t.head[o.b]);
+    if (lane == 0) {
+      head = static_cast<uint32_t>(t.head[o.b]);
+      if (t.epoch == 0) t.head[o.b] = kEmptyHead;
+    }
     const uint2 dv = *reinterpret_cast<const uint2*>(t.digests + static_cast<uint64_t>(o.b) * kSlots + lane * 8);
     RowRegs rr;
     const float* row = values + static_cast<uint64_t>(i) * t.dim;
@@ -1624,7 +1633,7 @@ __global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
     if (p < t.nb * 4) t.claim[p] = 0;
     if (p < t.nb) {
       t.occ[p] = 0;
-      t.head[p] = 0;
+      t.head[p] = kEmptyHead;
       if (t.bmin) {
         t.bmin[2 * p] = 0;
         t.bmin[2 * p + 1] = ~0ull;
@@ -1635,7 +1644,8 @@ __global__ __launch_bounds__(kBlock) void init_kernel(TableView t) {
 
 __global__ __launch_bounds__(kBlock) void reset_heads_kernel(TableView t) {
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; b < t.nb; b += stride) t.head[b] = 0;
+  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; b < t.nb; b += stride)
+    t.head[b] = kEmptyHead;
 }
 
 uint32_t grid_for(uint64_t threads) {

@@ -104,12 +104,14 @@ class Profiler final : public hkv::KernelTimer {
   void give_back(hipEvent_t e) { pool_.push_back(e); }
   // Creates events until the pool holds `count`, and records each new one
   // once (on a private stream, waited for), so that no event is created or
-  // used for the first time while launches are being timed.
+  // used for the first time while launches are being timed. The stream
+  // lives as long as the events: an event keeps a reference to the stream
+  // it was last recorded on, which later synchronization on it consults.
   void prewarm(size_t count) {
     if (pool_.size() >= count) return;
-    hipStream_t s = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    if (!warm_ && hipStreamCreateWithFlags(&warm_, hipStreamNonBlocking) != hipSuccess) {
       (void)hipGetLastError();
+      warm_ = nullptr;
       return;
     }
     while (pool_.size() < count) {
@@ -118,11 +120,10 @@ class Profiler final : public hkv::KernelTimer {
         (void)hipGetLastError();
         break;
       }
-      (void)hipEventRecord(e, s);
+      (void)hipEventRecord(e, warm_);
       pool_.push_back(e);
     }
-    (void)hipStreamSynchronize(s);
-    (void)hipStreamDestroy(s);
+    (void)hipStreamSynchronize(warm_);
   }
   void destroy_all() {
     for (auto& r : recs_) {
@@ -132,6 +133,8 @@ class Profiler final : public hkv::KernelTimer {
     for (auto e : pool_) (void)hipEventDestroy(e);
     recs_.clear();
     pool_.clear();
+    if (warm_) (void)hipStreamDestroy(warm_);
+    warm_ = nullptr;
   }
 
  private:
@@ -147,6 +150,7 @@ class Profiler final : public hkv::KernelTimer {
   }
   std::vector<Rec> recs_;
   std::vector<hipEvent_t> pool_;
+  hipStream_t warm_ = nullptr;  // the prewarm records' stream (kept with the pool)
 };
 
 }  // namespace
@@ -442,12 +446,25 @@ static hkv_status run_inserter(hkv_table* t, uint64_t n, hkv::InsertCall c, bool
   if ((st = order_before(t, kInserter, stream)) != HKV_OK) return st;
   // A new epoch per call: chain heads of earlier calls then read as empty.
   // After 2^32 - 1 calls the counter wraps and every head is reset first.
-  if (++t->view.epoch == 0) {
-    const hipError_t er = hkv::launch_reset_heads(t->view, stream);
-    if (er != hipSuccess) return fail_hip(er, what);
-    t->view.epoch = 1;
+  // A call captured into a graph is replayed with the arguments it was
+  // captured with, so it runs at epoch 0, whose owners reset their heads.
+  hkv::TableView v = t->view;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    cs = hipStreamCaptureStatusNone;
   }
-  const hipError_t e = hkv::launch_upsert(t->view, n, c, ws_next, ws_target, vec4, serial, stream, t->timer());
+  if (cs == hipStreamCaptureStatusActive) {
+    v.epoch = 0;
+  } else {
+    if (++t->view.epoch == 0) {
+      const hipError_t er = hkv::launch_reset_heads(t->view, stream);
+      if (er != hipSuccess) return fail_hip(er, what);
+      t->view.epoch = 1;
+    }
+    v.epoch = t->view.epoch;
+  }
+  const hipError_t e = hkv::launch_upsert(v, n, c, ws_next, ws_target, vec4, serial, stream, t->timer());
   if (e != hipSuccess) return fail_hip(e, what);
   return record_after(t, kInserter, stream);
 }
@@ -513,8 +530,8 @@ HKV_API hkv_status hkv_create(const hkv_options* o, hkv_table** out) {
   if (const char* g = std::getenv("HKV_GROUP_LANES")) v.lanes = static_cast<uint32_t>(std::atoi(g));
   v.keys_per_group = 2;
   if (const char* g = std::getenv("HKV_KEYS_PER_GROUP")) v.keys_per_group = static_cast<uint32_t>(std::atoi(g));
-  // Inserter-call counter (the first call takes epoch 1); a start value lets
-  // tests reach its wrap.
+  // Inserter-call counter (the first eager call takes epoch 1; 0 is kept for
+  // captured calls); a start value lets tests reach its wrap.
   v.epoch = 0;
   if (const char* g = std::getenv("HKV_EPOCH_START")) v.epoch = static_cast<uint32_t>(std::strtoul(g, nullptr, 0));
   bool ok = hipMalloc(&v.digests, cap) == hipSuccess && hipMalloc(&v.keys, cap * 8) == hipSuccess &&

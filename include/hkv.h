@@ -40,10 +40,11 @@
  *     the first call from a second stream waits once for the device
  *     (hipDeviceSynchronize). Several host threads may call concurrently.
  *     The table keeps the last event it recorded on each stream, and later
- *     calls from other streams query or wait on it; so a stream that has
- *     carried calls on the table must not be destroyed while another thread
- *     is inside a call on that table (destroy it once those calls have
- *     returned).
+ *     calls from other streams query or wait on it; an event refers to the
+ *     stream it was recorded on, so a stream that has carried calls on a
+ *     table used from several streams must stay alive until the table is
+ *     destroyed (likewise the streams of calls timed by hkv_profile_start,
+ *     until hkv_profile_stop).
  *   - The calls may be captured into a HIP graph when every call on the table
  *     is issued on the capturing stream and, for each inserter call captured,
  *     a call of the same kind with at least as many keys ran before the
@@ -61,8 +62,9 @@
  *     the default chosen from dim). HKV_KEYS_PER_GROUP: keys each group serves
  *     in the key-side probes of hkv_find_ptr and hkv_contains (1, 2 or 4;
  *     default 2). A third, HKV_EPOCH_START, sets the table's inserter-call
- *     counter (it tags the chain heads and wraps after 2^32 - 1 calls) to a
- *     start value, so that tests can reach the wrap quickly.
+ *     counter (it tags the chain heads and wraps after 2^32 - 1 calls; calls
+ *     captured into a graph use epoch 0 instead) to a start value, so that
+ *     tests can reach the wrap quickly.
  */
 #ifndef HKV_H_
 #define HKV_H_

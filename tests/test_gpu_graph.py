@@ -3,7 +3,8 @@ batches avoid per-call launch costs). Capture works when every call of the
 table is issued on the capturing stream (a table used from one stream records
 no events) and the inserter workspace was sized by an eager call of the same
 batch size before capture (capture cannot allocate). Every replay is checked
-against the oracle, with eager work and synchronizations between replays."""
+against the oracle, with eager work (inserts among it) and synchronizations
+between replays."""
 
 import numpy as np
 import pytest
@@ -69,4 +70,18 @@ def test_find_and_insert_or_assign_replay_from_a_graph():
             assert np.array_equal(out.cpu().numpy()[hit].view(np.uint32), ov[hit].view(np.uint32))
             o.insert_or_assign(u, np.full(n, step, np.uint64), values=uv.cpu().numpy())
             assert_same_contents(tab, o)
+            if r % 2 == 0:
+                # an eager insert between replays: eager calls tag the chain
+                # heads with a fresh epoch, replays run at the captured one
+                step += 1
+                e_res = sample_present(o, n // 4, 300 + r)
+                e_new = np_u64(gen.unique_keys(seed, 1, cursor, n - e_res.size))
+                cursor += e_new.size
+                ek = to_dev(np.concatenate([e_res, e_new]))
+                ev = gen.values(ek, step, D)
+                es = torch.full((n,), step, dtype=torch.int64, device=dev())
+                tab.insert_or_assign(ek, ev, es, stream=s)
+                s.synchronize()
+                o.insert_or_assign(np_u64(ek), np_u64(es), values=ev.cpu().numpy())
+                assert_same_contents(tab, o)
     tab.close()
