@@ -306,8 +306,10 @@ __device__ __forceinline__ uint32_t line_occupancy(const uint32_t (&w)[NW]) {
 }
 
 // Group-wide probe of the key's candidate bucket(s). Returns the hit position
-// (same value in every lane of the group) or -1. When occ1/occ2 are given they
-// receive the occupancy of the first / second candidate bucket.
+// (same value in every lane of the group) or -1. In dual mode the second
+// bucket's line is read only when the first bucket does not hold the key. When
+// occ1/occ2 are given they receive, for a key that is not found, the
+// occupancy of the first / second candidate bucket.
 template <int G, bool DUAL>
 __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane, uint32_t* occ1 = nullptr,
                                          uint32_t* occ2 = nullptr) {
@@ -317,70 +319,78 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
   const uint32_t b1 = bucket_of(t, h);
   uint32_t w1[NW];
   load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
-  uint32_t b2 = b1;
-  uint32_t w2[NW];
-  if constexpr (DUAL) {
-    b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
-    if (b2 != b1) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
-  }
+  const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
   int64_t hit = -1;
-  if (!is_reserved(k)) {
-    const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
-    const uint32_t m1 = candidate_mask<NW>(w1, pat);
-    uint32_t m2 = 0;
-    if constexpr (DUAL) {
-      if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
-    }
-    hit = match_candidates(t.keys, k, m1, static_cast<uint64_t>(b1) * kSlots + off, m2,
-                               static_cast<uint64_t>(b2) * kSlots + off);
-  }
+  const bool rsv = is_reserved(k);
+  if (!rsv) hit = match_candidates(t.keys, k, candidate_mask<NW>(w1, pat), static_cast<uint64_t>(b1) * kSlots + off, 0, 0);
+  uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (occ1) *occ1 = line_occupancy<G, NW>(w1);
   if constexpr (DUAL) {
-    if (occ2) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
+    // the second bucket only when the first does not hold the key
+    const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+    if (occ2) *occ2 = 0;
+    if (bits == 0 && b2 != b1) {
+      uint32_t w2[NW];
+      load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
+      if (!rsv) hit = match_candidates(t.keys, k, candidate_mask<NW>(w2, pat), static_cast<uint64_t>(b2) * kSlots + off, 0, 0);
+      bits = group_bits<G>(__ballot(hit >= 0));
+      if (occ2) *occ2 = line_occupancy<G, NW>(w2);
+    }
   }
-  const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (bits == 0) return -1;
   return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
 }
 
 // probe() for K keys per group with their memory round trips overlapped: all
 // K digest lines are requested before any is used, then all K keys'
-// candidate keys. hit[j] is group-uniform.
+// candidate keys (in dual mode, then the same for the second buckets of the
+// keys their first bucket does not hold). hit[j] is group-uniform.
 template <int G, bool DUAL, int K>
 __device__ __forceinline__ void probe_many(const TableView& t, const uint64_t (&k)[K], int lane,
                                            int64_t (&hit)[K]) {
   constexpr int NW = kSlots / G / 4;
-  uint32_t w1[K][NW], w2[K][NW];
-  uint32_t b1[K], b2[K], pat[K];
+  uint32_t w[K][NW];
+  uint32_t b1[K], pat[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const uint64_t h = fmix64(k[j]);
     pat[j] = digest_of(h) * 0x01010101u;
     b1[j] = bucket_of(t, h);
-    b2[j] = b1[j];
-    load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1[j]) * kSlots, lane, w1[j]);
-    if constexpr (DUAL) {
-      b2[j] = bucket_of(t, fmix64(k[j] ^ kSecondSalt));
-      if (b2[j] != b1[j]) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2[j]) * kSlots, lane, w2[j]);
-    }
+    load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1[j]) * kSlots, lane, w[j]);
   }
   const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
   Cand c[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    uint32_t m1 = is_reserved(k[j]) ? 0u : candidate_mask<NW>(w1[j], pat[j]);
-    uint32_t m2 = 0;
-    if constexpr (DUAL) {
-      if (b2[j] != b1[j] && !is_reserved(k[j])) m2 = candidate_mask<NW>(w2[j], pat[j]);
-    }
-    cand_issue(c[j], t.keys, m1, static_cast<uint64_t>(b1[j]) * kSlots + off, m2,
-                     static_cast<uint64_t>(b2[j]) * kSlots + off);
-  }
+  for (int j = 0; j < K; ++j)
+    cand_issue(c[j], t.keys, is_reserved(k[j]) ? 0u : candidate_mask<NW>(w[j], pat[j]),
+               static_cast<uint64_t>(b1[j]) * kSlots + off, 0, 0);
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const int64_t hj = cand_finish(c[j], t.keys, k[j]);
     const uint64_t bits = group_bits<G>(__ballot(hj >= 0));
     hit[j] = bits == 0 ? -1 : __shfl(hj, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
+  }
+  if constexpr (DUAL) {
+    // the second buckets of the keys their first bucket does not hold, again
+    // with every key's loads in flight together
+    uint32_t b2[K];
+    bool second[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      b2[j] = bucket_of(t, fmix64(k[j] ^ kSecondSalt));
+      second[j] = hit[j] < 0 && b2[j] != b1[j] && !is_reserved(k[j]);
+      if (second[j]) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2[j]) * kSlots, lane, w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (second[j]) cand_issue(c[j], t.keys, candidate_mask<NW>(w[j], pat[j]), static_cast<uint64_t>(b2[j]) * kSlots + off, 0, 0);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (!second[j]) continue;
+      const int64_t hj = cand_finish(c[j], t.keys, k[j]);
+      const uint64_t bits = group_bits<G>(__ballot(hj >= 0));
+      hit[j] = bits == 0 ? -1 : __shfl(hj, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
+    }
   }
 }
 
@@ -398,28 +408,31 @@ __device__ __forceinline__ int64_t probe_prefetch(const TableView& t, uint64_t k
   const uint32_t b1 = bucket_of(t, h);
   uint32_t w1[NW];
   load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
-  uint32_t b2 = b1;
-  uint32_t w2[NW];
-  if constexpr (DUAL) {
-    b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
-    if (b2 != b1) load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
-  }
   const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
-  const uint32_t m1 = candidate_mask<NW>(w1, pat);
-  uint32_t m2 = 0;
-  if constexpr (DUAL) {
-    if (b2 != b1) m2 = candidate_mask<NW>(w2, pat);
-  }
   Cand c;
-  cand_issue(c, t.keys, m1, static_cast<uint64_t>(b1) * kSlots + off, m2, static_cast<uint64_t>(b2) * kSlots + off);
+  cand_issue(c, t.keys, candidate_mask<NW>(w1, pat), static_cast<uint64_t>(b1) * kSlots + off, 0, 0);
   if (load_row && group_bits<G>(__ballot(c.h0)) != 0) group_row_load<G>(rr, src, t.dim, lane);
-  const int64_t hit = cand_finish(c, t.keys, k);
-  const uint64_t bits = group_bits<G>(__ballot(hit >= 0));
+  int64_t hit = cand_finish(c, t.keys, k);
+  uint64_t bits = group_bits<G>(__ballot(hit >= 0));
+  if constexpr (DUAL) {
+    // the second bucket only when the first does not hold the key
+    const uint32_t b2 = bucket_of(t, fmix64(k ^ kSecondSalt));
+    *occ2 = 0;
+    if (bits == 0 && b2 != b1) {
+      uint32_t w2[NW];
+      load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
+      Cand c2;
+      cand_issue(c2, t.keys, candidate_mask<NW>(w2, pat), static_cast<uint64_t>(b2) * kSlots + off, 0, 0);
+      if (load_row && group_bits<G>(__ballot(c2.h0)) != 0) group_row_load<G>(rr, src, t.dim, lane);
+      hit = cand_finish(c2, t.keys, k);
+      bits = group_bits<G>(__ballot(hit >= 0));
+      if (bits == 0) *occ2 = line_occupancy<G, NW>(w2);
+    }
+  }
   if (bits == 0) {
     // a miss: the occupancies choose its bucket (the result is group-uniform,
     // so the whole group takes this branch together)
     *occ1 = line_occupancy<G, NW>(w1);
-    if constexpr (DUAL) *occ2 = (b2 != b1) ? line_occupancy<G, NW>(w2) : 0u;
     return -1;
   }
   return __shfl(hit, __ffsll(static_cast<unsigned long long>(bits)) - 1, G);
