@@ -85,3 +85,98 @@ def test_find_and_insert_or_assign_replay_from_a_graph():
                 o.insert_or_assign(np_u64(ek), np_u64(es), values=ev.cpu().numpy())
                 assert_same_contents(tab, o)
     tab.close()
+
+
+def _graph_batches(o, n, r, cursor, seed, D, step):
+    """A replay's insert batch: a quarter resident keys, the rest new."""
+    res = sample_present(o, n // 4, 500 + r)
+    new = np_u64(gen.unique_keys(seed, 1, cursor, n - res.size))
+    return np.concatenate([res, new]), cursor + new.size
+
+
+def test_captured_insert_with_outcome_counts():
+    """insert_or_assign captured with the outcome counters on: every replay
+    leaves the oracle's contents and adds that call's counts (set
+    differences of the oracle's states before and after)."""
+    H = hkv()
+    C, D, n = 32 * SLOTS, 8, 2048
+    seed = 0x484B56000000C4AA
+    s = torch.cuda.Stream()
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    uk = torch.empty(n, dtype=torch.int64, device=dev())
+    uv = torch.empty((n, D), dtype=torch.float32, device=dev())
+    us = torch.empty(n, dtype=torch.int64, device=dev())
+    with torch.cuda.stream(s):
+        step, cursor = 0, 0
+        for j in range(2):  # eager fill (sizes the workspace for n keys)
+            step += 1
+            k = gen.unique_keys(seed, 1, cursor, n, device=dev())
+            cursor += n
+            v = gen.values(k, step, D)
+            sc = torch.full((n,), step, dtype=torch.int64, device=dev())
+            tab.insert_or_assign(k, v, sc, stream=s)
+            o.insert_or_assign(np_u64(k), np_u64(sc), values=v.cpu().numpy())
+        s.synchronize()
+        tab.count_outcomes()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            tab.insert_or_assign(uk, uv, us, stream=s)
+        was = tab.outcomes()
+        for r in range(3):
+            step += 1
+            u, cursor = _graph_batches(o, n, r, cursor, seed, D, step)
+            before = set(o.export()["keys"].tolist())
+            uk.copy_(to_dev(u))
+            uv.copy_(gen.values(uk, step, D))
+            us.fill_(step)
+            g.replay()
+            s.synchronize()
+            o.insert_or_assign(u, np.full(n, step, np.uint64), values=uv.cpu().numpy())
+            assert_same_contents(tab, o)
+            after = set(o.export()["keys"].tolist())
+            b = set(u.tolist())
+            now = tab.outcomes()
+            assert {k: now[k] - was[k] for k in now} == {
+                "updated": len(b & before), "inserted": len(after - before),
+                "evicted": len(before - after), "rejected": len(b - before - after)}
+            was = now
+    tab.close()
+
+
+def test_noalloc_insert_replays_from_a_graph():
+    """The entry point that allocates nothing, captured with no eager
+    inserter call before it (it needs no workspace) and replayed four times
+    with fresh inputs, each replay equal to the oracle."""
+    from hash_table_cache_amd import _native
+
+    H = hkv()
+    C, D, n = 32 * SLOTS, 16, 2048
+    seed = 0x484B56000000C4AB
+    s = torch.cuda.Stream()
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    uk = torch.empty(n, dtype=torch.int64, device=dev())
+    uv = torch.empty((n, D), dtype=torch.float32, device=dev())
+    us = torch.empty(n, dtype=torch.int64, device=dev())
+    L = _native.load()
+    with torch.cuda.stream(s):
+        uk.zero_()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            st = L.hkv_insert_or_assign_noalloc(tab.handle, n, uk.data_ptr(), uv.data_ptr(), us.data_ptr(),
+                                                s.cuda_stream)
+        assert st == _native.HKV_OK, L.hkv_last_error().decode()
+        step, cursor = 0, 0
+        for r in range(4):
+            step += 1
+            u, cursor = _graph_batches(o, n, r, cursor, seed, D, step)
+            uk.copy_(to_dev(u))
+            uv.copy_(gen.values(uk, step, D))
+            us.fill_(step)
+            g.replay()
+            s.synchronize()
+            o.insert_or_assign(u, np.full(n, step, np.uint64), values=uv.cpu().numpy())
+            assert_same_contents(tab, o)
+    tab.close()
