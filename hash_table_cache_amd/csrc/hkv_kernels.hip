@@ -1276,17 +1276,22 @@ __device__ __forceinline__ bool bucket_apply(Bucket& o, const TableView& t, uint
 
 // Insert, second kernel: the first-pushed key of each chain (next ==
 // kNoIdx) owns that bucket for the whole kernel. A block lists the owners
-// among its 256 keys in LDS and deals them out to its 16-lane groups in turn.
-// An owner loads, in one round trip, the bucket's
-// digest line, the chain head, its key's row and - when the probe kernel saw
-// the bucket full - the scores of all slots; it applies its own key, then the
-// chain from its head down to itself (Algorithm 2, each chain key costing one
-// round trip for its inputs), writes the occupancy and resets the chain head.
-// With distinct keys any order within a chain gives the same bucket contents.
+// among its kOwnerBlock keys in LDS and deals them out to its 16-lane groups
+// in turn. An owner loads, in one round trip, the bucket's digest line, the
+// chain head, its key's row and - when the probe kernel saw the bucket full -
+// the scores of all slots; it applies its own key, then the chain from its
+// head down to itself (Algorithm 2, each chain key costing one round trip for
+// its inputs), and writes the occupancy if it changed. With distinct keys any
+// order within a chain gives the same bucket contents. The kernel waits on
+// memory more than anything else; blocks of 128 threads (two waves) gave
+// 43 us per 2^20 keys of the 10 %-new mix against 46 us with 256 (a block
+// waits at its barrier for its slowest wave) and 55 us with 512.
 // STATS: the block's outcome counts (updated, inserted, evicted, rejected)
 // are added to stat_slots[c * kStatSlots + block mod kStatSlots].
+constexpr int kOwnerBlock = 128;
+
 template <bool V4, bool DUAL, bool EVICT, bool STATS>
-__global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint64_t n,
+__global__ __launch_bounds__(kOwnerBlock) void upsert_owner_kernel(TableView t, uint64_t n,
                                                               const uint64_t* __restrict__ keys,
                                                               const float* __restrict__ values,
                                                               const uint64_t* __restrict__ scores,
@@ -1295,15 +1300,15 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
                                                               EvictStage st, bool clear_all,
                                                               unsigned long long* __restrict__ stat_slots) {
   // The block's owners (keys with next == kNoIdx) are listed in LDS and dealt
-  // out to its 16 groups in turn, so that every group serves about the same
+  // out to its groups in turn, so that every group serves about the same
   // number of buckets.
-  __shared__ uint32_t s_idx[kBlock];
-  __shared__ uint32_t s_tgt[kBlock];
-  __shared__ uint64_t s_key[kBlock];
-  __shared__ uint64_t s_score[kBlock];
+  __shared__ uint32_t s_idx[kOwnerBlock];
+  __shared__ uint32_t s_tgt[kOwnerBlock];
+  __shared__ uint64_t s_key[kOwnerBlock];
+  __shared__ uint64_t s_score[kOwnerBlock];
   __shared__ uint32_t s_count;
   __shared__ uint32_t s_stat[4];
-  const uint64_t mine = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const uint64_t mine = static_cast<uint64_t>(blockIdx.x) * kOwnerBlock + threadIdx.x;
   const int lane = static_cast<int>(threadIdx.x & (kInsG - 1));
   if (threadIdx.x == 0) s_count = 0;
   if (STATS && threadIdx.x < 4) s_stat[threadIdx.x] = 0;
@@ -1333,12 +1338,12 @@ __global__ __launch_bounds__(kBlock) void upsert_owner_kernel(TableView t, uint6
     const uint64_t per = (t.nb + gridDim.x - 1) / gridDim.x;
     const uint64_t b0 = static_cast<uint64_t>(blockIdx.x) * per;
     const uint64_t b1 = b0 + per < t.nb ? b0 + per : t.nb;
-    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kBlock) clear_claims(t, static_cast<uint32_t>(b));
+    for (uint64_t b = b0 + threadIdx.x; b < b1; b += kOwnerBlock) clear_claims(t, static_cast<uint32_t>(b));
   }
   __syncthreads();
   const uint32_t owners = s_count;
   const bool in_regs = V4 && t.dim <= 8 * kInsG;
-  for (uint32_t e = threadIdx.x / kInsG; e < owners; e += kBlock / kInsG) {
+  for (uint32_t e = threadIdx.x / kInsG; e < owners; e += kOwnerBlock / kInsG) {
     const uint32_t i = s_idx[e];
     const uint32_t tgt = s_tgt[e];
     const uint64_t k = s_key[e];
@@ -1730,12 +1735,14 @@ hipError_t owner_l(const TableView& t, uint64_t n, const InsertCall& c, const ui
   const bool clear_all = t.claims && !c.fetch && t.nb <= 4 * n;
   hipError_t e = hipSuccess;
   if (!c.ev_keys) {
-    HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false, STATS>), dim3(grid_for(n)),
-               dim3(kBlock), s, t, n, c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
+    HKV_LAUNCH(tm, "upsert_owner", (upsert_owner_kernel<V4, DUAL, false, STATS>),
+               dim3(static_cast<uint32_t>((n + kOwnerBlock - 1) / kOwnerBlock)), dim3(kOwnerBlock), s, t, n,
+               c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
-    HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true, STATS>), dim3(grid_for(n)),
-               dim3(kBlock), s, t, n, c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
+    HKV_LAUNCH(tm, "owner_evict", (upsert_owner_kernel<V4, DUAL, true, STATS>),
+               dim3(static_cast<uint32_t>((n + kOwnerBlock - 1) / kOwnerBlock)), dim3(kOwnerBlock), s, t, n,
+               c.keys, c.values, c.scores, next, target, st, clear_all, c.stat_slots);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const Evicted out{c.ev_keys, c.ev_values, c.ev_scores, c.ev_count};
     const uint32_t chunks = static_cast<uint32_t>((n + kChunk - 1) / kChunk);
