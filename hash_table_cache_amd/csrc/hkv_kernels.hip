@@ -188,17 +188,21 @@ __device__ __forceinline__ bool claim_slot(const TableView& t, uint64_t p) {
 }
 
 // Loads this lane's share (NW dwords) of a bucket's 128-byte digest line.
-template <int NW>
+// KNT: with nontemporal loads (the find over host-resident rows, whose L2s
+// are better spent on the rows that repeated keys read again).
+template <int NW, bool KNT = false>
 __device__ __forceinline__ void load_digest_words(const uint8_t* line, int lane, uint32_t (&w)[NW]) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(line) + lane * NW;
   if constexpr (NW == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = KNT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)) : *reinterpret_cast<const u32x2_t*>(p);
     w[0] = v.x;
     w[1] = v.y;
   } else {
 #pragma unroll
     for (int q = 0; q < NW; q += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + q);
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t v = KNT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + q)) : *reinterpret_cast<const u32x4_t*>(p + q);
       w[q] = v.x;
       w[q + 1] = v.y;
       w[q + 2] = v.z;
@@ -243,6 +247,7 @@ struct Cand {
   bool h0, h1;
 };
 
+template <bool KNT = false>
 __device__ __forceinline__ void cand_issue(Cand& c, const uint64_t* __restrict__ keys, uint32_t m1,
                                            uint64_t base1, uint32_t m2, uint64_t base2) {
   // candidate positions in order: the bits of m1 (over base1), then of m2
@@ -260,14 +265,15 @@ __device__ __forceinline__ void cand_issue(Cand& c, const uint64_t* __restrict__
   }
   c.k0 = 0;
   c.k1 = 0;
-  if (c.h0) c.k0 = keys[c.p0];
-  if (c.h1) c.k1 = keys[c.p1];
+  if (c.h0) c.k0 = KNT ? __builtin_nontemporal_load(keys + c.p0) : keys[c.p0];
+  if (c.h1) c.k1 = KNT ? __builtin_nontemporal_load(keys + c.p1) : keys[c.p1];
   c.m1 = m1;
   c.m2 = m2;
   c.base1 = base1;
   c.base2 = base2;
 }
 
+template <bool KNT = false>
 __device__ __forceinline__ int64_t cand_finish(Cand& c, const uint64_t* __restrict__ keys, uint64_t k) {
   int64_t hit = -1;
   if (c.h0 && c.k0 == k) hit = static_cast<int64_t>(c.p0);
@@ -275,22 +281,23 @@ __device__ __forceinline__ int64_t cand_finish(Cand& c, const uint64_t* __restri
   while (c.m1) {
     const uint64_t p = c.base1 + __builtin_ctz(c.m1);
     c.m1 &= c.m1 - 1;
-    if (keys[p] == k) hit = static_cast<int64_t>(p);
+    if ((KNT ? __builtin_nontemporal_load(keys + p) : keys[p]) == k) hit = static_cast<int64_t>(p);
   }
   while (c.m2) {
     const uint64_t p = c.base2 + __builtin_ctz(c.m2);
     c.m2 &= c.m2 - 1;
-    if (keys[p] == k) hit = static_cast<int64_t>(p);
+    if ((KNT ? __builtin_nontemporal_load(keys + p) : keys[p]) == k) hit = static_cast<int64_t>(p);
   }
   return hit;
 }
 
+template <bool KNT = false>
 __device__ __forceinline__ int64_t match_candidates(const uint64_t* __restrict__ keys, uint64_t k,
                                                     uint32_t m1, uint64_t base1, uint32_t m2,
                                                     uint64_t base2) {
   Cand c;
-  cand_issue(c, keys, m1, base1, m2, base2);
-  return cand_finish(c, keys, k);
+  cand_issue<KNT>(c, keys, m1, base1, m2, base2);
+  return cand_finish<KNT>(c, keys, k);
 }
 
 // Occupied slots counted from a group's digest words: slots fill in order and
@@ -310,7 +317,7 @@ __device__ __forceinline__ uint32_t line_occupancy(const uint32_t (&w)[NW]) {
 // bucket's line is read only when the first bucket does not hold the key. When
 // occ1/occ2 are given they receive, for a key that is not found, the
 // occupancy of the first / second candidate bucket.
-template <int G, bool DUAL>
+template <int G, bool DUAL, bool KNT = false>
 __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lane, uint32_t* occ1 = nullptr,
                                          uint32_t* occ2 = nullptr) {
   constexpr int NW = kSlots / G / 4;
@@ -318,11 +325,11 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
   const uint32_t pat = digest_of(h) * 0x01010101u;
   const uint32_t b1 = bucket_of(t, h);
   uint32_t w1[NW];
-  load_digest_words<NW>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
+  load_digest_words<NW, KNT>(t.digests + static_cast<uint64_t>(b1) * kSlots, lane, w1);
   const uint64_t off = static_cast<uint64_t>(lane) * (NW * 4);
   int64_t hit = -1;
   const bool rsv = is_reserved(k);
-  if (!rsv) hit = match_candidates(t.keys, k, candidate_mask<NW>(w1, pat), static_cast<uint64_t>(b1) * kSlots + off, 0, 0);
+  if (!rsv) hit = match_candidates<KNT>(t.keys, k, candidate_mask<NW>(w1, pat), static_cast<uint64_t>(b1) * kSlots + off, 0, 0);
   uint64_t bits = group_bits<G>(__ballot(hit >= 0));
   if (occ1) *occ1 = line_occupancy<G, NW>(w1);
   if constexpr (DUAL) {
@@ -331,8 +338,8 @@ __device__ __forceinline__ int64_t probe(const TableView& t, uint64_t k, int lan
     if (occ2) *occ2 = 0;
     if (bits == 0 && b2 != b1) {
       uint32_t w2[NW];
-      load_digest_words<NW>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
-      if (!rsv) hit = match_candidates(t.keys, k, candidate_mask<NW>(w2, pat), static_cast<uint64_t>(b2) * kSlots + off, 0, 0);
+      load_digest_words<NW, KNT>(t.digests + static_cast<uint64_t>(b2) * kSlots, lane, w2);
+      if (!rsv) hit = match_candidates<KNT>(t.keys, k, candidate_mask<NW>(w2, pat), static_cast<uint64_t>(b2) * kSlots + off, 0, 0);
       bits = group_bits<G>(__ballot(hit >= 0));
       if (occ2) *occ2 = line_occupancy<G, NW>(w2);
     }
@@ -442,11 +449,11 @@ __device__ __forceinline__ int64_t probe_prefetch(const TableView& t, uint64_t k
 
 // find for key i by the G lanes of a group (Algorithm 1): probe, then the
 // row, found flag and (optionally) score of a hit; a miss writes found = 0.
-template <int G, bool V4, bool DUAL, bool NT>
+template <int G, bool V4, bool DUAL, bool NT, bool KNT = false>
 __device__ __forceinline__ void find_one(const TableView& t, uint64_t i, uint64_t k, float* __restrict__ out,
                                          uint8_t* __restrict__ found, uint64_t* __restrict__ scores_out,
                                          int lane) {
-  const int64_t p = probe<G, DUAL>(t, k, lane);
+  const int64_t p = probe<G, DUAL, KNT>(t, k, lane);
   if (p < 0) {
     if (lane == 0) found[i] = 0;
     return;
@@ -480,7 +487,10 @@ __global__ __launch_bounds__(kBlock) void find_kernel(TableView t, uint64_t n,
   find_one<G, V4, DUAL, NT>(t, i, keys[i], out, found, scores_out, lane);
 }
 
-// find when value rows live in host memory. The XCDs of the GPU have an L2
+// find when value rows live in host memory; its key-side reads (digest lines,
+// candidate keys) are nontemporal, so that they do not push out of L2 the host
+// rows that a batch's repeated keys read again (tiered Zipf(1.2) find: 1.587
+// vs 1.615 ms per 2^20 draws). The XCDs of the GPU have an L2
 // each, and workgroups are handed to the XCDs in turn (workgroup w to XCD
 // w mod 8), so a hot key whose draws land in workgroups of several XCDs has
 // its row fetched over the host link once per XCD. Here every chunk of
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void find_xcd_kernel(TableView t, uint64_t 
   const int lane = static_cast<int>(threadIdx.x & (G - 1));
   for (uint32_t e = threadIdx.x / G; e < mine; e += kGroups) {
     const uint64_t i = c0 + s_idx[e];
-    find_one<G, V4, DUAL, NT>(t, i, keys[i], out, found, scores_out, lane);
+    find_one<G, V4, DUAL, NT, true>(t, i, keys[i], out, found, scores_out, lane);
   }
 }
 
