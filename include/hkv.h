@@ -49,7 +49,8 @@
  *     is issued on the capturing stream and, for each inserter call captured,
  *     a call of the same kind with at least as many keys ran before the
  *     capture (inserters grow their workspaces on demand, which a capture
- *     cannot do).
+ *     cannot do; hkv_insert_or_assign_noalloc needs no such call). A captured
+ *     call keeps the outcome-counter setting it was captured with.
  *   - Arguments are validated synchronously; on any error nothing is enqueued,
  *     the call returns a negative status and hkv_last_error() describes it.
  *   - n == 0 is a valid no-op. Batches are limited to n <= 2^32 - 4 keys.
