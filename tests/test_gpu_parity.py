@@ -303,6 +303,43 @@ def test_serial_insert_mode_identical_positions(dual):
     assert_same_contents(tab, o)
 
 
+def test_dual_serial_zipf_lfu_stream_identical_positions():
+    """Serial dual-bucket mode under the online workload's shape, scaled
+    down: 256 buckets, batches of 16384 Zipf(1.05) draws over 2^20 ids,
+    deduplicated, score = cumulative frequency (ties everywhere at the low
+    end), driven well past full capacity so that D2 (the lower recorded
+    minimum, ties by key) decides most inserts. Every key's slot, score and
+    row equal the oracle's (Algorithm 3 applied key by key) after every
+    batch."""
+    H = hkv()
+    C, D = 256 * SLOTS, 2
+    tab = H.HashTable(C, D, dual_bucket=True, serial_insert=True)
+    o = oracle.OracleTable(C, D, dual=True)
+    zipf = gen.Zipf(1.05, 1 << 20)
+    freq = torch.zeros((1 << 20) + 1, dtype=torch.int64, device=dev())
+    full_at = None
+    for b in range(40):
+        r = zipf.draw(0x5EED0D2, 1, b * 16384, 16384, device=dev())
+        uniq, cnt = torch.unique(r, return_counts=True)
+        freq.index_add_(0, uniq, cnt)
+        sc = freq[uniq]
+        perm = torch.from_numpy(np.random.default_rng(b).permutation(uniq.numel())).to(dev())
+        k, s2 = uniq[perm].contiguous(), sc[perm].contiguous()
+        v = gen.values(k, s2, D)
+        tab.insert_or_assign(k, v, s2)
+        o.insert_or_assign(np_u64(k), np_u64(s2), values=v.cpu().numpy())
+        gk, _, gs, gp = tab.export_batch(with_values=False)
+        e = o.export()
+        order = np.argsort(np_u64(gp))
+        assert np.array_equal(np_u64(gp)[order], e["pos"]), f"batch {b}"
+        assert np.array_equal(np_u64(gk)[order], e["keys"]), f"batch {b}"
+        assert np.array_equal(np_u64(gs)[order], e["scores"]), f"batch {b}"
+        if full_at is None and e["keys"].size == C:
+            full_at = b
+    assert full_at is not None and full_at < 10, "the stream should fill the table early"
+    assert_same_contents(tab, o)
+
+
 def test_adversarial_all_keys_one_bucket():
     H = hkv()
     C, D = 8 * SLOTS, 8
