@@ -167,8 +167,8 @@ def owner_bytes_per_key(dim: int, f: float, e: float) -> float:
 
 def launch_cv(stat) -> float:
     """Coefficient of variation of a kernel's launch times from the library's
-    (launches, total, max, min, sum of squares) record."""
-    n, tot, _, _, sq = stat
+    (launches, total, max, min, sum of squares, median) record."""
+    n, tot, _, _, sq = stat[:5]
     mean = tot / n
     var = max(0.0, sq / n - mean * mean)
     return round(var ** 0.5 / mean, 4) if mean > 0 else 0.0
@@ -1257,9 +1257,11 @@ def run_extra_ops(args, tables, batch, dim, hit):
             torch.cuda.synchronize()
             timed = ms[reps // 2 + 2:]
             t = sorted(a.elapsed_time(b) for a, b in timed)[len(timed) // 2]
-            # per kernel: average, fastest and slowest launch (a single slow
-            # launch moves the average, not the call-time median)
+            # per kernel: median, average, fastest and slowest launch (a
+            # launch whose start event was taken before its dispatch moves
+            # the average and the maximum, not the median)
             r[name] = dict(call_ms_median=round(t, 5), bkvs=round(batch / t / 1e6, 3),
+                           kernel_median_ms={k: round(v[5], 5) for k, v in ks.items()},
                            kernel_avg_ms={k: round(v[1] / v[0], 5) for k, v in ks.items()},
                            kernel_min_max_ms={k: [round(v[3], 5), round(v[2], 5)] for k, v in ks.items()})
             if name == "insert_and_evict":

@@ -175,7 +175,8 @@ class HashTable:
         hkv_profile_start(self._h)
 
     def profile_stop(self) -> dict:
-        """Stop timing; {kernel: (launches, total_ms, max_ms, min_ms, sumsq_ms2)}. Waits for the timed work."""
+        """Stop timing; {kernel: (launches, total_ms, max_ms, min_ms, sumsq_ms2, median_ms)}. Waits for the
+        timed work."""
         return hkv_profile_stop(self._h)
 
     def export_batch(self, offset: int = 0, n_slots: int | None = None, with_values: bool = True, stream=None):

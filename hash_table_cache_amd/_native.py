@@ -76,6 +76,7 @@ class HkvKernelStat(ctypes.Structure):
         ("max_ms", ctypes.c_double),
         ("min_ms", ctypes.c_double),
         ("sumsq_ms2", ctypes.c_double),
+        ("median_ms", ctypes.c_double),
     ]
 
 
@@ -308,11 +309,11 @@ def hkv_profile_start(table) -> None:
 
 
 def hkv_profile_stop(table) -> dict:
-    """Returns {kernel name: (launches, total_ms, max_ms, min_ms, sumsq_ms2)}."""
+    """Returns {kernel name: (launches, total_ms, max_ms, min_ms, sumsq_ms2, median_ms)}."""
     cap = 16
     out = (HkvKernelStat * cap)()
     count = ctypes.c_uint32(0)
     _check(load().hkv_profile_stop(table, out, cap, ctypes.byref(count)))
     return {out[j].name.decode(): (int(out[j].launches), float(out[j].total_ms), float(out[j].max_ms),
-                                   float(out[j].min_ms), float(out[j].sumsq_ms2))
+                                   float(out[j].min_ms), float(out[j].sumsq_ms2), float(out[j].median_ms))
             for j in range(min(cap, count.value))}

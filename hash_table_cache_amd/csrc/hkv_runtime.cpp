@@ -10,6 +10,7 @@
 // event recorded by each incompatible group on every other stream, then
 // records its own event. The host never blocks, and calls issued on a single
 // stream need no waits at all because stream order already serializes them.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -891,6 +892,7 @@ HKV_API hkv_status hkv_profile_stop(hkv_table* t, hkv_kernel_stat* out, uint32_t
   DeviceGuard dg(t->opt.device);
   t->profiling = false;
   std::vector<hkv_kernel_stat> agg;
+  std::vector<std::vector<float>> times;  // per entry of agg: every launch's time
   hkv_status st = HKV_OK;
   for (auto& r : t->prof.records()) {
     float ms = 0.f;
@@ -898,14 +900,21 @@ HKV_API hkv_status hkv_profile_stop(hkv_table* t, hkv_kernel_stat* out, uint32_t
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
     if (e != hipSuccess && st == HKV_OK) st = fail_hip(e, "timing event");
     hkv_kernel_stat* a = nullptr;
-    for (auto& x : agg)
-      if (std::strncmp(x.name, r.name, sizeof(x.name)) == 0) a = &x;
+    size_t ai = 0;
+    for (size_t x = 0; x < agg.size(); ++x)
+      if (std::strncmp(agg[x].name, r.name, sizeof(agg[x].name)) == 0) {
+        a = &agg[x];
+        ai = x;
+      }
     if (!a) {
       agg.push_back(hkv_kernel_stat{});
+      times.emplace_back();
+      ai = agg.size() - 1;
       a = &agg.back();
       std::snprintf(a->name, sizeof(a->name), "%s", r.name);
       a->min_ms = ms;
     }
+    times[ai].push_back(ms);
     a->launches += 1;
     a->total_ms += ms;
     a->sumsq_ms2 += static_cast<double>(ms) * ms;
@@ -915,6 +924,11 @@ HKV_API hkv_status hkv_profile_stop(hkv_table* t, hkv_kernel_stat* out, uint32_t
     t->prof.give_back(r.stop);
   }
   t->prof.records().clear();
+  for (size_t x = 0; x < agg.size(); ++x) {
+    std::vector<float>& v = times[x];
+    std::nth_element(v.begin(), v.begin() + v.size() / 2, v.end());
+    agg[x].median_ms = v[v.size() / 2];
+  }
   *count = static_cast<uint32_t>(agg.size());
   for (uint32_t j = 0; j < cap && j < agg.size(); ++j) out[j] = agg[j];
   return st;

@@ -365,6 +365,9 @@ typedef struct hkv_kernel_stat {
   double max_ms;      /* longest one */
   double min_ms;      /* shortest one */
   double sumsq_ms2;   /* sum of their squared times (spread across launches) */
+  double median_ms;   /* median launch time (upper median for an even count): unlike the
+                         average, not moved by a few launches whose start event was taken
+                         before the kernel was dispatched */
 } hkv_kernel_stat;
 
 /* hkv_profile_start - discards earlier records and turns timing on. The

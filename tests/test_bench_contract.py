@@ -127,3 +127,10 @@ def test_json_line_carries_the_contract_fields(monkeypatch, capsys):
     assert r["traffic"] == bench.profiled_traffic("upsert_probe", 64, 26)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["unit"] == d["unit"] and c["sample"]
+
+
+def test_launch_cv_reads_the_library_record():
+    """The library's per-kernel record is (launches, total_ms, max_ms, min_ms,
+    sum of squares, median_ms); three launches of 1, 2 and 3 ms."""
+    rec = (3, 6.0, 3.0, 1.0, 14.0, 2.0)
+    assert bench.launch_cv(rec) == round((14.0 / 3 - 4.0) ** 0.5 / 2.0, 4)
