@@ -21,3 +21,5 @@ def test_readme_usage_example_runs():
     found = scope["found"]
     assert bool(found.bool().all())  # every key inserted, then found (capacity far above the batch)
     assert int(scope["count"].item()) == 0  # re-inserting resident keys hands nothing back
+    n = scope["keys"].numel()
+    assert scope["outcomes"] == {"updated": 0, "inserted": n, "evicted": 0, "rejected": 0}
