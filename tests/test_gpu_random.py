@@ -8,7 +8,9 @@ every kind with batch sizes from one key to three times the capacity. Scores
 never decrease for a key, so every call's result is the same in any order of
 its keys and single-bucket mode is compared exactly after every call:
 per-bucket contents, rows and scores, find outputs (misses untouched),
-insert_and_evict's hand-back as a set, find_or_insert's flags and rows.
+insert_and_evict's hand-back as a set, find_or_insert's flags and rows, and
+each call's outcome counts (set differences of the oracle's states before and
+after it; zero for the reader and updater calls).
 In serial insert mode (single and dual bucket) scores are arbitrary and
 every key's slot position is compared as well. Dual-bucket parallel mode is
 held to its invariants after every call.
@@ -47,6 +49,8 @@ def test_random_small_configuration_exact(case):
     scheme = str(rng.choice(["constant", "step", "jitter"]))
     C = B * SLOTS
     tab = H.HashTable(C, D)
+    tab.count_outcomes()
+    was = tab.outcomes()
     o = oracle.OracleTable(C, D)
     pool = gen.unique_keys(case, 7, 0, int(C * rng.uniform(0.5, 4.0)) + 1).numpy().view(np.uint64)
     absent = gen.unique_keys(case, 8, 0, 64).numpy().view(np.uint64)
@@ -61,6 +65,7 @@ def test_random_small_configuration_exact(case):
         sct = to_dev(sc)
         v = gen.values(kt, 100 * case + step, D)
         print(f"case {case}: B={B} D={D} scheme={scheme} step={step} call={call} n={n}", flush=True)
+        before = set(o.export()["keys"].tolist())
         if call == "insert_or_assign":
             tab.insert_or_assign(kt, v, sct)
             o.insert_or_assign(k, sc, values=v.cpu().numpy())
@@ -85,6 +90,15 @@ def test_random_small_configuration_exact(case):
             q = np.random.default_rng(case * 100 + step).permutation(np.concatenate([k[: max(1, n // 2)], absent]))
             check_find(tab, o, to_dev(q))
         assert_same_contents(tab, o)
+        after = set(o.export()["keys"].tolist())
+        now = tab.outcomes()
+        want = dict(updated=0, inserted=0, evicted=0, rejected=0)
+        if call in ("insert_or_assign", "insert_and_evict", "find_or_insert"):
+            b = set(k.tolist())
+            want = dict(updated=len(b & before), inserted=len(after - before), evicted=len(before - after),
+                        rejected=len(b - before - after))
+        assert {x: now[x] - was[x] for x in now} == want
+        was = now
 
 
 def assert_same_positions(tab, o):
