@@ -171,13 +171,16 @@ def test_random_dual_parallel_invariants(case):
     most 128 per bucket, every entry in one of its two candidate buckets, each
     resident key's score and row its last written ones, find hitting exactly
     the resident keys, and insert_and_evict's hand-back and the table together
-    holding exactly what was resident or offered."""
+    holding exactly what was resident or offered; each call's outcome counts
+    equal the set differences of the table's states before and after it."""
     H = hkv()
     rng = np.random.default_rng(9000 + case)
     B = int(rng.choice([2, 3, 5, 8, 13]))
     D = int(rng.choice([1, 4, 7, 64]))
     C = B * SLOTS
     tab = H.HashTable(C, D, dual_bucket=True)
+    tab.count_outcomes()
+    was = tab.outcomes()
     route = oracle.OracleTable(SLOTS * B, 1, dual=True)  # routing only
     pool = gen.unique_keys(case + 200, 11, 0, int(C * rng.uniform(0.5, 3.0)) + 1).numpy().view(np.uint64)
     absent = gen.unique_keys(case + 200, 12, 0, 64).numpy().view(np.uint64)
@@ -256,6 +259,13 @@ def test_random_dual_parallel_invariants(case):
             assert resident <= before | offered
         else:
             assert resident == before
+        now = tab.outcomes()
+        want = dict(updated=0, inserted=0, evicted=0, rejected=0)
+        if call != "assign":
+            want = dict(updated=len(offered & before), inserted=len(resident - before),
+                        evicted=len(before - resident), rejected=len(offered - before - resident))
+        assert {x: now[x] - was[x] for x in now} == want
+        was = now
 
 
 @pytest.mark.parametrize("lanes,keys_per_group", [("4", "1"), ("16", "4"), ("4", "4"), ("16", "1")])
