@@ -111,8 +111,9 @@ typedef int32_t hkv_status;
 #define HKV_FLAG_UNIQUE_KEYS 0x4u
 
 typedef struct hkv_options {
-  uint64_t capacity;        /* slots; a positive multiple of 128 (§3.2). B = capacity / 128 buckets */
-  uint32_t dim;             /* float32 elements per value row, >= 1 */
+  uint64_t capacity;        /* slots; a positive multiple of 128 (§3.2). B = capacity / 128 buckets,
+                               at most 2^31 - 1 */
+  uint32_t dim;             /* float32 elements per value row, 1 .. 2^20 */
   uint32_t bucket_slots;    /* must be 128 (or 0, meaning 128) */
   uint32_t dual_bucket;     /* 0: single-bucket (§3.2); 1: score-based dual-bucket (§3.4) */
   uint32_t values_on_host;  /* 0: value rows in HBM; 1: in pinned, GPU-mapped host memory (§3.6),
@@ -135,8 +136,9 @@ typedef struct hkv_options {
  * bucket, 28 bytes of bookkeeping in HBM (occupancy 4, inserter chain head 8,
  * one claim bit per slot) and, in dual-bucket mode, 16 more (its lowest entry).
  * Every slot starts empty. The table owns all of its storage.
- * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128,
- * dim == 0, bucket_slots not 128, bad device), HKV_ENOMEM, HKV_EHIP.
+ * Errors: HKV_EINVAL (null arguments, capacity not a positive multiple of 128
+ * or above 2^31 - 1 buckets, dim outside 1 .. 2^20, bucket_slots not 128, bad
+ * device), HKV_ENOMEM, HKV_EHIP.
  * On error *out is set to NULL.
  */
 hkv_status hkv_create(const hkv_options* options, hkv_table** out);

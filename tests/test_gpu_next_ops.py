@@ -604,6 +604,63 @@ def test_wide_rows_every_call_exact(D):
     check_find(tab, o, mixed_queries(o, 700, 0.7, 6, 12))
 
 
+def test_largest_row_width_every_call_exact():
+    """Rows of the largest width a table accepts (2^20 floats, 4 MiB each) in
+    one bucket: inserts that fill it and then evict, find with scores,
+    insert_and_evict, find_or_insert and assign, every result and the table's
+    contents bit-exact against the oracle (64-bit row offsets, long row-copy
+    loops, long chains of one owner)."""
+    H = hkv()
+    C, D = SLOTS, 1 << 20
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    step = 0
+    for b in range(3):  # 144 distinct keys into 128 slots
+        step += 1
+        k = gen.unique_keys(47, 1, 48 * b, 48, device=dev())
+        v = gen.values(k, step, D)
+        sc = torch.full((48,), step, dtype=torch.int64, device=dev())
+        tab.insert_or_assign(k, v, sc)
+        o.insert_or_assign(np_u64(k), np_u64(sc), values=v.cpu().numpy())
+        del v
+    assert o.size() == C
+    assert_same_contents(tab, o)
+    check_find(tab, o, mixed_queries(o, 24, 0.75, 5, 47))
+    step += 1
+    k = gen.unique_keys(47, 2, 0, 16, device=dev())
+    v = gen.values(k, step, D)
+    sc = torch.full((16,), step, dtype=torch.int64, device=dev())
+    got = evict_sets(*tab.insert_and_evict(k, v, sc))
+    want = oracle_evict_sets(o.insert_and_evict(np_u64(k), np_u64(sc), values=v.cpu().numpy()))
+    assert got[0].size == 16 and np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+    del got, want, v
+    step += 1
+    fresh = gen.unique_keys(47, 3, 0, 8).numpy().view(np.uint64)
+    k = np.random.default_rng(47).permutation(np.concatenate([fresh, sample_present(o, 8, 48)]))
+    kt = to_dev(k)
+    v = gen.values(kt, step, D)
+    sc = torch.full((k.size,), step, dtype=torch.int64, device=dev())
+    v0 = v.cpu().numpy()
+    rows, found = tab.find_or_insert(kt, v, sc)
+    orows, ofound = o.find_or_insert(k, np_u64(sc), values=v0)
+    torch.cuda.synchronize()
+    assert np.array_equal(found.cpu().numpy(), ofound)
+    assert np.array_equal(rows.cpu().numpy().view(np.uint32), orows.view(np.uint32))
+    del rows, orows, v, v0
+    step += 1
+    ak = sample_present(o, 16, 49)
+    akt = to_dev(ak)
+    av = gen.values(akt, step, D)
+    asc = torch.full((ak.size,), step, dtype=torch.int64, device=dev())
+    tab.assign(akt, av, asc)
+    o.assign(ak, values=av.cpu().numpy(), scores=np_u64(asc))
+    del av
+    assert_same_contents(tab, o)
+    check_find(tab, o, mixed_queries(o, 24, 0.75, 6, 50))
+    tab.close()
+
+
 def test_find_or_insert_dual_parallel_invariants():
     """Dual-bucket parallel find_or_insert under a Zipf stream: found iff the
     key was resident before, hits return the row of the key's last write,

@@ -74,6 +74,8 @@ def _create(**kw):
     (dict(capacity=0), "multiple of 128"),
     (dict(capacity=1000), "multiple of 128"),
     (dict(dim=0), "dim"),
+    (dict(dim=(1 << 20) + 1), "dim"),  # rows of at most 2^20 floats
+    (dict(capacity=128 << 31), "2^31 - 1 buckets"),
     (dict(bucket_slots=64), "128-slot"),
     (dict(dual_bucket=2), "0 or 1"),
     (dict(flags=0x80), "flags"),
