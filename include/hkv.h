@@ -341,6 +341,7 @@ hkv_status hkv_export_batch(hkv_table* table, uint64_t offset, uint64_t n_slots,
  * key repeated in a batch, updated counts it once in insert_or_assign and
  * insert_and_evict, once per occurrence in find_or_insert; rejected counts a
  * key again when an occurrence arrives after its earlier one was displaced.
+ * The reserved keys, which every inserter skips, count in none of the four.
  * counts: 4 uint64 in device memory of the table's GPU, owned by the caller
  * and valid while set; the calls add to them (zero them to start) with
  * device atomics, after the call's other kernels, on the call's stream.

@@ -164,6 +164,31 @@ def test_counts_with_repeated_keys(dual):
     tab.close()
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_reserved_keys_count_in_no_outcome(kind):
+    """The reserved keys (2^64 - 1, 2^64 - 2) are skipped by every inserter:
+    a batch that carries them among resident and new keys counts only the
+    others."""
+    H = hkv()
+    C, D = 8 * SLOTS, 4
+    tab = H.HashTable(C, D)
+    o = oracle.OracleTable(C, D)
+    tab.count_outcomes()
+    old = np.arange(1, 201, dtype=np.uint64)
+    call("insert_or_assign", tab, o, old, np.ones(200, np.uint64), 1, D)
+    was = tab.outcomes()
+    rsv = np.array([2**64 - 1, 2**64 - 2, 2**64 - 1], dtype=np.uint64)
+    k = np.random.default_rng(92).permutation(np.concatenate([rsv, old[:50], np.arange(1000, 1040, dtype=np.uint64)]))
+    before = set(o.export()["keys"].tolist())
+    call(kind, tab, o, k, np.full(k.size, 2, np.uint64), 2, D)
+    after = set(o.export()["keys"].tolist())
+    assert gpu_keys(tab) == after
+    d = delta(tab.outcomes(), was)
+    assert d == expected(k[k < 2**64 - 2], before, after) == {"updated": 50, "inserted": 40, "evicted": 0,
+                                                                "rejected": 0}
+    tab.close()
+
+
 def test_counting_off_serial_tables_and_bad_arguments():
     H = hkv()
     C, D = 4 * SLOTS, 4
