@@ -606,6 +606,35 @@ def test_invalid_pointers_are_rejected():
                          dim=4, device=0)
 
 
+def test_batches_beyond_the_index_limit_are_refused():
+    """Batch indices 2^32 - 4 .. 2^32 - 1 mark chain ends in the inserter, so
+    every batched call refuses n > 2^32 - 4 with HKV_EINVAL, before it reads
+    any buffer (the pointers here are small device buffers, never touched)."""
+    from hash_table_cache_amd import _native
+
+    H = hkv()
+    L = _native.load()
+    tab = H.HashTable(SLOTS, 4)
+    h = tab.handle
+    buf = torch.zeros(64, dtype=torch.int64, device=dev())
+    p = buf.data_ptr()
+    n = (1 << 32) - 3
+    calls = {
+        "find": lambda: L.hkv_find(h, n, p, p, p, None, None),
+        "find_ptr": lambda: L.hkv_find_ptr(h, n, p, p, p, None, None),
+        "contains": lambda: L.hkv_contains(h, n, p, p, None),
+        "insert_or_assign": lambda: L.hkv_insert_or_assign(h, n, p, p, p, None),
+        "insert_and_evict": lambda: L.hkv_insert_and_evict(h, n, p, p, p, p, None, None, p, None),
+        "find_or_insert": lambda: L.hkv_find_or_insert(h, n, p, p, p, None, None),
+        "assign": lambda: L.hkv_assign(h, n, p, p, p, None),
+    }
+    for name, c in calls.items():
+        assert c() == _native.HKV_EINVAL, name
+        assert b"exceeds the limit" in L.hkv_last_error(), name
+    assert tab.size() == 0
+    tab.close()
+
+
 def test_group_ordering_across_streams():
     """An upsert on one stream followed, without host synchronization, by a
     find on another stream must observe the upsert: the library orders the
