@@ -32,7 +32,7 @@ bucket):
                 + 8 key + 1 digest + 8 score + 4D row write
                 + e (1024 score column + 8 tied key)]
 
-Prints one JSON line. --gpus N > 1 exits: this build runs on one GPU.
+Prints one JSON line. --gpus N > 1 exits: the table lives on one GPU.
 """
 
 from __future__ import annotations
@@ -1373,7 +1373,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the table is a single-GPU "
-              "structure in this build and multi-GPU sharding is not implemented.", file=sys.stderr)
+              "structure and sharding it across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)

@@ -85,7 +85,7 @@ typedef int32_t hkv_status;
 #define HKV_EINVAL (-1)       /* bad argument (null, size, alignment, pointer kind) */
 #define HKV_ENOMEM (-2)       /* device or pinned host allocation failed */
 #define HKV_EHIP (-3)         /* a HIP runtime call or kernel launch failed */
-#define HKV_EUNSUPPORTED (-4) /* valid request this build does not implement */
+#define HKV_EUNSUPPORTED (-4) /* valid request the library does not implement */
 
 #define HKV_BUCKET_SLOTS 128u
 /* Reserved key values: an empty slot and the slot-lock sentinel (§4.4). */
